@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the dual-path quantized-base + LoRA linear on one MI355X.
+
+Headline (value): one 7B-style block of seven q8_0 linears at batch 1, each
+with a rank-16 LoRA at scale 1.0 (q,k,v,o 4096x4096; gate/up 4096->11008;
+down 11008->4096), run through qbl_block (prep/shrink + fused dequant-GEMV +
+expand, with the linear glue between the linears).  A step is one block for
+one token; the inputs are resident in HBM and the step rotates over
+independent copies of the weights and adapters so the 256 MB Infinity Cache
+cannot serve them.  value = algorithmic bytes per step / time per step.
+
+Also reported on the same JSON line:
+  roofline      the fused GEMV kernel: algorithmic bytes per launch / average
+                launch duration (HIP events on the launch stream), vs 8 TB/s
+  cpu_baseline  the float64 C oracle on the host cores, same workload
+  stack         32 such blocks, two adapters (r16@1.0 then r64@0.5), 256 tokens
+  q4_mlp        70B-style q4_sm MLP linears at batch 1 and 8
+  prefill       the JIT-materialisation prefill GEMM (when available)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "batch-1 q8_0+LoRA GEMV effective GB/s and % HBM peak; tokens/s over 32-block stack"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def linear_bytes(wl, i, with_a=True):
+    """Algorithmic bytes of one linear at batch 1: quantised base, LoRA factors
+    (A only if the shrink is counted), x read once, y written once."""
+    L = wl.linears[i]
+    r = sum(a.rank for a in wl.adapters)
+    b = wl.base_bytes(i) + 4 * r * L.n_out + 4 * (L.n_out + L.k_in)
+    if with_a:
+        b += 4 * r * L.k_in
+    return b
+
+
+def build_copies(q, wl, copies, adapter_idx):
+    """One base holding `copies` copies of the workload's linears, one adapter
+    per workload adapter covering every copy; returns (base, adapters, comp, blocks)."""
+    blocks = [q.qbl_quantize(L.qtype, wl.weight(i)) for i, L in enumerate(wl.linears)]
+    descs = []
+    for c in range(copies):
+        for i, L in enumerate(wl.linears):
+            descs.append((L.qtype, L.n_out, L.k_in, blocks[i]))
+    base = q.qbl_base_load(descs)
+    n = len(wl.linears)
+    ads = []
+    for a in adapter_idx:
+        fac = [(wl.lora_a(i, a), wl.lora_b(i, a)) for i in range(n)]
+        ads.append(q.qbl_adapter_load(base, [(c * n + i, A, B) for c in range(copies)
+                                             for i, (A, B) in enumerate(fac)]))
+    comp = q.qbl_comp_create(base)
+    q.qbl_comp_attach(comp, ads, [wl.adapters[a].scale for a in adapter_idx])
+    return base, ads, comp, blocks
+
+
+def free_all(q, base, ads, comp):
+    q.qbl_comp_free(comp)
+    for a in ads:
+        q.qbl_adapter_free(a)
+    q.qbl_base_free(base)
+
+
+def time_loop(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_block(torch, q, workloads, args):
+    wl = workloads.block()
+    copies = args.copies
+    log(f"[block] building {copies} copies of one 7B block (q8_0, r16)")
+    t0 = time.time()
+    base, ads, comp, blocks = build_copies(q, wl, copies, [0])
+    log(f"[block] built in {time.time() - t0:.1f}s")
+    x = torch.from_numpy(wl.x0()[0]).cuda()
+    ys = [torch.empty(4096, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    ws = q.workspace(comp, q.OP_BLOCK)
+
+    def step(i):
+        q.qbl_block(comp, i % copies, x, ys[i % copies], ws)
+
+    ms = time_loop(torch, step, args.steps, args.warmup)
+    step_bytes = sum(linear_bytes(wl, i) for i in range(7))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[block] {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+
+    # kernel durations: the same loop with timing events around every launch
+    q.qbl_profile_enable(True)
+    ms_prof = time_loop(torch, step, args.steps, 0)
+    n_gemv, ms_gemv = q.qbl_profile_read(q.KIND_GEMV)
+    n_prep, ms_prep = q.qbl_profile_read(q.KIND_PREP)
+    q.qbl_profile_enable(False)
+    # GEMV algorithmic bytes per step: base + B + x + y of the 7 linears plus
+    # the shrink results it reads (t), over the 4 fused launches
+    gemv_bytes_step = sum(linear_bytes(wl, i, with_a=False) for i in range(7))
+    gemv_bytes_step += 4 * (3 * 16 + 16 + 2 * 16 + 16)
+    launches_per_step = n_gemv / args.steps
+    avg_us = ms_gemv / max(n_gemv, 1) * 1e3
+    achieved = gemv_bytes_step / launches_per_step / (avg_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "gemv_kernel (fused q8_0 dequant-GEMV + LoRA expand)",
+            "launches_per_step": launches_per_step, "avg_launch_us": round(avg_us, 2),
+            "bytes_per_launch": int(gemv_bytes_step / launches_per_step),
+            "prep_avg_launch_us": round(ms_prep / max(n_prep, 1) * 1e3, 2),
+            "step_us_with_timing_events": round(ms_prof * 1e3, 1)}
+    free_all(q, base, ads, comp)
+    return wl, blocks, ms, step_bytes, gbs, roof
+
+
+def cpu_baseline(oracle, wl, blocks, seconds):
+    """The oracle's dual path over the block's seven linears, repeated for about
+    `seconds` of wall time on all host cores."""
+    import numpy as np
+    xs = [wl.x(i).astype(np.float64) for i in range(7)]
+    ads = [[oracle.Lora(wl.lora_a(i, 0), wl.lora_b(i, 0), 1.0)] for i in range(7)]
+    threads = oracle.default_threads()
+    done, total_bytes = 0, 0
+    t0 = time.time()
+    while True:
+        for i, L in enumerate(wl.linears):
+            oracle.linear_dual(L.qtype, blocks[i], L.n_out, L.k_in, xs[i], ads[i],
+                               nthreads=threads)
+            total_bytes += linear_bytes(wl, i)
+        done += 1
+        if time.time() - t0 >= seconds:
+            break
+    el = time.time() - t0
+    return {"value": round(total_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} full passes over the block's 7 linears (float64, row-parallel), {el:.1f}s"}
+
+
+def bench_stack(torch, q, workloads, args):
+    wl = workloads.stack(tokens=args.stack_tokens)
+    log("[stack] building 32 blocks (6.9 GB q8_0) + r16/r64 adapters")
+    t0 = time.time()
+    base, ads, comp, _ = build_copies(q, wl, 1, [0, 1])
+    log(f"[stack] built in {time.time() - t0:.1f}s")
+    d = 4096
+    x0 = torch.from_numpy(wl.x0()[0]).cuda()
+    y = torch.empty((wl.tokens, d), dtype=torch.float32, device="cuda")
+    ws = q.workspace(comp, q.OP_BLOCK)
+    q.qbl_decode(comp, 0, 32, x0, y, 2, ws)       # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    q.qbl_decode(comp, 0, 32, x0, y, wl.tokens, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    tok_s = wl.tokens / (ms * 1e-3)
+    per_tok = sum(linear_bytes(wl, i) for i in range(len(wl.linears)))
+    h0 = q.qbl_base_hash(base)
+    y_ab = y.clone()
+    q.qbl_comp_attach(comp, [ads[1], ads[0]], [0.5, 1.0])
+    q.qbl_decode(comp, 0, 32, x0, y, wl.tokens, ws)
+    torch.cuda.synchronize()
+    changed = not torch.equal(y, y_ab)
+    same_hash = q.qbl_base_hash(base) == h0
+    free_all(q, base, ads, comp)
+    log(f"[stack] {tok_s:.0f} tok/s, order swap changes output: {changed}, hash unchanged: {same_hash}")
+    return {"tokens_per_s": round(tok_s, 1), "tokens": wl.tokens, "ms_per_token": round(ms / wl.tokens, 4),
+            "GB_per_s": round(per_tok / (ms / wl.tokens * 1e-3) / 1e9, 1),
+            "frac_hbm": round(per_tok / (ms / wl.tokens * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_token": per_tok, "order_swap_changes_output": changed,
+            "base_hash_unchanged": same_hash}
+
+
+def bench_q4(torch, q, workloads, args):
+    out = {}
+    wl = workloads.mlp70b()
+    log("[q4] building 70B MLP linears (q4_sm, r32)")
+    base, ads, comp, _ = build_copies(q, wl, 1, [0])
+    for batch in (1, 8):
+        xs = [torch.from_numpy(wl.x(i, batch)).cuda() for i in range(3)]
+        ys = [torch.empty((batch, L.n_out), dtype=torch.float32, device="cuda") for L in wl.linears]
+        wss = [q.workspace(comp, q.OP_LINEAR, i, batch) for i in range(3)]
+
+        def step(_):
+            for i in range(3):
+                q.qbl_linear(comp, i, xs[i], ys[i], batch, wss[i])
+
+        ms = time_loop(torch, step, max(5, args.steps // 2), 2)
+        byts = sum(wl.base_bytes(i) + wl.lora_bytes(i) + 4 * batch * (L.n_out + L.k_in)
+                   for i, L in enumerate(wl.linears))
+        gbs = byts / (ms * 1e-3) / 1e9
+        out[f"batch{batch}"] = {"us_per_mlp": round(ms * 1e3, 1), "GB_per_s": round(gbs, 1),
+                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": byts}
+        log(f"[q4] batch {batch}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    free_all(q, base, ads, comp)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step (>= 600 MB)")
+    ap.add_argument("--stack-tokens", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-extras", action="store_true", help="skip the stack / q4 / prefill lines")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_base_linear_amd as q
+    from synth import workloads
+    torch.cuda.set_device(0)
+
+    wl, blocks, ms, step_bytes, gbs, roof = bench_block(torch, q, workloads, args)
+    result = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "q8_0/f32",
+        "data": "synthetic (seeded normal weights, adapters and activations)",
+        "config": {"workload": "7B-style block, 7 q8_0 linears (4096/11008), rank-16 LoRA at 1.0, batch 1",
+                   "batch": 1, "bytes_per_step": step_bytes, "weight_copies_rotated": args.copies,
+                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+    }
+    if not args.no_extras:
+        result["stack"] = bench_stack(torch, q, workloads, args)
+        result["q4_mlp"] = bench_q4(torch, q, workloads, args)
+    import oracle
+    log("[cpu] timing the oracle")
+    result["cpu_baseline"] = cpu_baseline(oracle, wl, blocks, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

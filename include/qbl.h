@@ -1,0 +1,268 @@
+/*
+ * qbl: the dual-path quantized-base + LoRA linear on AMD Instinct MI355X (gfx950).
+ *
+ *   y = dequant(W_q) x + sum_i s_i B_i (A_i x)        adapters summed in list order
+ *
+ * over an immutable block-quantized base (q8_0 or q4_sm), plus a per-layer
+ * just-in-time path for multi-token prefill that materialises
+ * W_eff = dequant(W_q) + sum_i s_i B_i A_i in on-chip scratch, uses it and
+ * discards it.
+ *
+ * The operations follow three pages on quantized-base adapter overlays:
+ *  [overlay]  mikekappel.com, "We propose a content-addressed overlay system"
+ *             (sections "Runtime Strategy Comparison Matrix", "Native/WASM Kernel
+ *             Implications", "Proposed Activation/Deactivation State Machine",
+ *             "Clean Replacement Plan and Rejection Criteria");
+ *  [design]   mikekappel.com, "Deep Technical Design: Exact, Atomic, Reversible
+ *             Specialist Overlays" (sections 1, 2, 5, 6, 8, 9, 11);
+ *  [lora]     contenox.com, "LoRA adapters" blueprint ("Backend Support
+ *             Position", llama.cpp adapter API and its shape rules).
+ *
+ * Conventions for every call:
+ *  - Every function returns a qbl_status (0 = QBL_OK, negative = error) unless
+ *    stated.  On error nothing changed: no handle, composition or base byte is
+ *    modified, out-parameters are left untouched, and qbl_last_error() returns
+ *    a description (thread-local).  No C++ exception crosses this boundary.
+ *  - "host" pointers are CPU memory; "device" pointers are GPU memory of the
+ *    base's device (e.g. torch CUDA tensors).  Matrices are row-major, float32
+ *    unless stated, contiguous, and at least 16-byte aligned.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream).  Run
+ *    calls only enqueue work on it and return without synchronising.
+ *  - The library owns the device copies of bases and adapters; the caller owns
+ *    x, y and the workspace.  Calls on one composition from several host threads
+ *    are serialised by the library.
+ */
+#ifndef QBL_H
+#define QBL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QBL_ABI_VERSION 1
+
+typedef int32_t qbl_status;
+#define QBL_OK 0
+#define QBL_E_ARG (-1)        /* null pointer, bad index or count */
+#define QBL_E_SHAPE (-2)      /* dimensions do not match the base */
+#define QBL_E_FORMAT (-3)     /* unknown quantisation type, k not a multiple of 32, bad byte count */
+#define QBL_E_NONFINITE (-4)  /* NaN/Inf in weights, adapter factors or scales */
+#define QBL_E_NOMEM (-5)      /* device or host allocation failed */
+#define QBL_E_BUDGET (-6)     /* workspace too small */
+#define QBL_E_BUSY (-7)       /* object still referenced */
+#define QBL_E_DEVICE (-8)     /* a HIP runtime call failed */
+#define QBL_E_FOREIGN (-9)    /* adapter bound to another base */
+#define QBL_E_DUPLICATE (-10) /* the same handle twice in one list, or one linear twice in one adapter */
+#define QBL_E_LIMIT (-11)     /* above a documented limit */
+
+/* Quantisation types.
+ * QBL_Q8_0: blocks of 32 weights along k: one fp16 scale d and 32 int8 q,
+ *   w = d*q ([design] section 5: 32 weights and one f16 scale, 8.5 bits per
+ *   weight).  Canonical block bytes: [d as fp16 little-endian][q0..q31] = 34 B.
+ * QBL_Q4_SM: blocks of 32 weights: fp16 scale d, fp16 min m, 32 unsigned
+ *   4-bit q, w = d*q + m ([design] section 5: per-block scale and minimum).
+ *   Canonical block bytes: [d][m][16 B; byte i = q[2i] | q[2i+1] << 4] = 20 B. */
+#define QBL_Q8_0 1
+#define QBL_Q4_SM 2
+
+/* Limits. */
+#define QBL_MAX_ADAPTERS 8     /* entries in one attached list */
+#define QBL_MAX_RANK 256       /* rank of one adapter on one linear */
+#define QBL_MAX_TOTAL_RANK 512 /* sum of ranks on one linear over an attached list */
+#define QBL_MAX_BATCH 8        /* rows of x for qbl_linear */
+#define QBL_MAX_K 65536        /* input features of a linear */
+
+typedef struct qbl_base qbl_base;
+typedef struct qbl_adapter qbl_adapter;
+typedef struct qbl_comp qbl_comp;
+
+/* Text of the calling thread's last error ("" if none).  Never NULL. */
+const char* qbl_last_error(void);
+
+/* QBL_ABI_VERSION of the built library (not a status). */
+int32_t qbl_abi_version(void);
+
+/* Bytes of one 32-weight block of qtype (34 or 20); 0 for an unknown type. */
+int64_t qbl_block_bytes(int32_t qtype);
+
+/* Quantise a host float32 matrix w (n x k, k a multiple of 32) into canonical
+ * blocks (host, n*k/32*qbl_block_bytes bytes, caller-owned).
+ * q8_0: d = fp16(max|w|/127), q = round-half-away(w / d) with the stored d, clamped
+ *   to [-127, 127]; an all-zero block gives d = 0, q = 0.
+ * q4_sm: m = fp16(min w), d = fp16((max w - m)/15), q = round-half-away((w - m)/d)
+ *   clamped to [0, 15]; q = 0 where d = 0.
+ * nthreads <= 0 uses the online cores.  QBL_E_NONFINITE on NaN/Inf input,
+ * QBL_E_LIMIT if a q8_0 scale would overflow fp16. */
+qbl_status qbl_quantize(int32_t qtype, const float* w, int64_t n, int64_t k, void* blocks_out,
+                        int32_t nthreads);
+
+/* SHA-256 (FIPS 180-4) of n host bytes: the digest used by qbl_base_hash and
+ * qbl_adapter_digest. */
+qbl_status qbl_sha256(const void* data, int64_t n, uint8_t sha256_out[32]);
+
+/* Dequantise canonical blocks (host) to float32 (host, n x k). */
+qbl_status qbl_dequantize(int32_t qtype, const void* blocks, int64_t n, int64_t k, float* w_out);
+
+/* ---------------------------------------------------------------- base --- */
+
+/* One linear of a base: n_out x k_in weights as canonical blocks in host memory. */
+typedef struct {
+  int32_t qtype;
+  int32_t reserved; /* must be 0 */
+  int64_t n_out;
+  int64_t k_in;
+  const void* blocks; /* host, n_out * k_in/32 * qbl_block_bytes(qtype) bytes */
+  int64_t nbytes;     /* must equal that size */
+} qbl_linear_desc;
+
+/* Load an immutable base of n_linears linears onto the current HIP device.
+ * Linears are numbered 0..n_linears-1 in this order.  Block b of a stack is
+ * linears 7b..7b+6 in the order q, k, v, o, gate, up, down; qbl_block and
+ * qbl_decode check those shapes when called.  The library copies the blocks
+ * (the caller may free them on return), repacks them into its device layout,
+ * and seals them: no kernel ever receives a writable pointer to base bytes
+ * ([design] section 2, the oracle invariant: base bytes stay bit-identical).
+ * *out receives the handle. */
+qbl_status qbl_base_load(const qbl_linear_desc* descs, int32_t n_linears, qbl_base** out);
+
+/* SHA-256 (FIPS 180-4) over the base's device bytes, re-read from the GPU on
+ * every call: the digest of the concatenation, in linear order, of each
+ * linear's SHA-256 over its device arrays.  Equal before and after any attach,
+ * clear or run ([overlay] "Checksum Verification"; [design] section 2). */
+qbl_status qbl_base_hash(qbl_base* base, uint8_t sha256_out[32]);
+
+/* Number of linears, and one linear's type and shape. */
+qbl_status qbl_base_count(const qbl_base* base, int32_t* n_linears);
+qbl_status qbl_base_info(const qbl_base* base, int32_t linear, int32_t* qtype, int64_t* n_out,
+                         int64_t* k_in);
+
+/* Free a base.  QBL_E_BUSY while any adapter or composition still refers to it
+ * (adapters are owned by the base they were loaded against, as in [lora]). */
+qbl_status qbl_base_free(qbl_base* base);
+
+/* ------------------------------------------------------------- adapters --- */
+
+/* One LoRA factor pair on one linear of the base: A is rank x k_in, B is
+ * n_out x rank, host float32 row-major ([overlay] "Memory, Byte, and Latency
+ * Formulas": A in R^{r x n}, B in R^{m x r}).  Shapes must satisfy the
+ * llama.cpp rule quoted in [lora]: A's columns = the base's inputs, B's rows =
+ * the base's outputs, A's rows = B's columns = rank. */
+typedef struct {
+  int32_t linear;
+  int32_t rank; /* 1..QBL_MAX_RANK */
+  const float* A;
+  const float* B;
+} qbl_lora_desc;
+
+/* Validate and upload an adapter touching n >= 1 linears of base (no linear
+ * twice).  Rejects non-finite values and unknown linears ([design] section 11
+ * deep compatibility checks; [lora]: an adapter that matches zero layers is
+ * rejected).  The adapter is bound to base.  *out receives the handle. */
+qbl_status qbl_adapter_load(qbl_base* base, const qbl_lora_desc* descs, int32_t n,
+                            qbl_adapter** out);
+
+/* SHA-256 of the adapter content: for each entry in order, the little-endian
+ * int32 linear and rank, then A's and B's float32 bytes. */
+qbl_status qbl_adapter_digest(const qbl_adapter* adapter, uint8_t sha256_out[32]);
+
+/* Drop the caller's reference.  Device memory lives on while an attached list
+ * uses the adapter, and until the last enqueued run that read it completes. */
+qbl_status qbl_adapter_free(qbl_adapter* adapter);
+
+/* --------------------------------------------------------- compositions --- */
+
+/* A composition: a base plus an ordered adapter list, initially empty.  An
+ * empty list is the base-only path. */
+qbl_status qbl_comp_create(qbl_base* base, qbl_comp** out);
+
+/* Replace the composition's adapter list with list[0..n) and effective scales
+ * scales[0..n) (alpha/rank already folded in, as [lora] describes for both
+ * backends; any finite value, negative included), 0 <= n <= QBL_MAX_ADAPTERS.
+ * Everything is validated before anything changes: every adapter bound to this
+ * base (QBL_E_FOREIGN), no handle twice (QBL_E_DUPLICATE), scales finite, the
+ * summed rank per linear within QBL_MAX_TOTAL_RANK.  Then a new immutable list
+ * replaces the old one in a single atomic exchange ([overlay] "Atomic Update";
+ * [design] section 6 COMMIT/SWAP).  Entries with scale 0 are dropped, so an
+ * all-zero list runs exactly the base-only instructions.  Runs already
+ * enqueued keep the list they captured.  Attaching the list already in place
+ * changes nothing ([overlay] "Idempotency"). */
+qbl_status qbl_comp_attach(qbl_comp* comp, const qbl_adapter* const* list, const float* scales,
+                           int32_t n);
+
+/* Empty the list (deactivation: drop the adapter references, the base is
+ * untouched; [design] section 6 "Exact Deactivation Flow"). */
+qbl_status qbl_comp_clear(qbl_comp* comp);
+
+/* Number of effective (non-zero-scale) entries in the current list. */
+qbl_status qbl_comp_count(const qbl_comp* comp, int32_t* n);
+
+qbl_status qbl_comp_free(qbl_comp* comp);
+
+/* ------------------------------------------------------------------ runs --- */
+
+/* Workspace bytes (device, caller-owned, 256-byte aligned) that a run needs:
+ *   op 0: qbl_linear on `index` = linear at batch m;
+ *   op 1: qbl_linear_jit on linear `index` with m rows;
+ *   op 2: qbl_block / qbl_decode (index ignored; m ignored).
+ * The size depends on the current list; query after attach. */
+qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index, int32_t m,
+                               int64_t* bytes_out);
+
+/* Dual path, decode ([overlay] "Native/WASM Kernel Implications": y = xW + x(BA)
+ * as a shrink t = A x then an expand B t; [design] section 8: dual path for
+ * batch-one GEMV, kernels fused so adapter rows are used as the base block is
+ * consumed; section 9: weighted adapters added at the final accumulation).
+ *   y[b][n] = sum_k deq(W)[n][k] x[b][k] + sum_i s_i sum_j B_i[n][j] t_i[b][j],
+ *   t_i[b] = A_i x[b],
+ * base sum first, adapters in list order, float32 accumulation.
+ * x: device float32 batch x k_in; y: device float32 batch x n_out (must not
+ * alias x); 1 <= batch <= QBL_MAX_BATCH.  Results are deterministic: the same
+ * inputs and list give the same bits. */
+qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x, float* y, int32_t batch,
+                      void* ws, int64_t ws_bytes, void* stream);
+
+/* Per-layer just-in-time path for prefill ([design] sections 1 and 8: for
+ * multi-token GEMM, materialise one layer in scratch, use it, discard it):
+ *   W_eff = bf16( float32(deq(W)) + sum_i bf16(s_i B_i) bf16(A_i) )    (tile by tile, on chip)
+ *   Y = X W_eff^T with float32 accumulation.
+ * X: device bfloat16 bit patterns, m x k_in; Y: device float32 m x n_out;
+ * q8_0 and q4_sm bases; m >= 1. */
+qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint16_t* x_bf16, float* y,
+                          int32_t m, void* ws, int64_t ws_bytes, void* stream);
+
+/* One block of linears at batch 1 (linears 7*block .. 7*block+6 = q, k, v, o,
+ * gate, up, down), with linear glue between them:
+ *   q,k,v = L(x); a = L_o(rms(q+k+v)); g,u = L_gate/up(rms(a));
+ *   d = L_down(rms(g+u)); y = rms(d),      rms(v) = v / sqrt(mean(v^2) + 1e-6).
+ * x, y: device float32 of the block's width. */
+qbl_status qbl_block(qbl_comp* comp, int32_t block, const float* x, float* y, void* ws,
+                     int64_t ws_bytes, void* stream);
+
+/* Decode n_tokens tokens through blocks first_block .. first_block+n_blocks-1:
+ * token 0 enters with x0, token t+1 with the output of token t.  y_tokens is
+ * device float32 n_tokens x width (row t = token t's output).  The list is read
+ * once at entry: a concurrent attach does not switch adapters inside one call
+ * ([overlay] "Concurrent Safety"). */
+qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_blocks, const float* x0,
+                      float* y_tokens, int32_t n_tokens, void* ws, int64_t ws_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------- timing --- */
+
+/* Kernel timing for measurement tools.  While enabled (on != 0), every launch
+ * of the library's kernels is bracketed by a pair of HIP events recorded on the
+ * launch stream.  Enabling clears earlier records.  qbl_profile_read waits for
+ * the recorded events and returns, per kernel kind (0 = fused dequant-GEMV,
+ * 1 = glue/shrink prep, 2 = JIT prefill GEMM), the number of launches and their
+ * summed duration in milliseconds.  Timing adds host work per launch: leave it
+ * off in production. */
+qbl_status qbl_profile_enable(int32_t on);
+qbl_status qbl_profile_read(int32_t kind, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QBL_H */

@@ -1,0 +1,316 @@
+"""Python binding of libqbl (include/qbl.h): the dual-path quantized-base + LoRA
+linear on MI355X.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Functions carry the C names; device buffers are torch CUDA tensors
+(their data pointers are passed), host buffers are numpy arrays, and the
+stream defaults to torch's current stream on the current device.  There is no
+CPU fallback: importing this module fails if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "libqbl.so")
+
+if not os.path.exists(_SO):
+    raise ImportError(f"{_SO} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+                      "or python quantized_base_linear_amd/build.py)")
+
+_lib = ctypes.CDLL(_SO)
+
+QBL_OK = 0
+QBL_Q8_0 = 1
+QBL_Q4_SM = 2
+QBL_MAX_ADAPTERS = 8
+QBL_MAX_RANK = 256
+QBL_MAX_TOTAL_RANK = 512
+QBL_MAX_BATCH = 8
+OP_LINEAR, OP_JIT, OP_BLOCK = 0, 1, 2
+
+STATUS = {0: "QBL_OK", -1: "QBL_E_ARG", -2: "QBL_E_SHAPE", -3: "QBL_E_FORMAT",
+          -4: "QBL_E_NONFINITE", -5: "QBL_E_NOMEM", -6: "QBL_E_BUDGET", -7: "QBL_E_BUSY",
+          -8: "QBL_E_DEVICE", -9: "QBL_E_FOREIGN", -10: "QBL_E_DUPLICATE", -11: "QBL_E_LIMIT"}
+
+
+class QblError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class qbl_linear_desc(ctypes.Structure):
+    _fields_ = [("qtype", ctypes.c_int32), ("reserved", ctypes.c_int32), ("n_out", ctypes.c_int64),
+                ("k_in", ctypes.c_int64), ("blocks", ctypes.c_void_p), ("nbytes", ctypes.c_int64)]
+
+
+class qbl_lora_desc(ctypes.Structure):
+    _fields_ = [("linear", ctypes.c_int32), ("rank", ctypes.c_int32), ("A", ctypes.c_void_p),
+                ("B", ctypes.c_void_p)]
+
+
+_vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+_PP = ctypes.POINTER(ctypes.c_void_p)
+EXPORTS = {
+    "qbl_last_error": (ctypes.c_char_p, []),
+    "qbl_abi_version": (_i32, []),
+    "qbl_block_bytes": (_i64, [_i32]),
+    "qbl_quantize": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32]),
+    "qbl_dequantize": (_i32, [_i32, _vp, _i64, _i64, _vp]),
+    "qbl_sha256": (_i32, [_vp, _i64, _vp]),
+    "qbl_base_load": (_i32, [_vp, _i32, _PP]),
+    "qbl_base_hash": (_i32, [_vp, _vp]),
+    "qbl_base_count": (_i32, [_vp, _vp]),
+    "qbl_base_info": (_i32, [_vp, _i32, _vp, _vp, _vp]),
+    "qbl_base_free": (_i32, [_vp]),
+    "qbl_adapter_load": (_i32, [_vp, _vp, _i32, _PP]),
+    "qbl_adapter_digest": (_i32, [_vp, _vp]),
+    "qbl_adapter_free": (_i32, [_vp]),
+    "qbl_comp_create": (_i32, [_vp, _PP]),
+    "qbl_comp_attach": (_i32, [_vp, _vp, _vp, _i32]),
+    "qbl_comp_clear": (_i32, [_vp]),
+    "qbl_comp_count": (_i32, [_vp, _vp]),
+    "qbl_comp_free": (_i32, [_vp]),
+    "qbl_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, _vp]),
+    "qbl_linear": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
+    "qbl_linear_jit": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
+    "qbl_block": (_i32, [_vp, _i32, _vp, _vp, _vp, _i64, _vp]),
+    "qbl_decode": (_i32, [_vp, _i32, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
+    "qbl_profile_enable": (_i32, [_i32]),
+    "qbl_profile_read": (_i32, [_i32, _vp, _vp]),
+}
+for _name, (_res, _args) in EXPORTS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def library_path() -> str:
+    return _SO
+
+
+def _check(status: int):
+    if status != QBL_OK:
+        raise QblError(status, _lib.qbl_last_error().decode(errors="replace"))
+
+
+def _host(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _dev_ptr(t, dtype=None):
+    """Data pointer of a contiguous CUDA tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("device buffers must be contiguous CUDA tensors")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# -- formats ---------------------------------------------------------------------
+def qbl_last_error() -> str:
+    return _lib.qbl_last_error().decode(errors="replace")
+
+
+def qbl_abi_version() -> int:
+    return int(_lib.qbl_abi_version())
+
+
+def qbl_block_bytes(qtype: int) -> int:
+    return int(_lib.qbl_block_bytes(qtype))
+
+
+def qbl_quantize(qtype: int, w, nthreads: int = 0) -> np.ndarray:
+    """Canonical blocks (uint8, n x k/32*block_bytes) of a host float32 matrix."""
+    w = _host(w, np.float32)
+    n, k = w.shape
+    out = np.empty((n, max(0, k // 32) * max(1, qbl_block_bytes(qtype))), np.uint8)
+    _check(_lib.qbl_quantize(qtype, w.ctypes.data, n, k, out.ctypes.data, nthreads))
+    return out
+
+
+def qbl_sha256(data: bytes) -> bytes:
+    buf = np.frombuffer(bytes(data), np.uint8) if len(data) else np.zeros(1, np.uint8)
+    out = (ctypes.c_uint8 * 32)()
+    _check(_lib.qbl_sha256(buf.ctypes.data, len(data), ctypes.addressof(out)))
+    return bytes(out)
+
+
+def qbl_dequantize(qtype: int, blocks, n: int, k: int) -> np.ndarray:
+    blocks = _host(blocks, np.uint8)
+    out = np.empty((n, k), np.float32)
+    _check(_lib.qbl_dequantize(qtype, blocks.ctypes.data, n, k, out.ctypes.data))
+    return out
+
+
+# -- base ------------------------------------------------------------------------
+def qbl_base_load(linears) -> int:
+    """linears: sequence of (qtype, n_out, k_in, blocks uint8 array)."""
+    keep = [_host(b, np.uint8) for (_, _, _, b) in linears]
+    descs = (qbl_linear_desc * len(linears))()
+    for i, ((qt, n, k, _), b) in enumerate(zip(linears, keep)):
+        descs[i].qtype, descs[i].reserved, descs[i].n_out, descs[i].k_in = qt, 0, n, k
+        descs[i].blocks, descs[i].nbytes = b.ctypes.data, b.nbytes
+    h = ctypes.c_void_p()
+    _check(_lib.qbl_base_load(ctypes.addressof(descs), len(linears), ctypes.byref(h)))
+    return h.value
+
+
+def qbl_base_hash(base) -> bytes:
+    out = (ctypes.c_uint8 * 32)()
+    _check(_lib.qbl_base_hash(base, ctypes.addressof(out)))
+    return bytes(out)
+
+
+def qbl_base_count(base) -> int:
+    n = ctypes.c_int32()
+    _check(_lib.qbl_base_count(base, ctypes.addressof(n)))
+    return n.value
+
+
+def qbl_base_info(base, linear: int):
+    qt, n, k = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.qbl_base_info(base, linear, ctypes.addressof(qt), ctypes.addressof(n),
+                              ctypes.addressof(k)))
+    return qt.value, n.value, k.value
+
+
+def qbl_base_free(base) -> None:
+    _check(_lib.qbl_base_free(base))
+
+
+# -- adapters --------------------------------------------------------------------
+def qbl_adapter_load(base, entries) -> int:
+    """entries: sequence of (linear, A (rank x k_in), B (n_out x rank)) host float32."""
+    keep = [(_host(A, np.float32), _host(B, np.float32)) for (_, A, B) in entries]
+    descs = (qbl_lora_desc * max(1, len(entries)))()
+    for i, ((lin, _, _), (A, B)) in enumerate(zip(entries, keep)):
+        if A.ndim != 2 or B.ndim != 2 or A.shape[0] != B.shape[1]:
+            raise ValueError("A must be rank x k_in and B n_out x rank")
+        descs[i].linear, descs[i].rank = lin, A.shape[0]
+        descs[i].A, descs[i].B = A.ctypes.data, B.ctypes.data
+    h = ctypes.c_void_p()
+    _check(_lib.qbl_adapter_load(base, ctypes.addressof(descs), len(entries), ctypes.byref(h)))
+    return h.value
+
+
+def qbl_adapter_digest(adapter) -> bytes:
+    out = (ctypes.c_uint8 * 32)()
+    _check(_lib.qbl_adapter_digest(adapter, ctypes.addressof(out)))
+    return bytes(out)
+
+
+def qbl_adapter_free(adapter) -> None:
+    _check(_lib.qbl_adapter_free(adapter))
+
+
+# -- compositions ----------------------------------------------------------------
+def qbl_comp_create(base) -> int:
+    h = ctypes.c_void_p()
+    _check(_lib.qbl_comp_create(base, ctypes.byref(h)))
+    return h.value
+
+
+def qbl_comp_attach(comp, adapters, scales) -> None:
+    n = len(adapters)
+    arr = (ctypes.c_void_p * max(1, n))(*adapters)
+    sc = np.ascontiguousarray(scales, np.float32)
+    if sc.size != n:
+        raise ValueError("one scale per adapter")
+    _check(_lib.qbl_comp_attach(comp, ctypes.addressof(arr), sc.ctypes.data if n else None, n))
+
+
+def qbl_comp_clear(comp) -> None:
+    _check(_lib.qbl_comp_clear(comp))
+
+
+def qbl_comp_count(comp) -> int:
+    n = ctypes.c_int32()
+    _check(_lib.qbl_comp_count(comp, ctypes.addressof(n)))
+    return n.value
+
+
+def qbl_comp_free(comp) -> None:
+    _check(_lib.qbl_comp_free(comp))
+
+
+# -- runs ------------------------------------------------------------------------
+def qbl_workspace_bytes(comp, op: int, index: int = 0, m: int = 1) -> int:
+    out = ctypes.c_int64()
+    _check(_lib.qbl_workspace_bytes(comp, op, index, m, ctypes.addressof(out)))
+    return out.value
+
+
+def workspace(comp, op: int, index: int = 0, m: int = 1, device=None):
+    """A device byte buffer of the size qbl_workspace_bytes reports (None if 0)."""
+    import torch
+    nb = qbl_workspace_bytes(comp, op, index, m)
+    if nb == 0:
+        return None
+    return torch.empty(nb, dtype=torch.uint8, device=device or "cuda")
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _dev_ptr(ws), ws.numel() * ws.element_size()
+
+
+def qbl_linear(comp, linear: int, x, y, batch: int, ws=None, stream=None) -> None:
+    import torch
+    wp, wb = _ws(ws)
+    _check(_lib.qbl_linear(comp, linear, _dev_ptr(x, torch.float32), _dev_ptr(y, torch.float32),
+                           batch, wp, wb, _stream(stream)))
+
+
+def qbl_linear_jit(comp, linear: int, x_bf16, y, m: int, ws=None, stream=None) -> None:
+    import torch
+    if x_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("x must hold bfloat16 bit patterns")
+    wp, wb = _ws(ws)
+    _check(_lib.qbl_linear_jit(comp, linear, _dev_ptr(x_bf16), _dev_ptr(y, torch.float32), m,
+                               wp, wb, _stream(stream)))
+
+
+def qbl_block(comp, block: int, x, y, ws=None, stream=None) -> None:
+    import torch
+    wp, wb = _ws(ws)
+    _check(_lib.qbl_block(comp, block, _dev_ptr(x, torch.float32), _dev_ptr(y, torch.float32),
+                          wp, wb, _stream(stream)))
+
+
+def qbl_decode(comp, first_block: int, n_blocks: int, x0, y_tokens, n_tokens: int, ws=None,
+               stream=None) -> None:
+    import torch
+    wp, wb = _ws(ws)
+    _check(_lib.qbl_decode(comp, first_block, n_blocks, _dev_ptr(x0, torch.float32),
+                           _dev_ptr(y_tokens, torch.float32), n_tokens, wp, wb, _stream(stream)))
+
+
+# -- timing ----------------------------------------------------------------------
+KIND_GEMV, KIND_PREP, KIND_JIT = 0, 1, 2
+
+
+def qbl_profile_enable(on: bool) -> None:
+    _check(_lib.qbl_profile_enable(1 if on else 0))
+
+
+def qbl_profile_read(kind: int):
+    """(launches, total_ms) of one kernel kind since timing was enabled."""
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(_lib.qbl_profile_read(kind, ctypes.addressof(n), ctypes.addressof(ms)))
+    return n.value, ms.value

@@ -1,0 +1,96 @@
+// Launch interface between the host runtime and the gfx950 kernels.
+// Internal to the library: not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qbl {
+
+constexpr int QBL_FMT_Q8 = 1;  // same values as QBL_Q8_0 / QBL_Q4_SM of the C ABI
+constexpr int QBL_FMT_Q4 = 2;
+constexpr int kMaxAdapters = 8;
+constexpr int kMaxSegs = 3;                        // linears sharing one input in one launch
+constexpr int kMaxPrepEntries = kMaxSegs * kMaxAdapters;
+
+// The adapters of one linear in list order, as the expand needs them.
+struct LoraSeg {
+  int n_ad;
+  int toff[kMaxAdapters];    // offset of t_i within a batch row of the t buffer
+  int rank[kMaxAdapters];
+  float scale[kMaxAdapters];
+  const float* B[kMaxAdapters];  // n_out x rank, row-major
+};
+
+// One linear of a fused GEMV launch.
+struct GemvSeg {
+  const uint8_t* qs;   // q8_0: int8 [n][k]; q4_sm: packed nibbles [n][k/2]
+  const void* sc;      // q8_0: fp16 d [n][k/32]; q4_sm: uint32 (d | m << 16) [n][k/32]
+  float* y;            // [batch][y_stride]
+  int64_t y_stride;
+  int n;
+  int wg_begin;        // first workgroup of this segment
+  LoraSeg lora;
+};
+
+struct GemvArgs {
+  GemvSeg seg[kMaxSegs];
+  int nseg;
+  int qtype;
+  int k;
+  int kt;              // input-tile width staged in LDS
+  int batch;
+  int rpw;             // rows per wave
+  const float* x;      // [batch][x_stride]
+  int64_t x_stride;
+  const float* t;      // [batch][t_stride] shrink results (may be null when no adapters)
+  int t_stride;
+  int grid;
+};
+
+// One (adapter, linear) pair whose shrink t = A x a prep launch computes.
+struct PrepEntry {
+  const float* A;      // rank x k
+  int rank;
+  int toff;
+};
+
+// Input glue + LoRA shrink.  xin = c * (v0 + v1 + v2) with c = rms scale or 1.
+struct PrepArgs {
+  const float* v[3];
+  int nv;
+  int rms;             // 1: c = 1/sqrt(mean(s^2) + 1e-6) of the summed vector (batch 1 only)
+  int batch;
+  int k;
+  int64_t v_stride;    // between batch rows of the inputs
+  float* xin;          // [batch][k] or null
+  float* t;            // [batch][T] or null
+  int T;
+  int n_ent;
+  int rows_total;      // sum of entry ranks
+  PrepEntry ent[kMaxPrepEntries];
+};
+
+// JIT prefill: Y[m][n] = sum_k X[m][k] * Weff[n][k], Weff built tile by tile.
+struct JitArgs {
+  int qtype;
+  const uint8_t* qs;
+  const void* sc;
+  int n, k, m;
+  const uint16_t* X;   // bf16 [m][k]
+  float* Y;            // [m][n]
+  int n_ad;
+  const float* A[kMaxAdapters];  // rank x k fp32
+  const float* B[kMaxAdapters];  // n x rank fp32
+  int rank[kMaxAdapters];
+  float scale[kMaxAdapters];
+  int total_rank;
+  uint16_t* ws;        // scratch for the staged bf16 factors (see launch_jit)
+};
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
+hipError_t launch_gemv(GemvArgs& a, hipStream_t s);
+hipError_t launch_jit(const JitArgs& a, hipStream_t s);
+int64_t jit_workspace_bytes(int n, int k, int total_rank);
+
+}  // namespace qbl

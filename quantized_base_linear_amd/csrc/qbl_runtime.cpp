@@ -1,0 +1,978 @@
+// The C ABI of include/qbl.h: immutable bases, refcounted adapters, compositions
+// with an atomically replaced adapter list, and the launch planning of the
+// decode and prefill paths.
+//
+// Lifecycle follows "Deep Technical Design: Exact, Atomic, Reversible
+// Specialist Overlays", section 6: validate everything first, stage the
+// adapter in its own device arena, then commit with one atomic pointer swap;
+// deactivation only drops references, the base bytes are never written
+// (section 2).  Adapters are bound to the base they were loaded against, as
+// the "LoRA adapters" blueprint reports for llama.cpp.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/qbl.h"
+#include "qbl_host.h"
+#include "qbl_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+qbl_status fail(qbl_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+qbl_status hip_fail(hipError_t e, const char* what) {
+  return fail(QBL_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define QBL_TRY(...)                                                     \
+  try {                                                                  \
+    __VA_ARGS__                                                          \
+  } catch (const std::bad_alloc&) {                                      \
+    return fail(QBL_E_NOMEM, "host allocation failed");                  \
+  } catch (...) {                                                        \
+    return fail(QBL_E_ARG, "unexpected internal exception");             \
+  }
+
+constexpr int64_t kAlign = 256;
+int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool all_finite(const float* p, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (!std::isfinite(p[i])) return false;
+  return true;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- objects ---
+
+struct DevLinear {
+  int qtype;
+  int64_t n, k;
+  uint8_t* qs;
+  uint8_t* sc;
+  int64_t qs_bytes, sc_bytes;
+  void* mem;
+};
+
+struct qbl_base {
+  int device = 0;
+  std::vector<DevLinear> lin;
+  std::atomic<int> refs{0};
+};
+
+struct AdEntry {
+  int linear;
+  int rank;
+  float* A;  // device rank x k
+  float* B;  // device n x rank
+};
+
+struct AdapterImpl {
+  qbl_base* base = nullptr;
+  std::vector<AdEntry> ent;
+  std::vector<int> slot;  // per base linear: index into ent, or -1
+  uint8_t digest[32] = {};
+  void* mem = nullptr;
+  ~AdapterImpl() {
+    if (mem) {
+      int cur = 0;
+      hipGetDevice(&cur);
+      hipSetDevice(base->device);
+      hipFree(mem);
+      hipSetDevice(cur);
+    }
+    if (base) base->refs.fetch_sub(1);
+  }
+};
+
+struct qbl_adapter {
+  std::shared_ptr<AdapterImpl> impl;
+};
+
+struct LoraRef {
+  const float* A;
+  const float* B;
+  int rank;
+  float scale;
+};
+
+// One attached list.  Immutable once published; freed when no composition or
+// run holds it, after the work enqueued on every stream that used it is done.
+struct ListImpl {
+  std::vector<std::shared_ptr<AdapterImpl>> ads;  // effective entries (scale != 0), in order
+  std::vector<float> scales;
+  std::vector<const AdapterImpl*> in_ads;         // as attached, for the idempotency check
+  std::vector<float> in_scales;
+  std::vector<std::vector<LoraRef>> plan;         // per linear, in list order
+  std::vector<int> total_rank;                    // per linear
+  int device = 0;
+  std::mutex ev_mu;
+  std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
+
+  void mark_use(hipStream_t st) {
+    std::lock_guard<std::mutex> g(ev_mu);
+    for (auto& u : uses)
+      if (u.first == st) {
+        hipEventRecord(u.second, st);
+        return;
+      }
+    hipEvent_t ev;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess) {
+      hipEventRecord(ev, st);
+      uses.emplace_back(st, ev);
+    } else {
+      hipStreamSynchronize(st);  // cannot track: make the use complete now
+    }
+  }
+  ~ListImpl() {
+    for (auto& u : uses) {
+      hipEventSynchronize(u.second);
+      hipEventDestroy(u.second);
+    }
+  }
+};
+
+struct qbl_comp {
+  qbl_base* base = nullptr;
+  std::mutex mu;
+  std::shared_ptr<ListImpl> list;  // read and replaced with std::atomic_load / atomic_store
+};
+
+namespace {
+
+std::shared_ptr<ListImpl> empty_list(const qbl_base* b) {
+  auto L = std::make_shared<ListImpl>();
+  L->device = b->device;
+  L->plan.assign(b->lin.size(), {});
+  L->total_rank.assign(b->lin.size(), 0);
+  return L;
+}
+
+qbl_status check_device(const qbl_base* b) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(QBL_E_DEVICE, "no HIP device");
+  if (cur != b->device)
+    return fail(QBL_E_ARG, "current HIP device %d is not the base's device %d", cur, b->device);
+  return QBL_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- utilities ---
+
+extern "C" const char* qbl_last_error(void) { return g_err.c_str(); }
+extern "C" int32_t qbl_abi_version(void) { return QBL_ABI_VERSION; }
+extern "C" int64_t qbl_block_bytes(int32_t qtype) {
+  return qtype == QBL_Q8_0 ? 34 : qtype == QBL_Q4_SM ? 20 : 0;
+}
+
+extern "C" qbl_status qbl_sha256(const void* data, int64_t n, uint8_t sha256_out[32]) {
+  if ((!data && n) || n < 0 || !sha256_out) return fail(QBL_E_ARG, "bad arguments");
+  qbl::Sha256 h;
+  h.update(data, (size_t)n);
+  h.final(sha256_out);
+  return QBL_OK;
+}
+
+static qbl_status check_qshape(int32_t qtype, int64_t n, int64_t k) {
+  if (!qbl_block_bytes(qtype)) return fail(QBL_E_FORMAT, "unknown quantisation type %d", qtype);
+  if (n <= 0 || k <= 0) return fail(QBL_E_SHAPE, "non-positive shape %lld x %lld", (long long)n, (long long)k);
+  if (k % 32) return fail(QBL_E_FORMAT, "k_in=%lld is not a multiple of 32", (long long)k);
+  if (k > QBL_MAX_K) return fail(QBL_E_LIMIT, "k_in=%lld above %d", (long long)k, QBL_MAX_K);
+  if (n > (int64_t)1 << 30) return fail(QBL_E_LIMIT, "n_out=%lld too large", (long long)n);
+  return QBL_OK;
+}
+
+extern "C" qbl_status qbl_quantize(int32_t qtype, const float* w, int64_t n, int64_t k,
+                                   void* blocks_out, int32_t nthreads) {
+  QBL_TRY({
+    if (qbl_status s = check_qshape(qtype, n, k)) return s;
+    if (!w || !blocks_out) return fail(QBL_E_ARG, "null pointer");
+    const int s = qbl::quantize_rows(qtype, w, n, k, static_cast<uint8_t*>(blocks_out), nthreads);
+    if (s == QBL_E_NONFINITE) return fail(s, "non-finite weight");
+    if (s == QBL_E_LIMIT) return fail(s, "block scale or minimum overflows fp16");
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_dequantize(int32_t qtype, const void* blocks, int64_t n, int64_t k,
+                                     float* w_out) {
+  QBL_TRY({
+    if (qbl_status s = check_qshape(qtype, n, k)) return s;
+    if (!blocks || !w_out) return fail(QBL_E_ARG, "null pointer");
+    return qbl::dequantize_rows(qtype, static_cast<const uint8_t*>(blocks), n, k, w_out);
+  })
+}
+
+// ------------------------------------------------------------------ base ---
+
+extern "C" qbl_status qbl_base_load(const qbl_linear_desc* descs, int32_t n_linears,
+                                    qbl_base** out) {
+  QBL_TRY({
+    if (!descs || !out || n_linears <= 0) return fail(QBL_E_ARG, "need descs, out and n_linears >= 1");
+    for (int i = 0; i < n_linears; ++i) {
+      const qbl_linear_desc& d = descs[i];
+      if (qbl_status s = check_qshape(d.qtype, d.n_out, d.k_in))
+        return fail(s, "linear %d: %s", i, qbl_last_error());
+      if (d.reserved != 0) return fail(QBL_E_ARG, "linear %d: reserved field must be 0", i);
+      if (!d.blocks) return fail(QBL_E_ARG, "linear %d: null blocks", i);
+      const int64_t want = d.n_out * (d.k_in / 32) * qbl_block_bytes(d.qtype);
+      if (d.nbytes != want)
+        return fail(QBL_E_FORMAT, "linear %d: nbytes %lld, expected %lld", i, (long long)d.nbytes,
+                    (long long)want);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::unique_ptr<qbl_base> b(new qbl_base);
+    b->device = dev;
+    b->lin.reserve(n_linears);
+    auto release = [&]() {
+      for (auto& L : b->lin) hipFree(L.mem);
+      b->lin.clear();
+    };
+    std::vector<uint8_t> stage;
+    for (int i = 0; i < n_linears; ++i) {
+      const qbl_linear_desc& d = descs[i];
+      DevLinear L{};
+      L.qtype = d.qtype;
+      L.n = d.n_out;
+      L.k = d.k_in;
+      L.qs_bytes = qbl::qs_bytes(d.qtype, d.n_out, d.k_in);
+      L.sc_bytes = qbl::sc_bytes(d.qtype, d.n_out, d.k_in);
+      const int64_t total = align_up(L.qs_bytes) + align_up(L.sc_bytes);
+      e = hipMalloc(&L.mem, (size_t)total);
+      if (e != hipSuccess) {
+        release();
+        return fail(QBL_E_NOMEM, "linear %d: hipMalloc(%lld): %s", i, (long long)total, hipGetErrorString(e));
+      }
+      L.qs = static_cast<uint8_t*>(L.mem);
+      L.sc = L.qs + align_up(L.qs_bytes);
+      b->lin.push_back(L);
+      stage.resize((size_t)total);
+      qbl::repack_rows(d.qtype, static_cast<const uint8_t*>(d.blocks), d.n_out, d.k_in, stage.data(),
+                       stage.data() + align_up(L.qs_bytes), 0);
+      e = hipMemcpy(L.mem, stage.data(), (size_t)total, hipMemcpyHostToDevice);
+      if (e != hipSuccess) {
+        release();
+        return hip_fail(e, "hipMemcpy of base linear");
+      }
+    }
+    *out = b.release();
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_base_count(const qbl_base* base, int32_t* n_linears) {
+  if (!base || !n_linears) return fail(QBL_E_ARG, "null pointer");
+  *n_linears = (int32_t)base->lin.size();
+  return QBL_OK;
+}
+
+extern "C" qbl_status qbl_base_info(const qbl_base* base, int32_t linear, int32_t* qtype,
+                                    int64_t* n_out, int64_t* k_in) {
+  if (!base) return fail(QBL_E_ARG, "null base");
+  if (linear < 0 || linear >= (int32_t)base->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", linear);
+  const DevLinear& L = base->lin[linear];
+  if (qtype) *qtype = L.qtype;
+  if (n_out) *n_out = L.n;
+  if (k_in) *k_in = L.k;
+  return QBL_OK;
+}
+
+extern "C" qbl_status qbl_base_hash(qbl_base* base, uint8_t sha256_out[32]) {
+  QBL_TRY({
+    if (!base || !sha256_out) return fail(QBL_E_ARG, "null pointer");
+    if (qbl_status s = check_device(base)) return s;
+    const int64_t n = (int64_t)base->lin.size();
+    std::vector<uint8_t> digests((size_t)n * 32);
+    std::vector<int> err((size_t)n, 0);
+    qbl::parallel_for(n, std::min(qbl::default_threads(), 16), [&](int64_t i) {
+      hipSetDevice(base->device);
+      const DevLinear& L = base->lin[(size_t)i];
+      std::vector<uint8_t> buf((size_t)(L.qs_bytes + L.sc_bytes));
+      if (hipMemcpy(buf.data(), L.qs, (size_t)L.qs_bytes, hipMemcpyDeviceToHost) != hipSuccess ||
+          hipMemcpy(buf.data() + L.qs_bytes, L.sc, (size_t)L.sc_bytes, hipMemcpyDeviceToHost) !=
+              hipSuccess) {
+        err[(size_t)i] = 1;
+        return;
+      }
+      qbl::Sha256 h;
+      h.update(buf.data(), buf.size());
+      h.final(&digests[(size_t)i * 32]);
+    });
+    for (int x : err)
+      if (x) return fail(QBL_E_DEVICE, "reading base bytes back failed");
+    qbl::Sha256 h;
+    h.update(digests.data(), digests.size());
+    h.final(sha256_out);
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_base_free(qbl_base* base) {
+  if (!base) return fail(QBL_E_ARG, "null base");
+  if (base->refs.load() != 0)
+    return fail(QBL_E_BUSY, "base still referenced by %d adapter(s)/composition(s)", base->refs.load());
+  int cur = 0;
+  hipGetDevice(&cur);
+  hipSetDevice(base->device);
+  for (auto& L : base->lin) hipFree(L.mem);
+  hipSetDevice(cur);
+  delete base;
+  return QBL_OK;
+}
+
+// -------------------------------------------------------------- adapters ---
+
+extern "C" qbl_status qbl_adapter_load(qbl_base* base, const qbl_lora_desc* descs, int32_t n,
+                                       qbl_adapter** out) {
+  QBL_TRY({
+    if (!base || !descs || !out) return fail(QBL_E_ARG, "null pointer");
+    if (n <= 0) return fail(QBL_E_ARG, "an adapter must target at least one linear");
+    if (qbl_status s = check_device(base)) return s;
+    const int nl = (int)base->lin.size();
+    std::vector<char> seen((size_t)nl, 0);
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+      const qbl_lora_desc& d = descs[i];
+      if (d.linear < 0 || d.linear >= nl)
+        return fail(QBL_E_SHAPE, "entry %d targets linear %d; the base has %d", i, d.linear, nl);
+      if (seen[(size_t)d.linear]) return fail(QBL_E_DUPLICATE, "linear %d appears twice", d.linear);
+      seen[(size_t)d.linear] = 1;
+      if (d.rank < 1 || d.rank > QBL_MAX_RANK)
+        return fail(QBL_E_LIMIT, "entry %d: rank %d outside 1..%d", i, d.rank, QBL_MAX_RANK);
+      if (!d.A || !d.B) return fail(QBL_E_ARG, "entry %d: null factor", i);
+      const DevLinear& L = base->lin[(size_t)d.linear];
+      if (!all_finite(d.A, (int64_t)d.rank * L.k) || !all_finite(d.B, L.n * d.rank))
+        return fail(QBL_E_NONFINITE, "entry %d: non-finite value in A or B", i);
+      total += align_up((int64_t)d.rank * L.k * 4) + align_up(L.n * d.rank * 4);
+    }
+    auto impl = std::make_shared<AdapterImpl>();
+    hipError_t e = hipMalloc(&impl->mem, (size_t)total);
+    if (e != hipSuccess) return fail(QBL_E_NOMEM, "hipMalloc(%lld): %s", (long long)total, hipGetErrorString(e));
+    impl->base = base;
+    base->refs.fetch_add(1);
+    impl->slot.assign((size_t)nl, -1);
+    uint8_t* p = static_cast<uint8_t*>(impl->mem);
+    qbl::Sha256 h;
+    for (int i = 0; i < n; ++i) {
+      const qbl_lora_desc& d = descs[i];
+      const DevLinear& L = base->lin[(size_t)d.linear];
+      AdEntry en{d.linear, d.rank, reinterpret_cast<float*>(p), nullptr};
+      p += align_up((int64_t)d.rank * L.k * 4);
+      en.B = reinterpret_cast<float*>(p);
+      p += align_up(L.n * d.rank * 4);
+      const size_t abytes = (size_t)d.rank * L.k * 4, bbytes = (size_t)L.n * d.rank * 4;
+      e = hipMemcpy(en.A, d.A, abytes, hipMemcpyHostToDevice);
+      if (e == hipSuccess) e = hipMemcpy(en.B, d.B, bbytes, hipMemcpyHostToDevice);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpy of adapter");  // impl frees itself
+      const int32_t hdr[2] = {d.linear, d.rank};
+      h.update(hdr, sizeof hdr);
+      h.update(d.A, abytes);
+      h.update(d.B, bbytes);
+      impl->slot[(size_t)d.linear] = (int)impl->ent.size();
+      impl->ent.push_back(en);
+    }
+    h.final(impl->digest);
+    auto* a = new qbl_adapter;
+    a->impl = std::move(impl);
+    *out = a;
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_adapter_digest(const qbl_adapter* adapter, uint8_t sha256_out[32]) {
+  if (!adapter || !sha256_out) return fail(QBL_E_ARG, "null pointer");
+  std::memcpy(sha256_out, adapter->impl->digest, 32);
+  return QBL_OK;
+}
+
+extern "C" qbl_status qbl_adapter_free(qbl_adapter* adapter) {
+  if (!adapter) return fail(QBL_E_ARG, "null adapter");
+  delete adapter;  // the attached lists keep their own references
+  return QBL_OK;
+}
+
+// ---------------------------------------------------------- compositions ---
+
+extern "C" qbl_status qbl_comp_create(qbl_base* base, qbl_comp** out) {
+  QBL_TRY({
+    if (!base || !out) return fail(QBL_E_ARG, "null pointer");
+    auto* c = new qbl_comp;
+    c->base = base;
+    std::atomic_store(&c->list, empty_list(base));
+    base->refs.fetch_add(1);
+    *out = c;
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_comp_attach(qbl_comp* comp, const qbl_adapter* const* list,
+                                      const float* scales, int32_t n) {
+  QBL_TRY({
+    if (!comp) return fail(QBL_E_ARG, "null composition");
+    if (n < 0 || n > QBL_MAX_ADAPTERS) return fail(QBL_E_LIMIT, "list of %d adapters; at most %d", n, QBL_MAX_ADAPTERS);
+    if (n > 0 && (!list || !scales)) return fail(QBL_E_ARG, "null list or scales");
+    const qbl_base* base = comp->base;
+    const size_t nl = base->lin.size();
+    // -- validation: nothing changes unless every check passes
+    for (int i = 0; i < n; ++i) {
+      if (!list[i]) return fail(QBL_E_ARG, "entry %d is null", i);
+      if (list[i]->impl->base != base) return fail(QBL_E_FOREIGN, "entry %d belongs to another base", i);
+      if (!std::isfinite(scales[i])) return fail(QBL_E_NONFINITE, "scale %d is not finite", i);
+      for (int j = 0; j < i; ++j)
+        if (list[j] == list[i] || list[j]->impl == list[i]->impl)
+          return fail(QBL_E_DUPLICATE, "entries %d and %d are the same adapter", j, i);
+    }
+    std::vector<int> rank_sum(nl, 0);
+    for (int i = 0; i < n; ++i) {
+      if (scales[i] == 0.0f) continue;
+      for (const AdEntry& e : list[i]->impl->ent) rank_sum[(size_t)e.linear] += e.rank;
+    }
+    for (size_t l = 0; l < nl; ++l)
+      if (rank_sum[l] > QBL_MAX_TOTAL_RANK)
+        return fail(QBL_E_LIMIT, "linear %zu: summed rank %d above %d", l, rank_sum[l], QBL_MAX_TOTAL_RANK);
+
+    std::lock_guard<std::mutex> g(comp->mu);
+    // -- idempotency: the same list and scales already in place
+    {
+      auto cur = std::atomic_load(&comp->list);
+      bool same = (int)cur->in_ads.size() == n;
+      for (int i = 0; same && i < n; ++i)
+        same = cur->in_ads[(size_t)i] == list[i]->impl.get() && cur->in_scales[(size_t)i] == scales[i];
+      if (same) return QBL_OK;
+    }
+    // -- staging: build the new immutable list
+    auto L = empty_list(base);
+    for (int i = 0; i < n; ++i) {
+      L->in_ads.push_back(list[i]->impl.get());
+      L->in_scales.push_back(scales[i]);
+      if (scales[i] == 0.0f) continue;  // a zero-scale entry contributes nothing
+      L->ads.push_back(list[i]->impl);
+      L->scales.push_back(scales[i]);
+      for (const AdEntry& e : list[i]->impl->ent) {
+        L->plan[(size_t)e.linear].push_back(LoraRef{e.A, e.B, e.rank, scales[i]});
+        L->total_rank[(size_t)e.linear] += e.rank;
+      }
+    }
+    // keep the refs of adapters in in_ads alive via ads only for non-zero entries;
+    // zero-scale entries are compared by address, so hold them as well
+    for (int i = 0; i < n; ++i)
+      if (scales[i] == 0.0f) L->ads.push_back(list[i]->impl);
+    // -- commit: one atomic exchange; the old list retires when its last user drops it
+    std::atomic_store(&comp->list, std::move(L));
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_comp_clear(qbl_comp* comp) {
+  QBL_TRY({
+    if (!comp) return fail(QBL_E_ARG, "null composition");
+    std::lock_guard<std::mutex> g(comp->mu);
+    if (std::atomic_load(&comp->list)->in_ads.empty()) return QBL_OK;
+    std::atomic_store(&comp->list, empty_list(comp->base));
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_comp_count(const qbl_comp* comp, int32_t* n) {
+  if (!comp || !n) return fail(QBL_E_ARG, "null pointer");
+  *n = (int32_t)std::atomic_load(&comp->list)->scales.size();
+  return QBL_OK;
+}
+
+extern "C" qbl_status qbl_comp_free(qbl_comp* comp) {
+  if (!comp) return fail(QBL_E_ARG, "null composition");
+  {
+    std::lock_guard<std::mutex> g(comp->mu);
+    std::atomic_store(&comp->list, std::shared_ptr<ListImpl>());
+  }
+  comp->base->refs.fetch_sub(1);
+  delete comp;
+  return QBL_OK;
+}
+
+// ---------------------------------------------------------------- timing ---
+
+namespace {
+
+struct Profiler {
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<Rec> recs;
+};
+
+Profiler& profiler() {
+  static Profiler p;
+  return p;
+}
+
+// Brackets one kernel launch with timing events while timing is enabled.
+class KernelTimer {
+ public:
+  KernelTimer(int kind, hipStream_t st) : kind_(kind), st_(st) {
+    if (!profiler().on.load()) return;
+    if (hipEventCreate(&a_) != hipSuccess || hipEventCreate(&b_) != hipSuccess) return;
+    hipEventRecord(a_, st_);
+  }
+  void stop() {
+    if (!a_ || !b_) return;
+    hipEventRecord(b_, st_);
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.recs.push_back(Profiler::Rec{kind_, a_, b_});
+    a_ = b_ = nullptr;
+  }
+  ~KernelTimer() {
+    if (a_) hipEventDestroy(a_);
+    if (b_) hipEventDestroy(b_);
+  }
+
+ private:
+  int kind_;
+  hipStream_t st_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
+void clear_records(Profiler& p) {
+  for (auto& r : p.recs) {
+    hipEventSynchronize(r.b);
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  p.recs.clear();
+}
+
+}  // namespace
+
+extern "C" qbl_status qbl_profile_enable(int32_t on) {
+  QBL_TRY({
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> g(p.mu);
+    clear_records(p);
+    p.on.store(on != 0);
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_profile_read(int32_t kind, int64_t* launches, double* total_ms) {
+  QBL_TRY({
+    if (!launches || !total_ms) return fail(QBL_E_ARG, "null pointer");
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> g(p.mu);
+    int64_t n = 0;
+    double ms = 0.0;
+    for (auto& r : p.recs) {
+      if (r.kind != kind) continue;
+      hipError_t e = hipEventSynchronize(r.b);
+      float t = 0.0f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+      if (e != hipSuccess) return hip_fail(e, "reading timing events");
+      ++n;
+      ms += t;
+    }
+    *launches = n;
+    *total_ms = ms;
+    return QBL_OK;
+  })
+}
+
+// ------------------------------------------------------------------ runs ---
+
+namespace {
+
+struct Block {
+  int first;  // linear index of q
+  int64_t d, h;
+};
+
+qbl_status block_shape(const qbl_base* b, int blk, Block* out) {
+  const int first = 7 * blk;
+  if (blk < 0 || first + 7 > (int)b->lin.size())
+    return fail(QBL_E_ARG, "block %d needs linears %d..%d; the base has %zu", blk, first, first + 6,
+                b->lin.size());
+  const DevLinear* L = &b->lin[(size_t)first];
+  const int64_t d = L[0].k, h = L[4].n;
+  for (int i = 0; i < 4; ++i)
+    if (L[i].n != d || L[i].k != d) return fail(QBL_E_SHAPE, "block %d: q/k/v/o must be d x d", blk);
+  if (L[4].k != d || L[5].n != h || L[5].k != d || L[6].n != d || L[6].k != h)
+    return fail(QBL_E_SHAPE, "block %d: gate/up must be h x d and down d x h", blk);
+  *out = Block{first, d, h};
+  return QBL_OK;
+}
+
+// Layout of the block/decode workspace (floats, 256-byte aligned pieces).
+struct BlockWs {
+  float *xin, *t, *q, *k, *v, *a, *g, *u, *dd;
+  int64_t bytes;
+};
+
+BlockWs block_ws(void* ws, int64_t d, int64_t h, int64_t tmax) {
+  BlockWs w{};
+  int64_t off = 0;
+  auto take = [&](int64_t floats) {
+    float* p = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + off) : nullptr;
+    off += align_up(floats * 4);
+    return p;
+  };
+  const int64_t m = std::max(d, h);
+  w.xin = take(m);
+  w.t = take(std::max<int64_t>(tmax, 1));
+  w.q = take(d);
+  w.k = take(d);
+  w.v = take(d);
+  w.a = take(d);
+  w.g = take(h);
+  w.u = take(h);
+  w.dd = take(d);
+  w.bytes = off;
+  return w;
+}
+
+int group_rank(const ListImpl* L, const int* lin, int nlin) {
+  int t = 0;
+  for (int i = 0; i < nlin; ++i) t += L->total_rank[(size_t)lin[i]];
+  return t;
+}
+
+// Max shrink width over the four launch groups of every block in range.
+int blocks_tmax(const ListImpl* L, int first_block, int n_blocks) {
+  int tmax = 0;
+  for (int b = first_block; b < first_block + n_blocks; ++b) {
+    const int f = 7 * b;
+    const int g0[3] = {f, f + 1, f + 2}, g1[1] = {f + 3}, g2[2] = {f + 4, f + 5}, g3[1] = {f + 6};
+    tmax = std::max({tmax, group_rank(L, g0, 3), group_rank(L, g1, 1), group_rank(L, g2, 2),
+                     group_rank(L, g3, 1)});
+  }
+  return tmax;
+}
+
+// One launch group: linears sharing one input.  Input = c * (v0 + v1 + v2) with
+// c the RMS scale when rms != 0.  Launches the prep kernel (glue and/or shrink)
+// when needed, then one fused GEMV per quantisation type present.
+qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, float* const* outs,
+                     int nlin, const float* const* vin, int nv, int rms, int batch, int64_t v_stride,
+                     float* xin_buf, float* t_buf, hipStream_t st) {
+  const int64_t K = base->lin[(size_t)lin[0]].k;
+  int T = 0;
+  qbl::PrepArgs p{};
+  for (int i = 0; i < nlin; ++i) {
+    for (const LoraRef& r : L->plan[(size_t)lin[i]]) {
+      p.ent[p.n_ent++] = qbl::PrepEntry{r.A, r.rank, T};
+      T += r.rank;
+    }
+  }
+  const bool glue = rms || nv > 1;
+  const float* x = vin[0];
+  if (glue || T > 0) {
+    for (int i = 0; i < nv; ++i) p.v[i] = vin[i];
+    p.nv = nv;
+    p.rms = rms;
+    p.batch = batch;
+    p.k = (int)K;
+    p.v_stride = v_stride;
+    p.xin = glue ? xin_buf : nullptr;
+    p.t = T > 0 ? t_buf : nullptr;
+    p.T = T;
+    p.rows_total = T;
+    KernelTimer tm(1, st);
+    hipError_t e = qbl::launch_prep(p, st);
+    if (e != hipSuccess) return hip_fail(e, "prep launch");
+    tm.stop();
+    if (glue) x = xin_buf;
+  }
+  for (int qt = QBL_Q8_0; qt <= QBL_Q4_SM; ++qt) {
+    qbl::GemvArgs a{};
+    int toff = 0;
+    for (int i = 0; i < nlin; ++i) {
+      const DevLinear& D = base->lin[(size_t)lin[i]];
+      const int this_rank = L->total_rank[(size_t)lin[i]];
+      if (D.qtype != qt) {
+        toff += this_rank;
+        continue;
+      }
+      qbl::GemvSeg& s = a.seg[a.nseg++];
+      s.qs = D.qs;
+      s.sc = D.sc;
+      s.y = outs[i];
+      s.y_stride = D.n;
+      s.n = (int)D.n;
+      int o = toff;
+      for (const LoraRef& r : L->plan[(size_t)lin[i]]) {
+        const int j = s.lora.n_ad++;
+        s.lora.toff[j] = o;
+        s.lora.rank[j] = r.rank;
+        s.lora.scale[j] = r.scale;
+        s.lora.B[j] = r.B;
+        o += r.rank;
+      }
+      toff += this_rank;
+    }
+    if (!a.nseg) continue;
+    a.qtype = qt;
+    a.k = (int)K;
+    a.batch = batch;
+    a.x = x;
+    a.x_stride = glue ? K : v_stride;
+    a.t = T > 0 ? t_buf : nullptr;
+    a.t_stride = T;
+    KernelTimer tm(0, st);
+    hipError_t e = qbl::launch_gemv(a, st);
+    if (e != hipSuccess) return hip_fail(e, "gemv launch");
+    tm.stop();
+  }
+  return QBL_OK;
+}
+
+// rms of one vector into y (a prep launch with no adapter rows)
+qbl_status run_rms(const float* v, int64_t n, float* y, hipStream_t st) {
+  qbl::PrepArgs p{};
+  p.v[0] = v;
+  p.nv = 1;
+  p.rms = 1;
+  p.batch = 1;
+  p.k = (int)n;
+  p.v_stride = n;
+  p.xin = y;
+  KernelTimer tm(1, st);
+  hipError_t e = qbl::launch_prep(p, st);
+  if (e != hipSuccess) return hip_fail(e, "rms launch");
+  tm.stop();
+  return QBL_OK;
+}
+
+// One block; `in` is either a plain input (rms_in = 0) or the previous block's
+// down output that still needs its RMS scale (rms_in = 1).  Leaves d in w.dd.
+qbl_status run_block(const qbl_base* base, const ListImpl* L, const Block& B, const float* in,
+                     int rms_in, const BlockWs& w, hipStream_t st) {
+  const int f = B.first;
+  {
+    const int lin[3] = {f, f + 1, f + 2};
+    float* outs[3] = {w.q, w.k, w.v};
+    const float* v[1] = {in};
+    if (qbl_status s = run_group(base, L, lin, outs, 3, v, 1, rms_in, 1, B.d, w.xin, w.t, st)) return s;
+  }
+  {
+    const int lin[1] = {f + 3};
+    float* outs[1] = {w.a};
+    const float* v[3] = {w.q, w.k, w.v};
+    if (qbl_status s = run_group(base, L, lin, outs, 1, v, 3, 1, 1, B.d, w.xin, w.t, st)) return s;
+  }
+  {
+    const int lin[2] = {f + 4, f + 5};
+    float* outs[2] = {w.g, w.u};
+    const float* v[1] = {w.a};
+    if (qbl_status s = run_group(base, L, lin, outs, 2, v, 1, 1, 1, B.d, w.xin, w.t, st)) return s;
+  }
+  {
+    const int lin[1] = {f + 6};
+    float* outs[1] = {w.dd};
+    const float* v[2] = {w.g, w.u};
+    if (qbl_status s = run_group(base, L, lin, outs, 1, v, 2, 1, 1, B.h, w.xin, w.t, st)) return s;
+  }
+  return QBL_OK;
+}
+
+qbl_status check_ws(void* ws, int64_t ws_bytes, int64_t need) {
+  if (need == 0) return QBL_OK;
+  if (!ws) return fail(QBL_E_BUDGET, "workspace of %lld bytes required", (long long)need);
+  if (ws_bytes < need)
+    return fail(QBL_E_BUDGET, "workspace of %lld bytes given, %lld required", (long long)ws_bytes,
+                (long long)need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(QBL_E_ARG, "workspace not 256-byte aligned");
+  return QBL_OK;
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+}  // namespace
+
+extern "C" qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index,
+                                          int32_t m, int64_t* bytes_out) {
+  QBL_TRY({
+    if (!comp || !bytes_out) return fail(QBL_E_ARG, "null pointer");
+    auto L = std::atomic_load(&comp->list);
+    const qbl_base* b = comp->base;
+    if (op == 0) {
+      if (index < 0 || index >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", index);
+      if (m < 1 || m > QBL_MAX_BATCH) return fail(QBL_E_LIMIT, "batch %d outside 1..%d", m, QBL_MAX_BATCH);
+      *bytes_out = align_up((int64_t)m * L->total_rank[(size_t)index] * 4);
+      return QBL_OK;
+    }
+    if (op == 1) {
+      if (index < 0 || index >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", index);
+      const DevLinear& D = b->lin[(size_t)index];
+      *bytes_out = align_up(qbl::jit_workspace_bytes((int)D.n, (int)D.k, L->total_rank[(size_t)index]));
+      return QBL_OK;
+    }
+    if (op == 2) {
+      const int nb = (int)b->lin.size() / 7;
+      if (nb < 1) return fail(QBL_E_SHAPE, "the base holds no block of 7 linears");
+      int64_t d = 0, h = 0;
+      for (int i = 0; i < nb; ++i) {
+        Block B;
+        if (qbl_status s = block_shape(b, i, &B)) return s;
+        d = std::max(d, B.d);
+        h = std::max(h, B.h);
+      }
+      *bytes_out = block_ws(nullptr, d, h, blocks_tmax(L.get(), 0, nb)).bytes;
+      return QBL_OK;
+    }
+    return fail(QBL_E_ARG, "unknown op %d", op);
+  })
+}
+
+extern "C" qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x, float* y,
+                                 int32_t batch, void* ws, int64_t ws_bytes, void* stream) {
+  QBL_TRY({
+    if (!comp || !x || !y) return fail(QBL_E_ARG, "null pointer");
+    const qbl_base* b = comp->base;
+    if (linear < 0 || linear >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", linear);
+    if (batch < 1 || batch > QBL_MAX_BATCH) return fail(QBL_E_LIMIT, "batch %d outside 1..%d", batch, QBL_MAX_BATCH);
+    if (!aligned16(x) || !aligned16(y)) return fail(QBL_E_ARG, "x and y must be 16-byte aligned");
+    if (x == y) return fail(QBL_E_ARG, "y must not alias x");
+    if (qbl_status s = check_device(b)) return s;
+    std::lock_guard<std::mutex> g(comp->mu);
+    auto L = std::atomic_load(&comp->list);
+    const int T = L->total_rank[(size_t)linear];
+    if (qbl_status s = check_ws(ws, ws_bytes, align_up((int64_t)batch * T * 4))) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int lin[1] = {linear};
+    float* outs[1] = {y};
+    const float* v[1] = {x};
+    const DevLinear& D = b->lin[(size_t)linear];
+    if (qbl_status s = run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr,
+                                 static_cast<float*>(ws), st))
+      return s;
+    if (T > 0) L->mark_use(st);
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint16_t* x_bf16,
+                                     float* y, int32_t m, void* ws, int64_t ws_bytes, void* stream) {
+  QBL_TRY({
+    if (!comp || !x_bf16 || !y) return fail(QBL_E_ARG, "null pointer");
+    const qbl_base* b = comp->base;
+    if (linear < 0 || linear >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", linear);
+    if (m < 1) return fail(QBL_E_ARG, "m must be >= 1");
+    if (!aligned16(x_bf16) || !aligned16(y)) return fail(QBL_E_ARG, "x and y must be 16-byte aligned");
+    if (qbl_status s = check_device(b)) return s;
+    std::lock_guard<std::mutex> g(comp->mu);
+    auto L = std::atomic_load(&comp->list);
+    const DevLinear& D = b->lin[(size_t)linear];
+    const int T = L->total_rank[(size_t)linear];
+    if (qbl_status s = check_ws(ws, ws_bytes, align_up(qbl::jit_workspace_bytes((int)D.n, (int)D.k, T))))
+      return s;
+    qbl::JitArgs a{};
+    a.qtype = D.qtype;
+    a.qs = D.qs;
+    a.sc = D.sc;
+    a.n = (int)D.n;
+    a.k = (int)D.k;
+    a.m = m;
+    a.X = x_bf16;
+    a.Y = y;
+    for (const LoraRef& r : L->plan[(size_t)linear]) {
+      const int j = a.n_ad++;
+      a.A[j] = r.A;
+      a.B[j] = r.B;
+      a.rank[j] = r.rank;
+      a.scale[j] = r.scale;
+    }
+    a.total_rank = T;
+    a.ws = static_cast<uint16_t*>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    KernelTimer tm(2, st);
+    hipError_t e = qbl::launch_jit(a, st);
+    if (e != hipSuccess) return hip_fail(e, "jit launch");
+    tm.stop();
+    if (T > 0) L->mark_use(st);
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_block(qbl_comp* comp, int32_t block, const float* x, float* y, void* ws,
+                                int64_t ws_bytes, void* stream) {
+  QBL_TRY({
+    if (!comp || !x || !y) return fail(QBL_E_ARG, "null pointer");
+    const qbl_base* b = comp->base;
+    Block B;
+    if (qbl_status s = block_shape(b, block, &B)) return s;
+    if (!aligned16(x) || !aligned16(y)) return fail(QBL_E_ARG, "x and y must be 16-byte aligned");
+    if (qbl_status s = check_device(b)) return s;
+    std::lock_guard<std::mutex> g(comp->mu);
+    auto L = std::atomic_load(&comp->list);
+    const BlockWs need = block_ws(nullptr, B.d, B.h, blocks_tmax(L.get(), block, 1));
+    if (qbl_status s = check_ws(ws, ws_bytes, need.bytes)) return s;
+    const BlockWs w = block_ws(ws, B.d, B.h, blocks_tmax(L.get(), block, 1));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (qbl_status s = run_block(b, L.get(), B, x, 0, w, st)) return s;
+    if (qbl_status s = run_rms(w.dd, B.d, y, st)) return s;
+    L->mark_use(st);
+    return QBL_OK;
+  })
+}
+
+extern "C" qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_blocks,
+                                 const float* x0, float* y_tokens, int32_t n_tokens, void* ws,
+                                 int64_t ws_bytes, void* stream) {
+  QBL_TRY({
+    if (!comp || !x0 || !y_tokens) return fail(QBL_E_ARG, "null pointer");
+    if (n_blocks < 1 || n_tokens < 1) return fail(QBL_E_ARG, "n_blocks and n_tokens must be >= 1");
+    const qbl_base* b = comp->base;
+    std::vector<Block> blocks((size_t)n_blocks);
+    for (int i = 0; i < n_blocks; ++i)
+      if (qbl_status s = block_shape(b, first_block + i, &blocks[(size_t)i])) return s;
+    const int64_t d = blocks[0].d;
+    int64_t h = 0;
+    for (auto& B : blocks) {
+      if (B.d != d) return fail(QBL_E_SHAPE, "blocks of different widths in one stack");
+      h = std::max(h, B.h);
+    }
+    if (!aligned16(x0) || !aligned16(y_tokens)) return fail(QBL_E_ARG, "x0 and y must be 16-byte aligned");
+    if (qbl_status s = check_device(b)) return s;
+    std::lock_guard<std::mutex> g(comp->mu);
+    auto L = std::atomic_load(&comp->list);  // one list for the whole call
+    const int tmax = blocks_tmax(L.get(), first_block, n_blocks);
+    if (qbl_status s = check_ws(ws, ws_bytes, block_ws(nullptr, d, h, tmax).bytes)) return s;
+    const BlockWs w = block_ws(ws, d, h, tmax);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int t = 0; t < n_tokens; ++t) {
+      const float* in = t == 0 ? x0 : y_tokens + (int64_t)(t - 1) * d;
+      for (int i = 0; i < n_blocks; ++i) {
+        if (qbl_status s = run_block(b, L.get(), blocks[(size_t)i], i == 0 ? in : w.dd, i == 0 ? 0 : 1, w, st))
+          return s;
+      }
+      if (qbl_status s = run_rms(w.dd, d, y_tokens + (int64_t)t * d, st)) return s;
+    }
+    L->mark_use(st);
+    return QBL_OK;
+  })
+}
