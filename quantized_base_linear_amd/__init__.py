@@ -21,6 +21,10 @@ if not os.path.exists(_SO):
     raise ImportError(f"{_SO} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
                       "or python quantized_base_linear_amd/build.py)")
 
+# torch first: the process then holds exactly one HIP runtime (torch's), which
+# this library binds to when it is loaded.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(_SO)
 
 QBL_OK = 0

@@ -24,7 +24,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kLdsFloats = 16384;  // x tile budget per workgroup (64 KiB)
+constexpr int kLdsFloats = 16384;      // GEMV x tile budget per workgroup (64 KiB)
+constexpr int kPrepLdsFloats = 40960;  // prep input staging budget (160 KiB)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -47,6 +48,17 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// Workgroup-wide sum in a fixed order; every thread receives it.  `red` holds
+// kWaves floats of LDS.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return s;
+}
+
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xFFFFu)));
 }
@@ -55,60 +67,109 @@ __device__ __forceinline__ float ub(uint32_t v, int byte) {
   return (float)((v >> (8 * byte)) & 0xFFu);  // selected into v_cvt_f32_ubyteN
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load of weight bytes: read once, not worth keeping in cache.
+__device__ __forceinline__ uint4 stream_load16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 mul4(float c, float4 a) {
+  return make_float4(c * a.x, c * a.y, c * a.z, c * a.w);
+}
+
 // ---------------------------------------------------------------------------
-// prep: xin = c * ((v0 + v1) + v2); t[b][toff + j] = A[j] . xin[b]
+// prep: s = v0 + v1 + v2 (summed left to right), xin = c * s, with c the RMS
+// scale 1/sqrt(mean(s^2) + 1e-6) when rms is set (batch 1) and 1 otherwise;
+// t[b][toff + j] = A[j] . xin[b].
+//
+// Workgroup g stages the whole summed input in LDS (each workgroup its own
+// copy: the inputs are tens of KiB and L2-resident), computes c, then takes
+// A row g (all batch rows) and slice g of the xin output.  Every load is a
+// 16-byte load, unrolled so many are in flight at once.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float prep_in(const PrepArgs& a, int b, int k) {
-  const int64_t o = (int64_t)b * a.v_stride + k;
-  float s = a.v[0][o];
-  if (a.nv > 1) s += a.v[1][o];
-  if (a.nv > 2) s += a.v[2][o];
+__device__ __forceinline__ float4 prep_in4(const PrepArgs& a, int b, int f) {
+  const int64_t o = (int64_t)b * a.v_stride + 4 * (int64_t)f;
+  float4 s = *reinterpret_cast<const float4*>(a.v[0] + o);
+  if (a.nv > 1) s = add4(s, *reinterpret_cast<const float4*>(a.v[1] + o));
+  if (a.nv > 2) s = add4(s, *reinterpret_cast<const float4*>(a.v[2] + o));
   return s;
 }
 
+template <bool LDS>
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
+  extern __shared__ float xs[];  // [batch][K] when LDS
   __shared__ float red[kWaves];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int K = a.k;
-  float c = 1.0f;
-  if (a.rms) {  // batch 1: one scale for the summed vector
-    float ss = 0.0f;
-    for (int k = tid; k < K; k += kThreads) {
-      const float s = prep_in(a, 0, k);
-      ss = fmaf(s, s, ss);
+  const int tid = threadIdx.x;
+  const int K = a.k, K4 = K / 4;
+
+  // stage s (and accumulate sum s^2 of batch row 0)
+  float ss = 0.0f;
+  if (LDS) {
+    for (int b = 0; b < a.batch; ++b) {
+#pragma unroll 8
+      for (int f = tid; f < K4; f += kThreads) {
+        const float4 s = prep_in4(a, b, f);
+        *reinterpret_cast<float4*>(xs + (int64_t)b * K + 4 * f) = s;
+        if (b == 0) ss = fmaf(s.x, s.x, fmaf(s.y, s.y, fmaf(s.z, s.z, fmaf(s.w, s.w, ss))));
+      }
     }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  } else if (a.rms) {
+#pragma unroll 8
+    for (int f = tid; f < K4; f += kThreads) {
+      const float4 s = prep_in4(a, 0, f);
+      ss = fmaf(s.x, s.x, fmaf(s.y, s.y, fmaf(s.z, s.z, fmaf(s.w, s.w, ss))));
+    }
+  }
+  float c = 1.0f;
+  if (a.rms) {
+    const float tot = block_sum(ss, red);  // its barrier also publishes xs
     c = 1.0f / sqrtf(tot / (float)K + 1e-6f);
+  } else if (LDS) {
+    __syncthreads();
   }
 
-  // shrink: one A row per wave
-  const int row = blockIdx.x * kWaves + wave;
-  if (row < a.rows_total) {
+  // shrink: A row g for every batch row
+  const int g = blockIdx.x;
+  if (g < a.rows_total) {
     int e = 0, base = 0;
-    while (base + a.ent[e].rank <= row) {
+    while (base + a.ent[e].rank <= g) {
       base += a.ent[e].rank;
       ++e;
     }
-    const int j = row - base;
+    const int j = g - base;
     const float* Ar = a.ent[e].A + (int64_t)j * K;
     for (int b = 0; b < a.batch; ++b) {
       float p = 0.0f;
-      for (int k = lane; k < K; k += 64) p = fmaf(Ar[k], a.rms ? c * prep_in(a, b, k) : prep_in(a, b, k), p);
-      p = wave_sum(p);
-      if (lane == 0) a.t[(int64_t)b * a.T + a.ent[e].toff + j] = p;
+#pragma unroll 8
+      for (int f = tid; f < K4; f += kThreads) {
+        const float4 w = *reinterpret_cast<const float4*>(Ar + 4 * f);
+        float4 s = LDS ? *reinterpret_cast<const float4*>(xs + (int64_t)b * K + 4 * f) : prep_in4(a, b, f);
+        if (a.rms) s = mul4(c, s);
+        p = fmaf(w.x, s.x, p);
+        p = fmaf(w.y, s.y, p);
+        p = fmaf(w.z, s.z, p);
+        p = fmaf(w.w, s.w, p);
+      }
+      p = block_sum(p, red);
+      if (tid == 0) a.t[(int64_t)b * a.T + a.ent[e].toff + j] = p;
     }
   }
 
-  // this workgroup's slice of xin
+  // slice g of xin
   if (a.xin) {
-    const int per = (K + gridDim.x - 1) / gridDim.x;
-    const int k0 = blockIdx.x * per, k1 = min(K, k0 + per);
+    const int per = (K4 + gridDim.x - 1) / gridDim.x;
+    const int f0 = g * per, f1 = min(K4, f0 + per);
     for (int b = 0; b < a.batch; ++b)
-      for (int k = k0 + tid; k < k1; k += kThreads)
-        a.xin[(int64_t)b * K + k] = a.rms ? c * prep_in(a, b, k) : prep_in(a, b, k);
+      for (int f = f0 + tid; f < f1; f += kThreads) {
+        float4 s = LDS ? *reinterpret_cast<const float4*>(xs + (int64_t)b * K + 4 * f) : prep_in4(a, b, f);
+        if (a.rms) s = mul4(c, s);
+        *reinterpret_cast<float4*>(a.xin + (int64_t)b * K + 4 * f) = s;
+      }
   }
 }
 
@@ -119,17 +180,17 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 // Workgroup = 4 waves; each wave owns RPW consecutive rows and walks the whole
 // input: lane l takes the 16-byte chunks l, l+64, l+128, ... of each of its rows
 // (q8_0: 16 weights; q4_sm: 32 weights = one block).  All of a wave's weight
-// loads for a tile are issued before any is consumed, so a small matrix has its
-// whole byte stream in flight at once.  The input x is staged in LDS one tile
-// at a time, with the 16-byte slots of each chunk rotated so that the 8 lanes
-// served together by an LDS read touch 8 different bank groups, plus per-chunk
-// sums of x for the integer-offset tricks in dot_q8 / the q4_sm minimum.
+// loads for a tile, and the B rows of its adapters, are issued before anything
+// is consumed, so a small matrix has its whole byte stream in flight at once.
+// The input x is staged in LDS one tile at a time, each thread staging whole
+// chunks and their sums (used by the integer-offset tricks below); the 16-byte
+// slots of each chunk are rotated so that the 8 lanes served together by an
+// LDS read touch 8 different bank groups.
 // ---------------------------------------------------------------------------
 template <int QT>
 struct Fmt {
   static constexpr int kWeightsPerChunk = QT == QBL_FMT_Q8 ? 16 : 32;
   static constexpr int kSlots = kWeightsPerChunk / 4;
-  // rotation of slot j of chunk c
   __device__ static __forceinline__ int slot(int c, int j) {
     return (j + (QT == QBL_FMT_Q8 ? (c >> 1) : c)) & (kSlots - 1);
   }
@@ -177,7 +238,9 @@ __device__ __forceinline__ float dot_q4(const uint4 q, const float4* xv) {
   return s0 + s1;
 }
 
-template <int QT, int BB, int CPL>
+constexpr int kPrefetchAdapters = 2;  // B rows prefetched for lists of <= 2 adapters of rank <= 64
+
+template <int QT, int BB, int CPL, int RPW>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   extern __shared__ float lds[];
   using F = Fmt<QT>;
@@ -188,8 +251,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   const int s = (a.nseg > 2 && wg >= a.seg[2].wg_begin) ? 2 : (a.nseg > 1 && wg >= a.seg[1].wg_begin) ? 1 : 0;
   const GemvSeg& g = a.seg[s];
   const int n = g.n;
-  const int row = (wg - g.wg_begin) * kWaves + wave;  // one row per wave
-  const int lrow = min(row, n - 1);                    // rows past n load row n-1, store nothing
+  const int row0 = (wg - g.wg_begin) * (kWaves * RPW) + wave * RPW;
   const int K = a.k, KT = a.kt, B = a.batch;
   const int tile_chunks = KT / WPC;
   float* xs = lds;                        // [BB][KT]
@@ -198,14 +260,29 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   const int T = a.t_stride;
   const int nblk = K / 32;
   const int64_t row_bytes = QT == QBL_FMT_Q8 ? (int64_t)K : (int64_t)K / 2;
-  const uint8_t* qrow = g.qs + (int64_t)lrow * row_bytes;
+  const int n_ad = g.lora.n_ad;
+  const bool prefetch = g.lora.prefetch != 0;
 
-  if (g.lora.n_ad > 0)
-    for (int i = tid; i < B * T; i += kThreads) ts[i] = a.t[i];
-
-  float acc[BB];
+  int lrow[RPW];
 #pragma unroll
-  for (int b = 0; b < BB; ++b) acc[b] = 0.0f;
+  for (int r = 0; r < RPW; ++r) lrow[r] = min(row0 + r, n - 1);  // rows past n load row n-1, store nothing
+
+  // B rows of the (at most two) adapters, one value per lane
+  float bpre[RPW][kPrefetchAdapters];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int i = 0; i < kPrefetchAdapters; ++i) {
+      bpre[r][i] = 0.0f;
+      if (prefetch && i < n_ad && lane < g.lora.rank[i])
+        bpre[r][i] = g.lora.B[i][(int64_t)lrow[r] * g.lora.rank[i] + lane];
+    }
+
+  float acc[RPW][BB];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int b = 0; b < BB; ++b) acc[r][b] = 0.0f;
 
   for (int k0 = 0; k0 < K; k0 += KT) {
     const int kt = min(KT, K - k0);
@@ -213,34 +290,42 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     const int c0 = k0 / WPC;
 
     // weight stream first: every load of this tile in flight before any use
-    uint4 q[CPL];
-    uint32_t sc[CPL];
+    uint4 q[RPW][CPL];
+    uint32_t sc[RPW][CPL];
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int c = min(lane + 64 * u, CT - 1);
-      q[u] = *reinterpret_cast<const uint4*>(qrow + (int64_t)(c0 + c) * 16);
-      if (QT == QBL_FMT_Q8)
-        sc[u] = reinterpret_cast<const uint16_t*>(g.sc)[(int64_t)lrow * nblk + ((c0 + c) >> 1)];
-      else
-        sc[u] = reinterpret_cast<const uint32_t*>(g.sc)[(int64_t)lrow * nblk + c0 + c];
+    for (int r = 0; r < RPW; ++r) {
+      const uint8_t* qrow = g.qs + (int64_t)lrow[r] * row_bytes;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = min(lane + 64 * u, CT - 1);
+        q[r][u] = stream_load16(qrow + (int64_t)(c0 + c) * 16);
+        if (QT == QBL_FMT_Q8)
+          sc[r][u] = reinterpret_cast<const uint16_t*>(g.sc)[(int64_t)lrow[r] * nblk + ((c0 + c) >> 1)];
+        else
+          sc[r][u] = reinterpret_cast<const uint32_t*>(g.sc)[(int64_t)lrow[r] * nblk + c0 + c];
+      }
     }
 
-    __syncthreads();  // the previous tile is consumed
-    const int nf4 = kt / 4;
-    for (int i = tid; i < BB * nf4; i += kThreads) {
-      const int b = i / nf4, f = i - b * nf4;
-      const int c = f / NS, j = f - c * NS;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (b < B) v = *reinterpret_cast<const float4*>(a.x + (int64_t)b * a.x_stride + k0 + 4 * f);
-      *reinterpret_cast<float4*>(xs + b * KT + c * WPC + 4 * F::slot(c, j)) = v;
-    }
-    __syncthreads();
+    if (k0 > 0) __syncthreads();  // the previous tile is consumed
+    if (k0 == 0 && n_ad > 0)
+      for (int i = tid; i < B * T; i += kThreads) ts[i] = a.t[i];
+    // stage whole chunks of x and their sums
     for (int i = tid; i < BB * CT; i += kThreads) {
       const int b = i / CT, c = i - b * CT;
-      const float* p = xs + b * KT + c * WPC;
+      float4 v[NS];
       float sum = 0.0f;
 #pragma unroll
-      for (int e = 0; e < WPC; ++e) sum += p[e];
+      for (int j = 0; j < NS; ++j) {
+        v[j] = b < B ? *reinterpret_cast<const float4*>(a.x + (int64_t)b * a.x_stride + k0 + c * WPC + 4 * j)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        sum += v[j].x;
+        sum += v[j].y;
+        sum += v[j].z;
+        sum += v[j].w;
+      }
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        *reinterpret_cast<float4*>(xs + b * KT + c * WPC + 4 * F::slot(c, j)) = v[j];
       xsum[b * tile_chunks + c] = sum;
     }
     __syncthreads();
@@ -249,13 +334,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     for (int u = 0; u < CPL; ++u) {
       const int c = lane + 64 * u;
       if (c < CT) {
-        float d, m = 0.0f;
-        if (QT == QBL_FMT_Q8) {
-          d = h2f(sc[u]);
-        } else {
-          d = h2f(sc[u]);
-          m = h2f(sc[u] >> 16);
-        }
 #pragma unroll
         for (int b = 0; b < BB; ++b) {
           const float* xc = xs + b * KT + c * WPC;
@@ -263,11 +341,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
 #pragma unroll
           for (int j = 0; j < NS; ++j) xv[j] = *reinterpret_cast<const float4*>(xc + 4 * F::slot(c, j));
           const float xsc = xsum[b * tile_chunks + c];
-          if (QT == QBL_FMT_Q8) {
-            acc[b] = fmaf(d, dot_q8(q[u], xv, xsc), acc[b]);
-          } else {
-            acc[b] = fmaf(d, dot_q4(q[u], xv), acc[b]);
-            acc[b] = fmaf(m, xsc, acc[b]);
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) {
+            const float d = h2f(sc[r][u]);
+            if (QT == QBL_FMT_Q8) {
+              acc[r][b] = fmaf(d, dot_q8(q[r][u], xv, xsc), acc[r][b]);
+            } else {
+              acc[r][b] = fmaf(d, dot_q4(q[r][u], xv), acc[r][b]);
+              acc[r][b] = fmaf(h2f(sc[r][u] >> 16), xsc, acc[r][b]);
+            }
           }
         }
       }
@@ -275,17 +357,25 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   }
 
   // epilogue: base sum complete, then the adapters in list order
-  if (row < n) {
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = row0 + r;
+    if (row >= n) break;
 #pragma unroll
     for (int b = 0; b < BB; ++b) {
       if (b >= B) break;
-      float y = wave_sum(acc[b]);
-      for (int i = 0; i < g.lora.n_ad; ++i) {
-        const int r = g.lora.rank[i];
-        const float* Br = g.lora.B[i] + (int64_t)row * r;
+      float y = wave_sum(acc[r][b]);
+      for (int i = 0; i < n_ad; ++i) {
+        const int rk = g.lora.rank[i];
         const float* ti = ts + b * T + g.lora.toff[i];
         float p = 0.0f;
-        for (int j = lane; j < r; j += 64) p = fmaf(Br[j], ti[j], p);
+        if (prefetch) {
+          const float bv = i == 0 ? bpre[r][0] : bpre[r][1];
+          if (lane < rk) p = bv * ti[lane];
+        } else {
+          const float* Br = g.lora.B[i] + (int64_t)row * rk;
+          for (int j = lane; j < rk; j += 64) p = fmaf(Br[j], ti[j], p);
+        }
         y = fmaf(g.lora.scale[i], wave_sum(p), y);
       }
       if (lane == 0) g.y[(int64_t)b * g.y_stride + row] = y;
@@ -293,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   }
 }
 
-template <int QT, int BB, int CPL>
+template <int QT, int BB, int CPL, int RPW>
 hipError_t launch_one(GemvArgs& a, hipStream_t st) {
   using F = Fmt<QT>;
   const size_t lds = sizeof(float) * ((size_t)BB * a.kt + (size_t)BB * (a.kt / F::kWeightsPerChunk) +
@@ -302,24 +392,42 @@ hipError_t launch_one(GemvArgs& a, hipStream_t st) {
   if (lds > 64 * 1024) {
     static bool raised = false;  // one attribute call per instantiation
     if (!raised) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<QT, BB, CPL>),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<QT, BB, CPL, RPW>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
       raised = true;
     }
   }
-  hipLaunchKernelGGL((gemv_kernel<QT, BB, CPL>), dim3(a.grid), dim3(kThreads), lds, st, a);
+  int wg = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg[i].wg_begin = wg;
+    wg += (a.seg[i].n + kWaves * RPW - 1) / (kWaves * RPW);
+  }
+  a.grid = wg;
+  a.rpw = RPW;
+  hipLaunchKernelGGL((gemv_kernel<QT, BB, CPL, RPW>), dim3(a.grid), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
+// rows per wave: enough weight loads in flight per wave without exhausting VGPRs
+template <int QT, int BB, int CPL>
+hipError_t launch_rpw(GemvArgs& a, hipStream_t st) {
+  if constexpr (BB == 1 && CPL <= 4) return launch_one<QT, BB, CPL, 4>(a, st);
+  else if constexpr (BB == 1 && CPL <= 8) return launch_one<QT, BB, CPL, 2>(a, st);
+  else return launch_one<QT, BB, CPL, 1>(a, st);
+}
+
+// chunks per lane: only the variants the LDS tile of this batch bucket can need
 template <int QT, int BB>
 hipError_t launch_cpl(GemvArgs& a, int cpl, hipStream_t st) {
-  if (cpl <= 1) return launch_one<QT, BB, 1>(a, st);
-  if (cpl <= 2) return launch_one<QT, BB, 2>(a, st);
-  if (cpl <= 4) return launch_one<QT, BB, 4>(a, st);
-  if (cpl <= 8) return launch_one<QT, BB, 8>(a, st);
-  if (cpl <= 12) return launch_one<QT, BB, 12>(a, st);
-  return launch_one<QT, BB, 16>(a, st);
+  constexpr int kMax = (kLdsFloats / BB) / Fmt<QT>::kWeightsPerChunk / 64;
+  if (cpl <= 1) return launch_rpw<QT, BB, 1>(a, st);
+  if constexpr (kMax >= 2) if (cpl <= 2) return launch_rpw<QT, BB, 2>(a, st);
+  if constexpr (kMax >= 4) if (cpl <= 4) return launch_rpw<QT, BB, 4>(a, st);
+  if constexpr (kMax >= 8) if (cpl <= 8) return launch_rpw<QT, BB, 8>(a, st);
+  if constexpr (kMax >= 12) if (cpl <= 12) return launch_rpw<QT, BB, 12>(a, st);
+  if constexpr (kMax >= 16) if (cpl <= 16) return launch_rpw<QT, BB, 16>(a, st);
+  return hipErrorInvalidValue;
 }
 
 template <int QT>
@@ -332,15 +440,31 @@ hipError_t launch_batch(GemvArgs& a, int bb, int cpl, hipStream_t st) {
   }
 }
 
+template <bool LDS>
+hipError_t launch_prep_t(const PrepArgs& a, int grid, size_t lds, hipStream_t st) {
+  if (LDS && lds > 64 * 1024) {
+    static bool raised = false;
+    if (!raised) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<LDS>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL((prep_kernel<LDS>), dim3(grid), dim3(kThreads), LDS ? lds : 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
-  const int rows_wg = (a.rows_total + kWaves - 1) / kWaves;
-  int grid = rows_wg;
+  if (a.k % 4) return hipErrorInvalidValue;
+  int grid = a.rows_total;
   if (a.xin) grid = max(grid, (a.k + 2047) / 2048);
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  const int64_t floats = (int64_t)a.batch * a.k;
+  if (floats <= kPrepLdsFloats) return launch_prep_t<true>(a, grid, sizeof(float) * floats, st);
+  return launch_prep_t<false>(a, grid, 0, st);
 }
 
 hipError_t launch_gemv(GemvArgs& a, hipStream_t st) {
@@ -352,12 +476,12 @@ hipError_t launch_gemv(GemvArgs& a, hipStream_t st) {
   if ((int64_t)bb * kt > kLdsFloats) kt = max(quant, (kLdsFloats / bb) / quant * quant);
   a.kt = kt;
   const int cpl = (kt / wpc + 63) / 64;
-  int wg = 0;
   for (int i = 0; i < a.nseg; ++i) {
-    a.seg[i].wg_begin = wg;
-    wg += (a.seg[i].n + kWaves - 1) / kWaves;
+    LoraSeg& L = a.seg[i].lora;
+    L.prefetch = L.n_ad <= kPrefetchAdapters;
+    for (int j = 0; j < L.n_ad; ++j)
+      if (L.rank[j] > 64) L.prefetch = 0;
   }
-  a.grid = wg;
   return a.qtype == QBL_FMT_Q8 ? launch_batch<QBL_FMT_Q8>(a, bb, cpl, st)
                                : launch_batch<QBL_FMT_Q4>(a, bb, cpl, st);
 }

@@ -16,6 +16,7 @@ constexpr int kMaxPrepEntries = kMaxSegs * kMaxAdapters;
 // The adapters of one linear in list order, as the expand needs them.
 struct LoraSeg {
   int n_ad;
+  int prefetch;              // set by launch_gemv: B rows loaded up front
   int toff[kMaxAdapters];    // offset of t_i within a batch row of the t buffer
   int rank[kMaxAdapters];
   float scale[kMaxAdapters];
