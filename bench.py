@@ -217,6 +217,37 @@ def bench_q4(torch, q, workloads, args):
     return out
 
 
+def bench_prefill(torch, q, workloads, args):
+    wl = workloads.prefill()
+    copies = 4
+    log(f"[prefill] building {copies} copies of the 14336x4096 q8_0 layer (r64)")
+    base, ads, comp, _ = build_copies(q, wl, copies, [0])
+    x = torch.from_numpy(wl.x_prefill_f32()).to(torch.bfloat16).view(torch.int16).cuda()
+    y = torch.empty((wl.m_tokens, wl.linears[0].n_out), dtype=torch.float32, device="cuda")
+    wss = [q.workspace(comp, q.OP_JIT, c, wl.m_tokens) for c in range(copies)]
+
+    def step(i):
+        q.qbl_linear_jit(comp, i % copies, x, y, wl.m_tokens, wss[i % copies])
+
+    ms = time_loop(torch, step, max(10, args.steps // 4), 3)
+    L = wl.linears[0]
+    r = wl.adapters[0].rank
+    flop = 2 * wl.m_tokens * L.n_out * L.k_in + 2 * r * L.n_out * L.k_in
+    q.qbl_profile_enable(True)
+    time_loop(torch, step, max(10, args.steps // 4), 0)
+    n_jit, ms_jit = q.qbl_profile_read(q.KIND_JIT)
+    q.qbl_profile_enable(False)
+    avg_us = ms_jit / max(n_jit, 1) * 1e3
+    tflops = flop / (ms * 1e-3) / 1e12
+    kern_tflops = flop / (avg_us * 1e-6) / 1e12
+    free_all(q, base, ads, comp)
+    log(f"[prefill] {ms * 1e3:.1f} us/layer, {tflops:.0f} TFLOP/s (kernel {kern_tflops:.0f})")
+    return {"us_per_layer": round(ms * 1e3, 1), "TFLOP_per_s": round(tflops, 1),
+            "kernel_avg_us": round(avg_us, 1), "kernel_TFLOP_per_s": round(kern_tflops, 1),
+            "frac_bf16_peak": round(kern_tflops / BF16_PEAK_TFLOPS, 4), "flop_per_layer": flop,
+            "tokens_per_s": round(wl.m_tokens / (ms * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +283,7 @@ def main():
     if not args.no_extras:
         result["stack"] = bench_stack(torch, q, workloads, args)
         result["q4_mlp"] = bench_q4(torch, q, workloads, args)
+        result["prefill"] = bench_prefill(torch, q, workloads, args)
     import oracle
     log("[cpu] timing the oracle")
     result["cpu_baseline"] = cpu_baseline(oracle, wl, blocks, args.cpu_seconds)

@@ -156,20 +156,36 @@ static void quantize_q4_sm_block(const float* w, uint8_t* blk) {
   for (int i = 0; i < 16; ++i) blk[4 + i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
 }
 
+typedef struct {
+  int32_t qtype;
+  const float* w;
+  int64_t k;
+  uint8_t* blocks;
+} quant_ctx;
+
+static void quant_row(void* vc, int64_t r, double* unused) {
+  const quant_ctx* c = (const quant_ctx*)vc;
+  (void)unused;
+  const int64_t nb = c->k / 32;
+  const int32_t bb = or_block_bytes(c->qtype);
+  for (int64_t b = 0; b < nb; ++b) {
+    const float* src = c->w + r * c->k + b * 32;
+    uint8_t* dst = c->blocks + (r * nb + b) * bb;
+    if (c->qtype == OR_Q8_0)
+      quantize_q8_0_block(src, dst);
+    else
+      quantize_q4_sm_block(src, dst);
+  }
+}
+
+static int32_t for_rows(int64_t n_rows, int32_t nthreads, int64_t scratch_len,
+                        void (*fn)(void*, int64_t, double*), void* ctx);
+
 int32_t or_quantize(int32_t qtype, const float* w, int64_t n, int64_t k, uint8_t* blocks) {
   const int32_t bb = or_block_bytes(qtype);
   if (!bb || !w || !blocks || n < 0 || k <= 0 || k % 32) return -1;
-  const int64_t nb = k / 32;
-  for (int64_t r = 0; r < n; ++r)
-    for (int64_t b = 0; b < nb; ++b) {
-      const float* src = w + r * k + b * 32;
-      uint8_t* dst = blocks + (r * nb + b) * bb;
-      if (qtype == OR_Q8_0)
-        quantize_q8_0_block(src, dst);
-      else
-        quantize_q4_sm_block(src, dst);
-    }
-  return 0;
+  quant_ctx c = {qtype, w, k, blocks};
+  return for_rows(n, 0, 0, quant_row, &c);
 }
 
 /* Dequantise one row into float64: exact, since d*q has at most 15

@@ -25,7 +25,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsFloats = 16384;      // GEMV x tile budget per workgroup (64 KiB)
-constexpr int kPrepLdsFloats = 40960;  // prep input staging budget (160 KiB)
+constexpr int kPrepLdsFloats = 32768;  // prep input staging budget (128 KiB)
+constexpr int kPrepAPre = 12;          // float4 of the A row held in registers per thread
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -106,6 +107,28 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   __shared__ float red[kWaves];
   const int tid = threadIdx.x;
   const int K = a.k, K4 = K / 4;
+  const int g = blockIdx.x;
+
+  // this workgroup's A row, requested before the input is staged so the two
+  // memory round trips overlap
+  int e = 0, j = 0;
+  const float* Ar = nullptr;
+  if (g < a.rows_total) {
+    int base = 0;
+    while (base + a.ent[e].rank <= g) {
+      base += a.ent[e].rank;
+      ++e;
+    }
+    j = g - base;
+    Ar = a.ent[e].A + (int64_t)j * K;
+  }
+  const bool apre = Ar && K4 <= kThreads * kPrepAPre;
+  float4 ap[kPrepAPre];
+#pragma unroll
+  for (int i = 0; i < kPrepAPre; ++i) {
+    const int f = tid + kThreads * i;
+    ap[i] = (apre && f < K4) ? *reinterpret_cast<const float4*>(Ar + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 
   // stage s (and accumulate sum s^2 of batch row 0)
   float ss = 0.0f;
@@ -134,26 +157,34 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   }
 
   // shrink: A row g for every batch row
-  const int g = blockIdx.x;
-  if (g < a.rows_total) {
-    int e = 0, base = 0;
-    while (base + a.ent[e].rank <= g) {
-      base += a.ent[e].rank;
-      ++e;
-    }
-    const int j = g - base;
-    const float* Ar = a.ent[e].A + (int64_t)j * K;
+  if (Ar) {
     for (int b = 0; b < a.batch; ++b) {
       float p = 0.0f;
+      if (apre) {
+#pragma unroll
+        for (int i = 0; i < kPrepAPre; ++i) {
+          const int f = tid + kThreads * i;
+          if (f < K4) {
+            const float4 w = ap[i];
+            float4 s = LDS ? *reinterpret_cast<const float4*>(xs + (int64_t)b * K + 4 * f) : prep_in4(a, b, f);
+            if (a.rms) s = mul4(c, s);
+            p = fmaf(w.x, s.x, p);
+            p = fmaf(w.y, s.y, p);
+            p = fmaf(w.z, s.z, p);
+            p = fmaf(w.w, s.w, p);
+          }
+        }
+      } else {
 #pragma unroll 8
-      for (int f = tid; f < K4; f += kThreads) {
-        const float4 w = *reinterpret_cast<const float4*>(Ar + 4 * f);
-        float4 s = LDS ? *reinterpret_cast<const float4*>(xs + (int64_t)b * K + 4 * f) : prep_in4(a, b, f);
-        if (a.rms) s = mul4(c, s);
-        p = fmaf(w.x, s.x, p);
-        p = fmaf(w.y, s.y, p);
-        p = fmaf(w.z, s.z, p);
-        p = fmaf(w.w, s.w, p);
+        for (int f = tid; f < K4; f += kThreads) {
+          const float4 w = *reinterpret_cast<const float4*>(Ar + 4 * f);
+          float4 s = LDS ? *reinterpret_cast<const float4*>(xs + (int64_t)b * K + 4 * f) : prep_in4(a, b, f);
+          if (a.rms) s = mul4(c, s);
+          p = fmaf(w.x, s.x, p);
+          p = fmaf(w.y, s.y, p);
+          p = fmaf(w.z, s.z, p);
+          p = fmaf(w.w, s.w, p);
+        }
       }
       p = block_sum(p, red);
       if (tid == 0) a.t[(int64_t)b * a.T + a.ent[e].toff + j] = p;

@@ -23,7 +23,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_SO):
         tmp = _SO + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+            ["gcc", "-O3", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-Wextra",
              os.path.join(_HERE, "synth.c"), "-o", tmp, "-lm", "-lpthread"])
         os.replace(tmp, _SO)
     return _SO

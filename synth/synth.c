@@ -58,8 +58,23 @@ typedef struct {
 
 static void* run_job(void* arg) {
   job_t* j = (job_t*)arg;
-  for (uint64_t i = j->begin; i < j->end; ++i)
+  uint64_t i = j->begin;
+  /* a leading odd index: its pair started before this slice */
+  if (i < j->end && ((j->offset + i) & 1)) {
     j->out[i] = (float)(j->mean + j->std * normal_at(j->seed, j->offset + i));
+    ++i;
+  }
+  /* whole pairs share one radius and one angle */
+  for (; i + 1 < j->end; i += 2) {
+    const uint64_t p = (j->offset + i) >> 1;
+    const double u1 = (double)((synth_splitmix64_at(j->seed, 2 * p) >> 11) + 1) * 0x1p-53;
+    const double u2 = (double)(synth_splitmix64_at(j->seed, 2 * p + 1) >> 11) * 0x1p-53;
+    const double r = sqrt(-2.0 * log(u1));
+    const double a = 6.283185307179586476925286766559 * u2;
+    j->out[i] = (float)(j->mean + j->std * (r * cos(a)));
+    j->out[i + 1] = (float)(j->mean + j->std * (r * sin(a)));
+  }
+  if (i < j->end) j->out[i] = (float)(j->mean + j->std * normal_at(j->seed, j->offset + i));
   return NULL;
 }
 

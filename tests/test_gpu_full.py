@@ -1,0 +1,163 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration the
+benchmark times:
+
+* 7B block (4096/11008, q8_0, r16): every linear and the chained block, all outputs;
+* 32-block stack, r16@1.0 then r64@0.5, 256 tokens: the free-running chain for the
+  first tokens, teacher-forced tokens later on (the oracle fed the GPU's previous
+  token), the swapped order, and the base hash;
+* 70B MLP linears (q4_sm, r32) at batch 1 and 8: sampled output rows;
+* prefill M=512, K=4096 -> N=14336 (q8_0, r64) through JIT materialisation:
+  sampled output columns for all 512 tokens, against the bf16 recipe and within
+  the bf16 bound of the dual path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import workloads
+from tests.gpu_harness import Built, log, rel_l2
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+def _sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = set([0, n - 1, n // 2]) | set(rng.choice(n, size=min(n, count), replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_block_7b_full(torch_cuda):
+    torch = torch_cuda
+    wl = workloads.block()
+    log("7B block: building (q8_0, r16)")
+    b = Built(wl)
+    q = b.q
+    try:
+        b.attach([0])
+        worst = 0.0
+        for i, L in enumerate(wl.linears):
+            x = wl.x(i)
+            xd = torch.from_numpy(x).cuda()
+            yd = torch.empty((1, L.n_out), dtype=torch.float32, device="cuda")
+            q.qbl_linear(b.comp, i, xd, yd, 1, q.workspace(b.comp, q.OP_LINEAR, i, 1))
+            torch.cuda.synchronize()
+            ref = oracle.linear_dual(L.qtype, b.or_blocks[i], L.n_out, L.k_in, x, b.oracle_ads(i, [0]))
+            worst = max(worst, rel_l2(yd.cpu().numpy(), ref))
+        log(f"  worst linear rel-L2 {worst:.2e}")
+        assert worst <= TOL
+        x0 = wl.x0()[0]
+        xd = torch.from_numpy(x0).cuda()
+        yd = torch.empty(4096, dtype=torch.float32, device="cuda")
+        q.qbl_block(b.comp, 0, xd, yd, q.workspace(b.comp, q.OP_BLOCK))
+        torch.cuda.synchronize()
+        r = rel_l2(yd.cpu().numpy(), oracle.block(b.oracle_layers([0]), x0.astype(np.float64)))
+        log(f"  block rel-L2 {r:.2e}")
+        assert r <= TOL
+    finally:
+        b.close()
+
+
+def test_stack_32_blocks_256_tokens(torch_cuda):
+    torch = torch_cuda
+    wl = workloads.stack()
+    log("stack: building 32 blocks (6.9 GB q8_0) with r16 and r64 adapters")
+    b = Built(wl)
+    q = b.q
+    try:
+        d, nt = 4096, wl.tokens
+        x0 = wl.x0()[0]
+        xd = torch.from_numpy(x0).cuda()
+        h0 = q.qbl_base_hash(b.base)
+        b.attach([0, 1])
+        ws = q.workspace(b.comp, q.OP_BLOCK)
+        y = torch.empty((nt, d), dtype=torch.float32, device="cuda")
+        q.qbl_decode(b.comp, 0, 32, xd, y, nt, ws)
+        torch.cuda.synchronize()
+        yg = y.cpu().numpy()
+        layers = b.oracle_layers([0, 1])
+        free = oracle.stack(layers, x0.astype(np.float64), 32)
+        worst = max(rel_l2(yg[t], free[t]) for t in range(32))
+        log(f"  free-running tokens 0..31: worst rel-L2 {worst:.2e}")
+        assert worst <= TOL
+        for t in (64, 255):
+            ref = oracle.stack(layers, yg[t - 1].astype(np.float64), 1)[0]
+            r = rel_l2(yg[t], ref)
+            log(f"  teacher-forced token {t}: rel-L2 {r:.2e}")
+            assert r <= TOL
+        assert rel_l2(yg[255], yg[254]) > 1e-3
+        # swap the order: only rounding changes, the base bytes never do
+        b.attach([1, 0])
+        ws = q.workspace(b.comp, q.OP_BLOCK)
+        y2 = torch.empty((nt, d), dtype=torch.float32, device="cuda")
+        q.qbl_decode(b.comp, 0, 32, xd, y2, nt, ws)
+        torch.cuda.synchronize()
+        ys = y2.cpu().numpy()
+        assert not np.array_equal(ys, yg)
+        ref = oracle.stack(b.oracle_layers([1, 0]), ys[254].astype(np.float64), 1)[0]
+        assert rel_l2(ys[255], ref) <= TOL
+        assert q.qbl_base_hash(b.base) == h0
+    finally:
+        b.close()
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_mlp70b_q4_sampled_rows(torch_cuda, batch):
+    torch = torch_cuda
+    wl = workloads.mlp70b(batch=batch)
+    log(f"70B MLP q4_sm r32 batch {batch}: building")
+    b = Built(wl)
+    q = b.q
+    try:
+        b.attach([0])
+        for i, L in enumerate(wl.linears):
+            x = wl.x(i)
+            xd = torch.from_numpy(x).cuda()
+            yd = torch.empty((batch, L.n_out), dtype=torch.float32, device="cuda")
+            q.qbl_linear(b.comp, i, xd, yd, batch, q.workspace(b.comp, q.OP_LINEAR, i, batch))
+            torch.cuda.synchronize()
+            rows = _sample_rows(L.n_out, 192, 100 + i)
+            ref = oracle.linear_dual(L.qtype, b.or_blocks[i], L.n_out, L.k_in, x, b.oracle_ads(i, [0]), rows=rows)
+            ref0 = oracle.linear_dual(L.qtype, b.or_blocks[i], L.n_out, L.k_in, x, rows=rows)
+            y = yd.cpu().numpy()[:, rows]
+            r, rd = rel_l2(y, ref), rel_l2(y - ref0, ref - ref0)
+            log(f"  linear {i}: rel-L2 {r:.2e}, LoRA-delta rel-L2 {rd:.2e}")
+            assert r <= TOL and rd <= TOL
+    finally:
+        b.close()
+
+
+def test_prefill_jit_full_sampled_columns(torch_cuda):
+    torch = torch_cuda
+    wl = workloads.prefill()
+    log("prefill 512 x 4096 -> 14336 q8_0 r64: building")
+    b = Built(wl)
+    q = b.q
+    try:
+        b.attach([0])
+        L = wl.linears[0]
+        xb = torch.from_numpy(wl.x_prefill_f32()).to(torch.bfloat16)
+        bits = xb.view(torch.int16).numpy().view(np.uint16)
+        xd = xb.view(torch.int16).cuda()
+        yd = torch.empty((512, L.n_out), dtype=torch.float32, device="cuda")
+        q.qbl_linear_jit(b.comp, 0, xd, yd, 512, q.workspace(b.comp, q.OP_JIT, 0, 512))
+        torch.cuda.synchronize()
+        rows = _sample_rows(L.n_out, 160, 7)
+        ads = b.oracle_ads(0, [0])
+        ref = oracle.linear_jit(L.qtype, b.or_blocks[0], L.n_out, L.k_in, bits, ads, rows=rows)
+        y = yd.cpu().numpy()[:, rows]
+        r = rel_l2(y, ref)
+        dual = oracle.linear_dual(L.qtype, b.or_blocks[0], L.n_out, L.k_in,
+                                  oracle.f32_from_bf16(bits).astype(np.float64), ads, rows=rows)
+        rd = rel_l2(y, dual)
+        log(f"  rel-L2 vs recipe {r:.2e}, vs dual path {rd:.2e}")
+        assert r <= TOL and rd <= 2.0 ** -8
+    finally:
+        b.close()
