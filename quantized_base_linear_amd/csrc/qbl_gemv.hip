@@ -25,7 +25,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsFloats = 16384;      // GEMV x tile budget per workgroup (64 KiB)
-constexpr int kPrepLdsFloats = 32768;  // prep input staging budget (128 KiB)
+constexpr int kPrepLdsFloats = 36864;  // prep input staging budget (144 KiB)
 constexpr int kPrepAPre = 12;          // float4 of the A row held in registers per thread
 
 template <int CTRL>
@@ -414,21 +414,24 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   }
 }
 
+// Dynamic LDS above 64 KiB needs a per-kernel opt-in; raise it to what this
+// launch needs (static LDS of these kernels is at most 16 bytes).
+constexpr size_t kMaxDynLds = 160 * 1024 - 256;
+
+hipError_t allow_dyn_lds(const void* fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  if (bytes > kMaxDynLds) return hipErrorInvalidValue;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 template <int QT, int BB, int CPL, int RPW>
 hipError_t launch_one(GemvArgs& a, hipStream_t st) {
   using F = Fmt<QT>;
   const size_t lds = sizeof(float) * ((size_t)BB * a.kt + (size_t)BB * (a.kt / F::kWeightsPerChunk) +
                                       (size_t)a.batch * a.t_stride);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  if (lds > 64 * 1024) {
-    static bool raised = false;  // one attribute call per instantiation
-    if (!raised) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<QT, BB, CPL, RPW>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
-  }
+  if (lds > kMaxDynLds) return hipErrorInvalidValue;
+  hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&gemv_kernel<QT, BB, CPL, RPW>), lds);
+  if (e != hipSuccess) return e;
   int wg = 0;
   for (int i = 0; i < a.nseg; ++i) {
     a.seg[i].wg_begin = wg;
@@ -473,14 +476,9 @@ hipError_t launch_batch(GemvArgs& a, int bb, int cpl, hipStream_t st) {
 
 template <bool LDS>
 hipError_t launch_prep_t(const PrepArgs& a, int grid, size_t lds, hipStream_t st) {
-  if (LDS && lds > 64 * 1024) {
-    static bool raised = false;
-    if (!raised) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<LDS>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
+  if (LDS) {
+    hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&prep_kernel<LDS>), lds);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((prep_kernel<LDS>), dim3(grid), dim3(kThreads), LDS ? lds : 0, st, a);
   return hipGetLastError();
@@ -489,6 +487,7 @@ hipError_t launch_prep_t(const PrepArgs& a, int grid, size_t lds, hipStream_t st
 }  // namespace
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   if (a.k % 4) return hipErrorInvalidValue;
   int grid = a.rows_total;
   if (a.xin) grid = max(grid, (a.k + 2047) / 2048);
@@ -499,6 +498,7 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemv(GemvArgs& a, hipStream_t st) {
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   const int bb = a.batch <= 1 ? 1 : a.batch <= 2 ? 2 : a.batch <= 4 ? 4 : 8;
   const int wpc = a.qtype == QBL_FMT_Q8 ? 16 : 32;
   // x tile: whole input when it fits the LDS budget, else multiples of 64 chunks

@@ -265,6 +265,7 @@ int64_t jit_workspace_bytes(int n, int k, int total_rank) {
 }
 
 hipError_t launch_jit(const JitArgs& a, hipStream_t st) {
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   if (a.k % 32 || a.n < 1 || a.m < 1) return hipErrorInvalidValue;
   const int tp = rank_pad(a.total_rank);
   if (tp > 0) {
