@@ -125,6 +125,7 @@ def bench_block(torch, q, workloads, args):
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "kernel": "gemv_kernel (fused q8_0 dequant-GEMV + LoRA expand)",
+            "timing": "HIP events attached to each GEMV dispatch (hipExtLaunchKernelGGL) on the launch stream",
             "launches_per_step": launches_per_step, "avg_launch_us": round(avg_us, 2),
             "bytes_per_launch": int(gemv_bytes_step / launches_per_step),
             "prep_avg_launch_us": round(ms_prep / max(n_prep, 1) * 1e3, 2),
@@ -257,6 +258,9 @@ def main():
     ap.add_argument("--stack-tokens", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extras", action="store_true", help="skip the stack / q4 / prefill lines")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of this many MiB (a known-size kernel "
+                         "for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
@@ -269,6 +273,14 @@ def main():
     from synth import workloads
     torch.cuda.set_device(0)
 
+    if args.calib_copy:
+        n = args.calib_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[calib] copied {args.calib_copy} MiB")
+        del src, dst
     wl, blocks, ms, step_bytes, gbs, roof = bench_block(torch, q, workloads, args)
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,

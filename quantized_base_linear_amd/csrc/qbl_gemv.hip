@@ -425,7 +425,7 @@ hipError_t allow_dyn_lds(const void* fn, size_t bytes) {
 }
 
 template <int QT, int BB, int CPL, int RPW>
-hipError_t launch_one(GemvArgs& a, hipStream_t st) {
+hipError_t launch_one(GemvArgs& a, const LaunchCtx& lc) {
   using F = Fmt<QT>;
   const size_t lds = sizeof(float) * ((size_t)BB * a.kt + (size_t)BB * (a.kt / F::kWeightsPerChunk) +
                                       (size_t)a.batch * a.t_stride);
@@ -439,65 +439,65 @@ hipError_t launch_one(GemvArgs& a, hipStream_t st) {
   }
   a.grid = wg;
   a.rpw = RPW;
-  hipLaunchKernelGGL((gemv_kernel<QT, BB, CPL, RPW>), dim3(a.grid), dim3(kThreads), lds, st, a);
+  QBL_LAUNCH((gemv_kernel<QT, BB, CPL, RPW>), dim3(a.grid), dim3(kThreads), lds, lc, a);
   return hipGetLastError();
 }
 
 // rows per wave: enough weight loads in flight per wave without exhausting VGPRs
 template <int QT, int BB, int CPL>
-hipError_t launch_rpw(GemvArgs& a, hipStream_t st) {
-  if constexpr (BB == 1 && CPL <= 4) return launch_one<QT, BB, CPL, 4>(a, st);
-  else if constexpr (BB == 1 && CPL <= 8) return launch_one<QT, BB, CPL, 2>(a, st);
-  else return launch_one<QT, BB, CPL, 1>(a, st);
+hipError_t launch_rpw(GemvArgs& a, const LaunchCtx& lc) {
+  if constexpr (BB == 1 && CPL <= 4) return launch_one<QT, BB, CPL, 4>(a, lc);
+  else if constexpr (BB == 1 && CPL <= 8) return launch_one<QT, BB, CPL, 2>(a, lc);
+  else return launch_one<QT, BB, CPL, 1>(a, lc);
 }
 
 // chunks per lane: only the variants the LDS tile of this batch bucket can need
 template <int QT, int BB>
-hipError_t launch_cpl(GemvArgs& a, int cpl, hipStream_t st) {
+hipError_t launch_cpl(GemvArgs& a, int cpl, const LaunchCtx& lc) {
   constexpr int kMax = (kLdsFloats / BB) / Fmt<QT>::kWeightsPerChunk / 64;
-  if (cpl <= 1) return launch_rpw<QT, BB, 1>(a, st);
-  if constexpr (kMax >= 2) if (cpl <= 2) return launch_rpw<QT, BB, 2>(a, st);
-  if constexpr (kMax >= 4) if (cpl <= 4) return launch_rpw<QT, BB, 4>(a, st);
-  if constexpr (kMax >= 8) if (cpl <= 8) return launch_rpw<QT, BB, 8>(a, st);
-  if constexpr (kMax >= 12) if (cpl <= 12) return launch_rpw<QT, BB, 12>(a, st);
-  if constexpr (kMax >= 16) if (cpl <= 16) return launch_rpw<QT, BB, 16>(a, st);
+  if (cpl <= 1) return launch_rpw<QT, BB, 1>(a, lc);
+  if constexpr (kMax >= 2) if (cpl <= 2) return launch_rpw<QT, BB, 2>(a, lc);
+  if constexpr (kMax >= 4) if (cpl <= 4) return launch_rpw<QT, BB, 4>(a, lc);
+  if constexpr (kMax >= 8) if (cpl <= 8) return launch_rpw<QT, BB, 8>(a, lc);
+  if constexpr (kMax >= 12) if (cpl <= 12) return launch_rpw<QT, BB, 12>(a, lc);
+  if constexpr (kMax >= 16) if (cpl <= 16) return launch_rpw<QT, BB, 16>(a, lc);
   return hipErrorInvalidValue;
 }
 
 template <int QT>
-hipError_t launch_batch(GemvArgs& a, int bb, int cpl, hipStream_t st) {
+hipError_t launch_batch(GemvArgs& a, int bb, int cpl, const LaunchCtx& lc) {
   switch (bb) {
-    case 1: return launch_cpl<QT, 1>(a, cpl, st);
-    case 2: return launch_cpl<QT, 2>(a, cpl, st);
-    case 4: return launch_cpl<QT, 4>(a, cpl, st);
-    default: return launch_cpl<QT, 8>(a, cpl, st);
+    case 1: return launch_cpl<QT, 1>(a, cpl, lc);
+    case 2: return launch_cpl<QT, 2>(a, cpl, lc);
+    case 4: return launch_cpl<QT, 4>(a, cpl, lc);
+    default: return launch_cpl<QT, 8>(a, cpl, lc);
   }
 }
 
 template <bool LDS>
-hipError_t launch_prep_t(const PrepArgs& a, int grid, size_t lds, hipStream_t st) {
+hipError_t launch_prep_t(const PrepArgs& a, int grid, size_t lds, const LaunchCtx& lc) {
   if (LDS) {
     hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&prep_kernel<LDS>), lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((prep_kernel<LDS>), dim3(grid), dim3(kThreads), LDS ? lds : 0, st, a);
+  QBL_LAUNCH((prep_kernel<LDS>), dim3(grid), dim3(kThreads), LDS ? lds : 0, lc, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
+hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc) {
   (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   if (a.k % 4) return hipErrorInvalidValue;
   int grid = a.rows_total;
   if (a.xin) grid = max(grid, (a.k + 2047) / 2048);
   if (grid < 1) grid = 1;
   const int64_t floats = (int64_t)a.batch * a.k;
-  if (floats <= kPrepLdsFloats) return launch_prep_t<true>(a, grid, sizeof(float) * floats, st);
-  return launch_prep_t<false>(a, grid, 0, st);
+  if (floats <= kPrepLdsFloats) return launch_prep_t<true>(a, grid, sizeof(float) * floats, lc);
+  return launch_prep_t<false>(a, grid, 0, lc);
 }
 
-hipError_t launch_gemv(GemvArgs& a, hipStream_t st) {
+hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc) {
   (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   const int bb = a.batch <= 1 ? 1 : a.batch <= 2 ? 2 : a.batch <= 4 ? 4 : 8;
   const int wpc = a.qtype == QBL_FMT_Q8 ? 16 : 32;
@@ -513,8 +513,8 @@ hipError_t launch_gemv(GemvArgs& a, hipStream_t st) {
     for (int j = 0; j < L.n_ad; ++j)
       if (L.rank[j] > 64) L.prefetch = 0;
   }
-  return a.qtype == QBL_FMT_Q8 ? launch_batch<QBL_FMT_Q8>(a, bb, cpl, st)
-                               : launch_batch<QBL_FMT_Q4>(a, bb, cpl, st);
+  return a.qtype == QBL_FMT_Q8 ? launch_batch<QBL_FMT_Q8>(a, bb, cpl, lc)
+                               : launch_batch<QBL_FMT_Q4>(a, bb, cpl, lc);
 }
 
 }  // namespace qbl

@@ -242,16 +242,16 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
 int rank_pad(int t) { return t <= 0 ? 0 : t <= 16 * JRMAX ? (t + 15) / 16 * 16 : (t + 63) / 64 * 64; }
 
 template <int QT>
-hipError_t launch_q(const JitArgs& a, int tp, hipStream_t st) {
+hipError_t launch_q(const JitArgs& a, int tp, const LaunchCtx& lc) {
   const dim3 grid((a.n + JBN - 1) / JBN, (a.m + JBM - 1) / JBM);
   const int rs = tp / 16;
   switch (rs) {
-    case 0: hipLaunchKernelGGL((jit_kernel<QT, 0>), grid, dim3(JTHREADS), 0, st, a, tp); break;
-    case 1: hipLaunchKernelGGL((jit_kernel<QT, 1>), grid, dim3(JTHREADS), 0, st, a, tp); break;
-    case 2: hipLaunchKernelGGL((jit_kernel<QT, 2>), grid, dim3(JTHREADS), 0, st, a, tp); break;
-    case 3: hipLaunchKernelGGL((jit_kernel<QT, 3>), grid, dim3(JTHREADS), 0, st, a, tp); break;
-    case 4: hipLaunchKernelGGL((jit_kernel<QT, 4>), grid, dim3(JTHREADS), 0, st, a, tp); break;
-    default: hipLaunchKernelGGL((jit_kernel<QT, JRMAX + 1>), grid, dim3(JTHREADS), 0, st, a, tp); break;
+    case 0: QBL_LAUNCH((jit_kernel<QT, 0>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
+    case 1: QBL_LAUNCH((jit_kernel<QT, 1>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
+    case 2: QBL_LAUNCH((jit_kernel<QT, 2>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
+    case 3: QBL_LAUNCH((jit_kernel<QT, 3>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
+    case 4: QBL_LAUNCH((jit_kernel<QT, 4>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
+    default: QBL_LAUNCH((jit_kernel<QT, JRMAX + 1>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
   }
   return hipGetLastError();
 }
@@ -264,7 +264,7 @@ int64_t jit_workspace_bytes(int n, int k, int total_rank) {
   return ((int64_t)k * tp * 2 + 255) / 256 * 256 + ((int64_t)n * tp * 2 + 255) / 256 * 256;
 }
 
-hipError_t launch_jit(const JitArgs& a, hipStream_t st) {
+hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc) {
   (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   if (a.k % 32 || a.n < 1 || a.m < 1) return hipErrorInvalidValue;
   const int tp = rank_pad(a.total_rank);
@@ -272,11 +272,11 @@ hipError_t launch_jit(const JitArgs& a, hipStream_t st) {
     const int64_t total = (int64_t)a.k * tp + (int64_t)a.n * tp;
     const int threads = 256;
     hipLaunchKernelGGL(stage_lora_kernel, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0,
-                       st, a, tp);
+                       lc.stream, a, tp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return a.qtype == QBL_FMT_Q8 ? launch_q<QBL_FMT_Q8>(a, tp, st) : launch_q<QBL_FMT_Q4>(a, tp, st);
+  return a.qtype == QBL_FMT_Q8 ? launch_q<QBL_FMT_Q8>(a, tp, lc) : launch_q<QBL_FMT_Q4>(a, tp, lc);
 }
 
 }  // namespace qbl

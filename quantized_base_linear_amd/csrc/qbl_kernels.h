@@ -1,11 +1,22 @@
 // Launch interface between the host runtime and the gfx950 kernels.
 // Internal to the library: not part of the C ABI.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 namespace qbl {
+
+// Launch `kernel` on lc.stream, with lc's timing events when they are set.
+#define QBL_LAUNCH(kernel, grid, block, lds, lc, ...)                                              \
+  do {                                                                                             \
+    if ((lc).start)                                                                                \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, (lc).stream, (lc).start, (lc).stop, 0,       \
+                            __VA_ARGS__);                                                          \
+    else                                                                                           \
+      hipLaunchKernelGGL(kernel, grid, block, lds, (lc).stream, __VA_ARGS__);                      \
+  } while (0)
 
 constexpr int QBL_FMT_Q8 = 1;  // same values as QBL_Q8_0 / QBL_Q4_SM of the C ABI
 constexpr int QBL_FMT_Q4 = 2;
@@ -89,9 +100,17 @@ struct JitArgs {
   uint16_t* ws;        // scratch for the staged bf16 factors (see launch_jit)
 };
 
-hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
-hipError_t launch_gemv(GemvArgs& a, hipStream_t s);
-hipError_t launch_jit(const JitArgs& a, hipStream_t s);
+// Where a kernel goes: the stream, and optionally a pair of events that the
+// runtime attaches to the dispatch itself (hipExtLaunchKernelGGL) so that they
+// time the kernel's execution.
+struct LaunchCtx {
+  hipStream_t stream = nullptr;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc);
+hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc);
+hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc);
 int64_t jit_workspace_bytes(int n, int k, int total_rank);
 
 }  // namespace qbl

@@ -533,17 +533,20 @@ Profiler& profiler() {
   return p;
 }
 
-// Brackets one kernel launch with timing events while timing is enabled.
+// Timing events for one kernel launch while timing is enabled: they ride on the
+// dispatch itself, so they measure the kernel, not the queue around it.
 class KernelTimer {
  public:
-  KernelTimer(int kind, hipStream_t st) : kind_(kind), st_(st) {
+  KernelTimer(int kind, hipStream_t st) : kind_(kind) {
+    ctx_.stream = st;
     if (!profiler().on.load()) return;
     if (hipEventCreate(&a_) != hipSuccess || hipEventCreate(&b_) != hipSuccess) return;
-    hipEventRecord(a_, st_);
+    ctx_.start = a_;
+    ctx_.stop = b_;
   }
+  const qbl::LaunchCtx& ctx() const { return ctx_; }
   void stop() {
     if (!a_ || !b_) return;
-    hipEventRecord(b_, st_);
     Profiler& p = profiler();
     std::lock_guard<std::mutex> g(p.mu);
     p.recs.push_back(Profiler::Rec{kind_, a_, b_});
@@ -556,7 +559,7 @@ class KernelTimer {
 
  private:
   int kind_;
-  hipStream_t st_;
+  qbl::LaunchCtx ctx_;
   hipEvent_t a_ = nullptr, b_ = nullptr;
 };
 
@@ -702,7 +705,7 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     p.T = T;
     p.rows_total = T;
     KernelTimer tm(1, st);
-    hipError_t e = qbl::launch_prep(p, st);
+    hipError_t e = qbl::launch_prep(p, tm.ctx());
     if (e != hipSuccess) return hip_fail(e, "prep launch");
     tm.stop();
     if (glue) x = xin_buf;
@@ -743,7 +746,7 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     a.t = T > 0 ? t_buf : nullptr;
     a.t_stride = T;
     KernelTimer tm(0, st);
-    hipError_t e = qbl::launch_gemv(a, st);
+    hipError_t e = qbl::launch_gemv(a, tm.ctx());
     if (e != hipSuccess) return hip_fail(e, "gemv launch");
     tm.stop();
   }
@@ -761,7 +764,7 @@ qbl_status run_rms(const float* v, int64_t n, float* y, hipStream_t st) {
   p.v_stride = n;
   p.xin = y;
   KernelTimer tm(1, st);
-  hipError_t e = qbl::launch_prep(p, st);
+  hipError_t e = qbl::launch_prep(p, tm.ctx());
   if (e != hipSuccess) return hip_fail(e, "rms launch");
   tm.stop();
   return QBL_OK;
@@ -910,7 +913,7 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
     a.ws = static_cast<uint16_t*>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
     KernelTimer tm(2, st);
-    hipError_t e = qbl::launch_jit(a, st);
+    hipError_t e = qbl::launch_jit(a, tm.ctx());
     if (e != hipSuccess) return hip_fail(e, "jit launch");
     tm.stop();
     if (T > 0) L->mark_use(st);
