@@ -90,6 +90,27 @@ def time_loop(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def counter_traffic(summary):
+    """HBM bytes per launch measured with rocprofv3 byte counters, as recorded in
+    a profiles/ summary; None when the kernel source changed since then."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("    "):
+            k, v = line.strip().split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        src = open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def bench_block(torch, q, workloads, args):
     wl = workloads.block()
     copies = args.copies
@@ -123,7 +144,8 @@ def bench_block(torch, q, workloads, args):
     avg_us = ms_gemv / max(n_gemv, 1) * 1e3
     achieved = gemv_bytes_step / launches_per_step / (avg_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": counter_traffic("gemv_block7b_q8_r16_counters.md"),
             "kernel": "gemv_kernel (fused q8_0 dequant-GEMV + LoRA expand)",
             "timing": "HIP events attached to each GEMV dispatch (hipExtLaunchKernelGGL) on the launch stream",
             "launches_per_step": launches_per_step, "avg_launch_us": round(avg_us, 2),
