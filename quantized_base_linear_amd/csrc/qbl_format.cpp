@@ -170,8 +170,9 @@ void repack_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, uint8_t
   parallel_for(n, nthreads, [&](int64_t r) {
     for (int64_t b = 0; b < nb; ++b) {
       const uint8_t* p = blocks + (r * nb + b) * bb;
-      if (qtype == QBL_Q8_0) {
-        std::memcpy(qs + r * k + 32 * b, p + 2, 32);
+      if (qtype == QBL_Q8_0) {  // offset-binary on the device: u = q + 128
+        uint8_t* dst = qs + r * k + 32 * b;
+        for (int j = 0; j < 32; ++j) dst[j] = (uint8_t)(p[2 + j] ^ 0x80u);
         std::memcpy(sc + (r * nb + b) * 2, p, 2);
       } else {
         std::memcpy(qs + r * (k / 2) + 16 * b, p + 4, 16);

@@ -227,12 +227,11 @@ struct Fmt {
   }
 };
 
-// Sum_j q_j x_j over one q8_0 chunk of 16 int8 weights.  Each byte is biased
-// to unsigned (xor 0x80) so it converts with v_cvt_f32_ubyte; the bias is
-// removed with the chunk's x sum: sum (u-128) x = sum u x - 128 sum x.
+// Sum_j q_j x_j over one q8_0 chunk of 16 weights.  The device stores q8_0
+// bytes offset-binary (u = q + 128), which convert with v_cvt_f32_ubyte; the
+// offset is removed with the chunk's x sum: sum (u-128) x = sum u x - 128 sum x.
 __device__ __forceinline__ float dot_q8(const uint4 q, const float4* xv, float xsum) {
-  const uint32_t u[4] = {q.x ^ 0x80808080u, q.y ^ 0x80808080u, q.z ^ 0x80808080u,
-                         q.w ^ 0x80808080u};
+  const uint32_t u[4] = {q.x, q.y, q.z, q.w};
   float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
   for (int w = 0; w < 4; w += 2) {
@@ -320,7 +319,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     const int CT = kt / WPC;
     const int c0 = k0 / WPC;
 
-    // weight stream first: every load of this tile in flight before any use
+    // this thread's chunks of x first (they gate the barrier), then the whole
+    // weight stream of the wave, then x into LDS
+    constexpr int XC = 1;  // x chunks per thread loaded ahead of the weights
+    float4 xv_st[XC][NS];
+#pragma unroll
+    for (int h = 0; h < XC; ++h) {
+      const int i = tid + kThreads * h;
+      const int b = i / CT, c = i - b * CT;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        xv_st[h][j] = (i < BB * CT && b < B)
+                          ? *reinterpret_cast<const float4*>(a.x + (int64_t)b * a.x_stride + k0 + c * WPC + 4 * j)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
     uint4 q[RPW][CPL];
     uint32_t sc[RPW][CPL];
 #pragma unroll
@@ -341,14 +354,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     if (k0 == 0 && n_ad > 0)
       for (int i = tid; i < B * T; i += kThreads) ts[i] = a.t[i];
     // stage whole chunks of x and their sums
-    for (int i = tid; i < BB * CT; i += kThreads) {
+    auto stage = [&](int i, const float4* v) {
       const int b = i / CT, c = i - b * CT;
-      float4 v[NS];
       float sum = 0.0f;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        v[j] = b < B ? *reinterpret_cast<const float4*>(a.x + (int64_t)b * a.x_stride + k0 + c * WPC + 4 * j)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
         sum += v[j].x;
         sum += v[j].y;
         sum += v[j].z;
@@ -358,6 +368,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
       for (int j = 0; j < NS; ++j)
         *reinterpret_cast<float4*>(xs + b * KT + c * WPC + 4 * F::slot(c, j)) = v[j];
       xsum[b * tile_chunks + c] = sum;
+    };
+#pragma unroll
+    for (int h = 0; h < XC; ++h)
+      if (tid + kThreads * h < BB * CT) stage(tid + kThreads * h, xv_st[h]);
+    for (int i = tid + kThreads * XC; i < BB * CT; i += kThreads) {
+      const int b = i / CT, c = i - b * CT;
+      float4 v[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        v[j] = b < B ? *reinterpret_cast<const float4*>(a.x + (int64_t)b * a.x_stride + k0 + c * WPC + 4 * j)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      stage(i, v);
     }
     __syncthreads();
 
@@ -387,7 +409,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  // epilogue: base sum complete, then the adapters in list order
+  // epilogue: each lane adds s_i * B_i[row][j] * t_i[j] for its j to its
+  // partial sum, adapters in list order; then one wave reduction per output
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int row = row0 + r;
@@ -395,20 +418,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int b = 0; b < BB; ++b) {
       if (b >= B) break;
-      float y = wave_sum(acc[r][b]);
+      float v = acc[r][b];
       for (int i = 0; i < n_ad; ++i) {
         const int rk = g.lora.rank[i];
         const float* ti = ts + b * T + g.lora.toff[i];
-        float p = 0.0f;
         if (prefetch) {
           const float bv = i == 0 ? bpre[r][0] : bpre[r][1];
-          if (lane < rk) p = bv * ti[lane];
+          if (lane < rk) v = fmaf(g.lora.scale[i], bv * ti[lane], v);
         } else {
           const float* Br = g.lora.B[i] + (int64_t)row * rk;
+          float p = 0.0f;
           for (int j = lane; j < rk; j += 64) p = fmaf(Br[j], ti[j], p);
+          v = fmaf(g.lora.scale[i], p, v);
         }
-        y = fmaf(g.lora.scale[i], wave_sum(p), y);
       }
+      const float y = wave_sum(v);
       if (lane == 0) g.y[(int64_t)b * g.y_stride + row] = y;
     }
   }
@@ -422,194 +446,6 @@ hipError_t allow_dyn_lds(const void* fn, size_t bytes) {
   if (bytes <= 64 * 1024) return hipSuccess;
   if (bytes > kMaxDynLds) return hipErrorInvalidValue;
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
-// ---------------------------------------------------------------------------
-// Batch-1 streaming variant.  A persistent grid of about two workgroups per CU
-// stages x (and t) once per workgroup; its waves then walk row sets
-// (RPW rows each, assigned round robin over all waves of the grid) with the
-// next set's weight, scale and B loads in flight while the current set is
-// reduced, so each CU keeps a steady stream of 16-byte loads outstanding
-// instead of ramping up and draining once per workgroup.
-// ---------------------------------------------------------------------------
-template <int QT, int CPL, int RPW>
-struct StreamBuf {
-  uint4 q[RPW][CPL];
-  uint32_t sc[RPW][CPL];
-  float bp[RPW][kPrefetchAdapters];
-  int seg, row0;
-};
-
-template <int QT, int CPL, int RPW>
-__device__ __forceinline__ void stream_load(const GemvArgs& a, int set, int lane, int CT, int nblk,
-                                            StreamBuf<QT, CPL, RPW>& B) {
-  const int s = (a.nseg > 2 && set >= a.seg[2].wg_begin) ? 2 : (a.nseg > 1 && set >= a.seg[1].wg_begin) ? 1 : 0;
-  const GemvSeg& g = a.seg[s];
-  B.seg = s;
-  B.row0 = (set - g.wg_begin) * RPW;
-  const int64_t row_bytes = QT == QBL_FMT_Q8 ? (int64_t)a.k : (int64_t)a.k / 2;
-  const bool prefetch = g.lora.prefetch != 0;
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int lrow = min(B.row0 + r, g.n - 1);
-    const uint8_t* qrow = g.qs + (int64_t)lrow * row_bytes;
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int c = min(lane + 64 * u, CT - 1);
-      B.q[r][u] = stream_load16(qrow + (int64_t)c * 16);
-      if (QT == QBL_FMT_Q8)
-        B.sc[r][u] = reinterpret_cast<const uint16_t*>(g.sc)[(int64_t)lrow * nblk + (c >> 1)];
-      else
-        B.sc[r][u] = reinterpret_cast<const uint32_t*>(g.sc)[(int64_t)lrow * nblk + c];
-    }
-#pragma unroll
-    for (int i = 0; i < kPrefetchAdapters; ++i) {
-      B.bp[r][i] = 0.0f;
-      if (prefetch && i < g.lora.n_ad && lane < g.lora.rank[i])
-        B.bp[r][i] = g.lora.B[i][(int64_t)lrow * g.lora.rank[i] + lane];
-    }
-  }
-}
-
-template <int QT, int CPL, int RPW>
-__device__ __forceinline__ void stream_reduce(const GemvArgs& a, int lane, int CT, const float* xs,
-                                              const float* xsum, const float* ts,
-                                              const StreamBuf<QT, CPL, RPW>& B) {
-  using F = Fmt<QT>;
-  constexpr int WPC = F::kWeightsPerChunk;
-  constexpr int NS = F::kSlots;
-  const GemvSeg& g = a.seg[B.seg];
-  float acc[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
-#pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    const int c = lane + 64 * u;
-    if (c < CT) {
-      const float* xc = xs + c * WPC;
-      float4 xv[NS];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) xv[j] = *reinterpret_cast<const float4*>(xc + 4 * F::slot(c, j));
-      const float xsc = xsum[c];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const float d = h2f(B.sc[r][u]);
-        if (QT == QBL_FMT_Q8) {
-          acc[r] = fmaf(d, dot_q8(B.q[r][u], xv, xsc), acc[r]);
-        } else {
-          acc[r] = fmaf(d, dot_q4(B.q[r][u], xv), acc[r]);
-          acc[r] = fmaf(h2f(B.sc[r][u] >> 16), xsc, acc[r]);
-        }
-      }
-    }
-  }
-  const bool prefetch = g.lora.prefetch != 0;
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int row = B.row0 + r;
-    if (row >= g.n) break;
-    float y = wave_sum(acc[r]);
-    for (int i = 0; i < g.lora.n_ad; ++i) {
-      const int rk = g.lora.rank[i];
-      const float* ti = ts + g.lora.toff[i];
-      float p = 0.0f;
-      if (prefetch) {
-        const float bv = i == 0 ? B.bp[r][0] : B.bp[r][1];
-        if (lane < rk) p = bv * ti[lane];
-      } else {
-        const float* Br = g.lora.B[i] + (int64_t)row * rk;
-        for (int j = lane; j < rk; j += 64) p = fmaf(Br[j], ti[j], p);
-      }
-      y = fmaf(g.lora.scale[i], wave_sum(p), y);
-    }
-    if (lane == 0) g.y[row] = y;
-  }
-}
-
-template <int QT, int CPL, int RPW>
-__global__ __launch_bounds__(kThreads) void gemv_stream_kernel(GemvArgs a) {
-  extern __shared__ float lds[];
-  using F = Fmt<QT>;
-  constexpr int WPC = F::kWeightsPerChunk;
-  constexpr int NS = F::kSlots;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int K = a.k, CT = K / WPC, nblk = K / 32, T = a.t_stride;
-  float* xs = lds;          // [K], slots rotated per chunk
-  float* xsum = xs + K;     // [CT]
-  float* ts = xsum + CT;    // [T]
-  const int total = a.grid;  // row sets over all segments
-  const int TW = gridDim.x * kWaves;
-  int set = blockIdx.x * kWaves + wave;
-
-  StreamBuf<QT, CPL, RPW> b0, b1;
-  if (set < total) stream_load(a, set, lane, CT, nblk, b0);
-
-  for (int i = tid; i < T; i += kThreads) ts[i] = a.t[i];
-  for (int c = tid; c < CT; c += kThreads) {
-    float4 v[NS];
-    float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      v[j] = *reinterpret_cast<const float4*>(a.x + c * WPC + 4 * j);
-      sum += v[j].x;
-      sum += v[j].y;
-      sum += v[j].z;
-      sum += v[j].w;
-    }
-#pragma unroll
-    for (int j = 0; j < NS; ++j) *reinterpret_cast<float4*>(xs + c * WPC + 4 * F::slot(c, j)) = v[j];
-    xsum[c] = sum;
-  }
-  __syncthreads();
-
-  while (set < total) {
-    int next = set + TW;
-    if (next < total) stream_load(a, next, lane, CT, nblk, b1);
-    stream_reduce(a, lane, CT, xs, xsum, ts, b0);
-    set = next;
-    if (set >= total) break;
-    next = set + TW;
-    if (next < total) stream_load(a, next, lane, CT, nblk, b0);
-    stream_reduce(a, lane, CT, xs, xsum, ts, b1);
-    set = next;
-  }
-}
-
-constexpr int kStreamMaxK = 32768;  // x, its chunk sums and t must fit the LDS of one workgroup
-
-template <int QT, int CPL>
-hipError_t launch_stream(GemvArgs& a, const LaunchCtx& lc) {
-  constexpr int RPW = CPL <= 4 ? 2 : 1;
-  int sets = 0;
-  for (int i = 0; i < a.nseg; ++i) {
-    a.seg[i].wg_begin = sets;  // first row set of the segment
-    sets += (a.seg[i].n + RPW - 1) / RPW;
-  }
-  a.grid = sets;
-  a.rpw = RPW;
-  const size_t lds = sizeof(float) * ((size_t)a.k + a.k / Fmt<QT>::kWeightsPerChunk + (size_t)a.t_stride);
-  if (lds > kMaxDynLds) return hipErrorInvalidValue;
-  hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(&gemv_stream_kernel<QT, CPL, RPW>), lds);
-  if (e != hipSuccess) return e;
-  const int per_cu = lds <= 48 * 1024 ? 2 : 1;
-  const int max_waves = 256 * per_cu * kWaves;
-  const int per_wave = (sets + max_waves - 1) / max_waves;          // sets per wave, balanced
-  const int waves = (sets + per_wave - 1) / per_wave;
-  const int grid = (waves + kWaves - 1) / kWaves;
-  QBL_LAUNCH((gemv_stream_kernel<QT, CPL, RPW>), dim3(grid), dim3(kThreads), lds, lc, a);
-  return hipGetLastError();
-}
-
-template <int QT>
-hipError_t launch_stream_cpl(GemvArgs& a, const LaunchCtx& lc) {
-  const int cpl = (a.k / Fmt<QT>::kWeightsPerChunk + 63) / 64;
-  if (cpl <= 1) return launch_stream<QT, 1>(a, lc);
-  if (cpl <= 2) return launch_stream<QT, 2>(a, lc);
-  if (cpl <= 4) return launch_stream<QT, 4>(a, lc);
-  if (cpl <= 8) return launch_stream<QT, 8>(a, lc);
-  if (cpl <= 12) return launch_stream<QT, 12>(a, lc);
-  if (cpl <= 16) return launch_stream<QT, 16>(a, lc);
-  return hipErrorInvalidValue;
 }
 
 template <int QT, int BB, int CPL, int RPW>
@@ -634,8 +470,7 @@ hipError_t launch_one(GemvArgs& a, const LaunchCtx& lc) {
 // rows per wave: enough weight loads in flight per wave without exhausting VGPRs
 template <int QT, int BB, int CPL>
 hipError_t launch_rpw(GemvArgs& a, const LaunchCtx& lc) {
-  if constexpr (BB == 1 && CPL <= 4) return launch_one<QT, BB, CPL, 4>(a, lc);
-  else if constexpr (BB == 1 && CPL <= 8) return launch_one<QT, BB, CPL, 2>(a, lc);
+  if constexpr (BB == 1 && CPL <= 8) return launch_one<QT, BB, CPL, 2>(a, lc);
   else return launch_one<QT, BB, CPL, 1>(a, lc);
 }
 
@@ -700,10 +535,6 @@ hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc) {
     L.prefetch = L.n_ad <= kPrefetchAdapters;
     for (int j = 0; j < L.n_ad; ++j)
       if (L.rank[j] > 64) L.prefetch = 0;
-  }
-  if (a.batch == 1 && a.k <= kStreamMaxK) {
-    a.kt = a.k;
-    return a.qtype == QBL_FMT_Q8 ? launch_stream_cpl<QBL_FMT_Q8>(a, lc) : launch_stream_cpl<QBL_FMT_Q4>(a, lc);
   }
   return a.qtype == QBL_FMT_Q8 ? launch_batch<QBL_FMT_Q8>(a, bb, cpl, lc)
                                : launch_batch<QBL_FMT_Q4>(a, bb, cpl, lc);

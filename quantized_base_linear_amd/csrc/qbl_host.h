@@ -31,7 +31,7 @@ int quantize_rows(int qtype, const float* w, int64_t n, int64_t k, uint8_t* bloc
 int dequantize_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, float* out);
 
 // Canonical blocks -> device layout (host staging buffers):
-//   q8_0 : qs int8 [n][k] and d fp16 [n][k/32]
+//   q8_0 : qs offset-binary bytes u = q + 128 [n][k] and d fp16 [n][k/32]
 //   q4_sm: qs packed nibbles [n][k/2] and dm uint32 (d | m << 16) [n][k/32]
 void repack_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, uint8_t* qs, uint8_t* sc,
                  int nthreads);

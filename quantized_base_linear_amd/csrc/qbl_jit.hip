@@ -185,7 +185,7 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
         for (int j = 0; j < 4; ++j) {
           float deq;
           if (QT == QBL_FMT_Q8)
-            deq = d * (float)(int8_t)((qd[g] >> (8 * j)) & 0xFFu);          // exact in float32
+            deq = d * (float)((int)((qd[g] >> (8 * j)) & 0xFFu) - 128);  // offset-binary byte; exact in float32
           else
             deq = fmaf(d, (float)((qd[g] >> (4 * j)) & 0xFu), mn);           // float32(d q + m)
           wv[j] = RS > 0 ? deq + dsum[4 * g + j] : deq;

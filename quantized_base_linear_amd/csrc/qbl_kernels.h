@@ -36,7 +36,7 @@ struct LoraSeg {
 
 // One linear of a fused GEMV launch.
 struct GemvSeg {
-  const uint8_t* qs;   // q8_0: int8 [n][k]; q4_sm: packed nibbles [n][k/2]
+  const uint8_t* qs;   // q8_0: offset-binary bytes q + 128 [n][k]; q4_sm: packed nibbles [n][k/2]
   const void* sc;      // q8_0: fp16 d [n][k/32]; q4_sm: uint32 (d | m << 16) [n][k/32]
   float* y;            // [batch][y_stride]
   int64_t y_stride;
