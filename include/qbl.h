@@ -207,7 +207,14 @@ qbl_status qbl_comp_free(qbl_comp* comp);
  *   op 0: qbl_linear on `index` = linear at batch m;
  *   op 1: qbl_linear_jit on linear `index` with m rows;
  *   op 2: qbl_block / qbl_decode (index ignored; m ignored).
- * The size depends on the current list; query after attach. */
+ * The size depends on the current list; query after attach.
+ * At batch 1 (ops 0 and 2) one launch both computes the adapter shrink and
+ * consumes it: each shrink value is stored with the launch's number beside it,
+ * and readers wait until they see that number.  Zero the buffer once before its
+ * first use (e.g. hipMemset) so that it holds no stale number; the library
+ * keeps it valid afterwards.  Launch numbers repeat after 2^32 launches.  Runs
+ * sharing one workspace must be ordered on one stream: concurrent runs on one
+ * workspace race on its contents. */
 qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index, int32_t m,
                                int64_t* bytes_out);
 

@@ -260,12 +260,12 @@ def qbl_workspace_bytes(comp, op: int, index: int = 0, m: int = 1) -> int:
 
 
 def workspace(comp, op: int, index: int = 0, m: int = 1, device=None):
-    """A device byte buffer of the size qbl_workspace_bytes reports (None if 0)."""
+    """A zeroed device byte buffer of the size qbl_workspace_bytes reports (None if 0)."""
     import torch
     nb = qbl_workspace_bytes(comp, op, index, m)
     if nb == 0:
         return None
-    return torch.empty(nb, dtype=torch.uint8, device=device or "cuda")
+    return torch.zeros(nb, dtype=torch.uint8, device=device or "cuda")
 
 
 def _ws(ws):

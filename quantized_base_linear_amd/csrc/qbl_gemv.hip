@@ -17,6 +17,8 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "qbl_kernels.h"
 
 namespace qbl {
@@ -448,6 +450,438 @@ hipError_t allow_dyn_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+
+// ---------------------------------------------------------------------------
+// Batch-1 kernel: glue + shrink + GEMV + expand in one launch.
+//
+// Layout of the work.  A workgroup of W waves splits the input dimension: the
+// 16-byte chunks of a weight row are taken in blocks of 64 (one per lane), and
+// wave w owns blocks w, w+W, w+2W, ...  Each lane loads the input values under
+// its chunks once into registers and keeps them for every row the workgroup
+// computes, so the input is read once per workgroup however many rows it has.
+// Rows are streamed in groups of G, the next group's loads in flight while the
+// current one is consumed; a row's partial sums are reduced within each wave,
+// then across the W waves in LDS, in a fixed order.
+//
+// Glue.  The input is s = v0 + v1 + v2 (left to right), scaled by the RMS factor
+// c = 1/sqrt(mean(s^2) + 1e-6) when rms is set; c multiplies the finished dot
+// products.  With `sum` set, the segments (same height) are computed by the
+// same workgroups and written as one vector y0 = y_seg0 + y_seg1 (+ y_seg2): the
+// block's glue needs only the sum of parallel projections.
+//
+// Shrink.  Workgroups [0, shrink_wgs) compute t = c (A s), kRS rows of A each,
+// and store each value as one 64-bit word tagged with the launch's number.  The
+// dispatcher hands out workgroups in index order, so they are resident before
+// any GEMV workgroup, and they never wait.  GEMV workgroups read t only after
+// their row loop, waiting (bounded) until each word carries this launch's tag:
+// the data is its own flag, so the hand-off needs no counters, fences or cache
+// maintenance and nothing is reset afterwards.  A violated assumption shows as
+// wrong values, never as a hang.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float tagged_get(const uint64_t* p, uint32_t tag, int spin_limit) {
+  uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int spins = 0; (uint32_t)(w >> 32) != tag && spins < spin_limit; ++spins) {
+    __builtin_amdgcn_s_sleep(1);
+    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return __uint_as_float((uint32_t)w);
+}
+
+constexpr int kB1MaxSlots = 64;   // output rows (over all segments) per workgroup
+constexpr int kB1MaxT = kMaxSegs * 512;
+constexpr int kB1PrefetchPerThread = 8;  // B values a thread loads ahead of the row loop
+
+template <int QT, int CPW>
+struct B1Shape {
+  static constexpr int kNS = Fmt<QT>::kSlots;
+  static constexpr int kG = CPW >= 2 ? 2 : 4;                                   // rows per load group
+  static constexpr int kRS = CPW * kNS >= 16 ? 1 : 16 / (CPW * kNS);           // A rows per shrink workgroup
+};
+
+// One DPP exchange-and-add step of the transposed row reduction: lanes whose
+// bit (the partner distance) is clear keep the first half of the values, the
+// others the second half; each adds its partner's copy of the half it keeps.
+template <int CTRL, int N>
+__device__ __forceinline__ void fold_half(float (&p)[8], bool upper) {
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float send = upper ? p[k] : p[k + N / 2];
+    const float keep = upper ? p[k + N / 2] : p[k];
+    p[k] = keep + dpp_mov<CTRL>(send);
+  }
+}
+
+// Reduces G per-lane partials (one per row) over each 16-lane row of the wave.
+// Afterwards lane i of a 16-lane row holds the partial of row (i >> (4 - log2 G))
+// in p[0]: lanes 0, 16/G, 2*16/G, ... hold rows 0, 1, 2, ...
+template <int G>
+__device__ __forceinline__ void reduce_rows16(float (&p)[8], int lane) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G");
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  if constexpr (G == 8) {
+    fold_half<0x140, 8>(p, b3);  // row_mirror: partner 15 - i
+    fold_half<0x141, 4>(p, b2);  // row_half_mirror: partner 7 - i
+    fold_half<0x4E, 2>(p, b1);   // quad_perm [2,3,0,1]: partner i ^ 2
+    p[0] += dpp_mov<0xB1>(p[0]);  // quad_perm [1,0,3,2]
+  } else if constexpr (G == 4) {
+    fold_half<0x140, 4>(p, b3);
+    fold_half<0x141, 2>(p, b2);
+    p[0] += dpp_mov<0x4E>(p[0]);
+    p[0] += dpp_mov<0xB1>(p[0]);
+  } else if constexpr (G == 2) {
+    fold_half<0x140, 2>(p, b3);
+    p[0] += dpp_mov<0x141>(p[0]);
+    p[0] += dpp_mov<0x4E>(p[0]);
+    p[0] += dpp_mov<0xB1>(p[0]);
+  } else {
+    p[0] += dpp_mov<0x140>(p[0]);
+    p[0] += dpp_mov<0x141>(p[0]);
+    p[0] += dpp_mov<0x4E>(p[0]);
+    p[0] += dpp_mov<0xB1>(p[0]);
+  }
+}
+
+template <int QT, int W, int CPW, int G>
+__global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
+  using F = Fmt<QT>;
+  using S = B1Shape<QT, CPW>;
+  constexpr int WPC = F::kWeightsPerChunk;
+  constexpr int NS = F::kSlots;
+  constexpr int RS = S::kRS;
+  constexpr int NT = W * 64;
+  constexpr int LG = G == 8 ? 3 : G == 4 ? 2 : G == 2 ? 1 : 0;
+  __shared__ float red[W][kB1MaxSlots][4];  // per wave, slot, 16-lane row
+  __shared__ float ssred[W];
+  __shared__ float tl[kB1MaxT];
+  __shared__ float lb[kB1PrefetchPerThread * NT];
+  __shared__ float outl[kB1MaxSlots];
+
+  const GemvArgs& a = f.g;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int K = a.k, CT = K / WPC, nblk = K / 32;
+  const int64_t row_bytes = QT == QBL_FMT_Q8 ? (int64_t)K : (int64_t)K / 2;
+  const bool shrinker = (int)blockIdx.x < f.shrink_wgs;
+  const int wg = (int)blockIdx.x - f.shrink_wgs;
+
+  // this lane's chunks
+  int cidx[CPW];
+  bool cval[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int c = 64 * (u * W + wave) + lane;
+    cval[u] = c < CT;
+    cidx[u] = min(c, CT - 1);
+  }
+
+  // ---- the workgroup's rows (GEMV role)
+  int sg0 = 0, row0 = 0, nslots = 0, R = f.rows_per_wg;
+  if (!shrinker) {
+    if (f.sum) {
+      row0 = wg * R;
+      nslots = R * a.nseg;
+    } else {
+      sg0 = (a.nseg > 2 && wg >= a.seg[2].wg_begin) ? 2 : (a.nseg > 1 && wg >= a.seg[1].wg_begin) ? 1 : 0;
+      row0 = (wg - a.seg[sg0].wg_begin) * R;
+      nslots = R;
+    }
+  }
+  auto slot_seg = [&](int s) { return f.sum ? s / R : sg0; };
+  auto slot_row = [&](int s) { return row0 + (f.sum ? s % R : s); };
+
+  // ---- loads, in the order they are needed: the input (L2-resident), the B
+  // values of the expand, then the weight stream (or the A rows when shrinking)
+  float4 xr[CPW][NS];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (cval[u]) {
+        const int64_t o = (int64_t)cidx[u] * WPC + 4 * j;
+        t4 = *reinterpret_cast<const float4*>(f.v[0] + o);
+        if (f.nv > 1) t4 = add4(t4, *reinterpret_cast<const float4*>(f.v[1] + o));
+        if (f.nv > 2) t4 = add4(t4, *reinterpret_cast<const float4*>(f.v[2] + o));
+      }
+      xr[u][j] = t4;
+    }
+
+  const int tm = f.tmax_seg;
+  const bool bpf = !shrinker && f.n_ent > 0 && nslots * tm <= kB1PrefetchPerThread * NT;
+  float bq[kB1PrefetchPerThread];
+#pragma unroll
+  for (int m = 0; m < kB1PrefetchPerThread; ++m) {
+    bq[m] = 0.0f;
+    const int fl = tid + m * NT;
+    if (bpf && fl < nslots * tm) {
+      const int s = fl / tm, j = fl - s * tm;
+      const GemvSeg& g = a.seg[slot_seg(s)];
+      const int row = min(slot_row(s), g.n - 1);
+      int jj = j;
+      for (int i = 0; i < g.lora.n_ad; ++i) {
+        if (jj < g.lora.rank[i]) {
+          bq[m] = g.lora.B[i][(int64_t)row * g.lora.rank[i] + jj];
+          break;
+        }
+        jj -= g.lora.rank[i];
+      }
+    }
+  }
+
+  uint4 qa[G][CPW], qb[G][CPW];
+  uint32_t sa[G][CPW], sb[G][CPW];
+  float4 av[RS][CPW][NS];
+  auto load_group = [&](uint4 (&q)[G][CPW], uint32_t (&sc)[G][CPW], int grp) {
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const int s = grp * G + r;
+      if (s < nslots) {
+        const GemvSeg& g = a.seg[slot_seg(s)];
+        const int row = min(slot_row(s), g.n - 1);
+        const uint8_t* qrow = g.qs + (int64_t)row * row_bytes;
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) {
+          q[r][u] = stream_load16(qrow + (int64_t)cidx[u] * 16);
+          if (QT == QBL_FMT_Q8)
+            sc[r][u] = reinterpret_cast<const uint16_t*>(g.sc)[(int64_t)row * nblk + (cidx[u] >> 1)];
+          else
+            sc[r][u] = reinterpret_cast<const uint32_t*>(g.sc)[(int64_t)row * nblk + cidx[u]];
+        }
+      }
+    }
+  };
+  const int ngroups = (nslots + G - 1) / G;
+  if (shrinker) {
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      const int arow = (int)blockIdx.x * RS + rs;
+      const float* Ar = nullptr;
+      if (arow < f.rows_total) {
+        int e = 0, base = 0;
+        while (base + f.ent[e].rank <= arow) {
+          base += f.ent[e].rank;
+          ++e;
+        }
+        Ar = f.ent[e].A + (int64_t)(arow - base) * K;
+      }
+#pragma unroll
+      for (int u = 0; u < CPW; ++u)
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          av[rs][u][j] = Ar ? *reinterpret_cast<const float4*>(Ar + (int64_t)cidx[u] * WPC + 4 * j)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+    if (ngroups > 0) load_group(qa, sa, 0);
+    if (ngroups > 1) load_group(qb, sb, 1);
+  }
+
+  // ---- chunk sums and sum of squares of the input; B values into LDS
+  float xsm[CPW];
+  float ss = 0.0f;
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float4 t4 = xr[u][j];
+      sum += t4.x;
+      sum += t4.y;
+      sum += t4.z;
+      sum += t4.w;
+      ss = fmaf(t4.x, t4.x, fmaf(t4.y, t4.y, fmaf(t4.z, t4.z, fmaf(t4.w, t4.w, ss))));
+    }
+    xsm[u] = sum;
+  }
+  if (bpf) {
+#pragma unroll
+    for (int m = 0; m < kB1PrefetchPerThread; ++m) lb[tid + m * NT] = bq[m];
+  }
+  float cscale = 1.0f;
+  if (f.rms) {
+    const float w = wave_sum(ss);
+    if (lane == 0) ssred[wave] = w;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) tot += ssred[i];
+    cscale = 1.0f / sqrtf(tot / (float)K + 1e-6f);
+  }
+
+  if (shrinker) {
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      float p = 0.0f;
+#pragma unroll
+      for (int u = 0; u < CPW; ++u)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          p = fmaf(av[rs][u][j].x, xr[u][j].x, p);
+          p = fmaf(av[rs][u][j].y, xr[u][j].y, p);
+          p = fmaf(av[rs][u][j].z, xr[u][j].z, p);
+          p = fmaf(av[rs][u][j].w, xr[u][j].w, p);
+        }
+      p = wave_sum(p);
+      if (lane == 0) red[wave][rs][0] = p;
+    }
+    __syncthreads();
+    const int arow = (int)blockIdx.x * RS + tid;
+    if (tid < RS && arow < f.rows_total) {
+      float p = 0.0f;
+#pragma unroll
+      for (int i = 0; i < W; ++i) p += red[i][tid][0];
+      const uint64_t word = ((uint64_t)f.tag << 32) | __float_as_uint(cscale * p);
+      __hip_atomic_store(f.t + arow, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  // ---- row loop: two groups in flight; each group's rows reduced together
+  auto compute_group = [&](const uint4 (&q)[G][CPW], const uint32_t (&sc)[G][CPW], int grp) {
+    float p[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p[r] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        const float d = h2f(sc[r][u]);
+        if (QT == QBL_FMT_Q8) {
+          p[r] = fmaf(d, dot_q8(q[r][u], xr[u], xsm[u]), p[r]);
+        } else {
+          p[r] = fmaf(d, dot_q4(q[r][u], xr[u]), p[r]);
+          p[r] = fmaf(h2f(sc[r][u] >> 16), xsm[u], p[r]);
+        }
+      }
+    }
+    reduce_rows16<G>(p, lane);
+    const int r = (lane & 15) >> (4 - LG);
+    const int s = grp * G + r;
+    if ((lane & ((16 >> LG) - 1)) == 0 && s < nslots) red[wave][s][lane >> 4] = p[0];
+  };
+  for (int grp = 0; grp < ngroups; grp += 2) {
+    compute_group(qa, sa, grp);
+    if (grp + 2 < ngroups) load_group(qa, sa, grp + 2);
+    if (grp + 1 < ngroups) {
+      compute_group(qb, sb, grp + 1);
+      if (grp + 3 < ngroups) load_group(qb, sb, grp + 3);
+    }
+  }
+
+  // ---- shrink values of this launch, then the row outputs
+  for (int j = tid; j < f.rows_total; j += NT) tl[j] = tagged_get(f.t + j, f.tag, f.spin_limit);
+  __syncthreads();
+  if (tid < nslots) {
+    const int s = tid;
+    const GemvSeg& g = a.seg[slot_seg(s)];
+    const int row = slot_row(s);
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) v += (red[i][s][0] + red[i][s][1]) + (red[i][s][2] + red[i][s][3]);
+    v *= cscale;
+    int off = 0;
+    for (int i = 0; i < g.lora.n_ad; ++i) {
+      const int rk = g.lora.rank[i];
+      const float* ti = tl + g.lora.toff[i];
+      float p = 0.0f;
+      if (bpf) {
+        const float* bl = lb + s * tm + off;
+        for (int j = 0; j < rk; ++j) p = fmaf(bl[j], ti[j], p);
+      } else {
+        const float* Br = g.lora.B[i] + (int64_t)min(row, g.n - 1) * rk;
+        for (int j = 0; j < rk; ++j) p = fmaf(Br[j], ti[j], p);
+      }
+      v = fmaf(g.lora.scale[i], p, v);
+      off += rk;
+    }
+    if (f.sum) outl[s] = v;
+    else if (row < g.n) g.y[row] = v;
+  }
+  if (f.sum) {
+    __syncthreads();
+    const int row = row0 + tid;
+    if (tid < R && row < a.seg[0].n) {
+      float y = outl[tid];
+      for (int i = 1; i < a.nseg; ++i) y += outl[i * R + tid];
+      a.seg[0].y[row] = y;
+    }
+  }
+}
+
+// Workgroups of gemv_b1_kernel<QT, W, CPW, G> that one CU holds at once.
+template <int QT, int W, int CPW, int G>
+int b1_resident_per_cu() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (!n) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&gemv_b1_kernel<QT, W, CPW, G>), W * 64, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+int device_cus() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (!n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int QT, int W, int CPW, int G = B1Shape<QT, CPW>::kG>
+hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
+  using S = B1Shape<QT, CPW>;
+  GemvArgs& a = f.g;
+  f.shrink_wgs = (f.rows_total + S::kRS - 1) / S::kRS;
+  if (f.rows_per_wg <= 0) {
+    // one round: as many GEMV workgroups as the chip holds next to the shrink ones
+    const int units = f.sum ? a.seg[0].n : [&] { int u = 0; for (int i = 0; i < a.nseg; ++i) u += a.seg[i].n; return u; }();
+    const int slots = b1_resident_per_cu<QT, W, CPW, G>() * device_cus() - f.shrink_wgs;
+    const int rmax = kB1MaxSlots / (f.sum ? a.nseg : 1);
+    int r = slots > 0 ? (units + slots - 1) / slots : rmax;
+    f.rows_per_wg = r < 1 ? 1 : (r > rmax ? rmax : r);
+  }
+  int wg = 0;
+  if (f.sum) {
+    wg = (a.seg[0].n + f.rows_per_wg - 1) / f.rows_per_wg;
+  } else {
+    for (int i = 0; i < a.nseg; ++i) {
+      a.seg[i].wg_begin = wg;
+      wg += (a.seg[i].n + f.rows_per_wg - 1) / f.rows_per_wg;
+    }
+  }
+  a.grid = f.shrink_wgs + wg;
+  QBL_LAUNCH((gemv_b1_kernel<QT, W, CPW, G>), dim3(a.grid), dim3(W * 64), 0, lc, f);
+  return hipGetLastError();
+}
+
+template <int QT>
+hipError_t launch_b1_q(FusedArgs& f, const LaunchCtx& lc) {
+  const int blocks = (f.g.k / Fmt<QT>::kWeightsPerChunk + 63) / 64;
+  constexpr int kMaxCpw = QT == QBL_FMT_Q8 ? 4 : 2;  // input registers per lane: 64 floats
+  const int w = (blocks + 3) / 4 <= kMaxCpw ? 4 : 8;
+  const int cpw = (blocks + w - 1) / w;
+  if (w == 4) {
+    if (cpw <= 1) return launch_b1_t<QT, 4, 1>(f, lc);
+    if (cpw <= 2) return launch_b1_t<QT, 4, 2>(f, lc);
+    if constexpr (kMaxCpw >= 3) if (cpw <= 3) return launch_b1_t<QT, 4, 3>(f, lc);
+    if constexpr (kMaxCpw >= 4) if (cpw <= 4) return launch_b1_t<QT, 4, 4>(f, lc);
+  } else {
+    if (cpw <= 1) return launch_b1_t<QT, 8, 1>(f, lc);
+    if (cpw <= 2) return launch_b1_t<QT, 8, 2>(f, lc);
+    if constexpr (kMaxCpw >= 3) if (cpw <= 3) return launch_b1_t<QT, 8, 3>(f, lc);
+    if constexpr (kMaxCpw >= 4) if (cpw <= 4) return launch_b1_t<QT, 8, 4>(f, lc);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int QT, int BB, int CPL, int RPW>
 hipError_t launch_one(GemvArgs& a, const LaunchCtx& lc) {
   using F = Fmt<QT>;
@@ -518,6 +952,28 @@ hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc) {
   const int64_t floats = (int64_t)a.batch * a.k;
   if (floats <= kPrepLdsFloats) return launch_prep_t<true>(a, grid, sizeof(float) * floats, lc);
   return launch_prep_t<false>(a, grid, 0, lc);
+}
+
+bool fused_supported(int qtype, int k) {
+  const int wpc = qtype == QBL_FMT_Q8 ? 16 : 32;
+  const int max_cpw = qtype == QBL_FMT_Q8 ? 4 : 2;
+  return k % 32 == 0 && (k / wpc + 63) / 64 <= 8 * max_cpw;
+}
+
+hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc) {
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
+  GemvArgs& a = f.g;
+  if (a.batch != 1 || !fused_supported(a.qtype, a.k) || f.rows_total > kB1MaxT) return hipErrorInvalidValue;
+  int tmax = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    int t = 0;
+    for (int j = 0; j < a.seg[i].lora.n_ad; ++j) t += a.seg[i].lora.rank[j];
+    tmax = t > tmax ? t : tmax;
+    if (f.sum && a.seg[i].n != a.seg[0].n) return hipErrorInvalidValue;
+  }
+  f.tmax_seg = tmax;
+  f.rows_per_wg = 0;  // chosen by the launcher from the kernel's occupancy
+  return a.qtype == QBL_FMT_Q8 ? launch_b1_q<QBL_FMT_Q8>(f, lc) : launch_b1_q<QBL_FMT_Q4>(f, lc);
 }
 
 hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc) {

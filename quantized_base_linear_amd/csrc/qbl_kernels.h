@@ -83,6 +83,28 @@ struct PrepArgs {
   PrepEntry ent[kMaxPrepEntries];
 };
 
+// Batch-1 GEMV with the glue and the shrink in the same launch.  Workgroups
+// [0, shrink_wgs) compute t (kRS rows of A each) and store each value as one
+// 64-bit word tagged with the launch's number; the GEMV workgroups after them
+// read t only after their row loop, waiting (bounded) until each word carries
+// this launch's tag.  Input: s = v0 + v1 + v2, scaled by c (RMS or 1).
+struct FusedArgs {
+  GemvArgs g;          // segments (qs, sc, y, n, lora), nseg, qtype, k; wg_begin set by the launcher
+  const float* v[3];
+  int nv;
+  int rms;
+  int sum;             // 1: segments of equal height summed into seg[0].y
+  int rows_per_wg;     // set by the launcher
+  int tmax_seg;        // set by the launcher: largest total rank of one segment
+  int n_ent;
+  int rows_total;      // A rows = shrink results
+  int shrink_wgs;      // set by the launcher
+  int spin_limit;      // bound on the sleeps of one wait for a shrink result
+  uint32_t tag;        // this launch's number, never 0
+  uint64_t* t;         // [rows_total] shrink results, (tag << 32) | float bits
+  PrepEntry ent[kMaxPrepEntries];
+};
+
 // JIT prefill: Y[m][n] = sum_k X[m][k] * Weff[n][k], Weff built tile by tile.
 struct JitArgs {
   int qtype;
@@ -110,6 +132,9 @@ struct LaunchCtx {
 
 hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc);
 hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc);
+// false when the fused path cannot serve this shape (the caller then uses prep + gemv)
+bool fused_supported(int qtype, int k);
+hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc);
 hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc);
 int64_t jit_workspace_bytes(int n, int k, int total_rank);
 

@@ -646,7 +646,7 @@ BlockWs block_ws(void* ws, int64_t d, int64_t h, int64_t tmax) {
   };
   const int64_t m = std::max(d, h);
   w.xin = take(m);
-  w.t = take(std::max<int64_t>(tmax, 1));
+  w.t = take(2 * std::max<int64_t>(tmax, 1));  // batch-1 shrink results, 8 bytes each
   w.q = take(d);
   w.k = take(d);
   w.v = take(d);
@@ -677,41 +677,39 @@ int blocks_tmax(const ListImpl* L, int first_block, int n_blocks) {
 }
 
 // One launch group: linears sharing one input.  Input = c * (v0 + v1 + v2) with
-// c the RMS scale when rms != 0.  Launches the prep kernel (glue and/or shrink)
-// when needed, then one fused GEMV per quantisation type present.
+// c the RMS scale when rms != 0.  At batch 1 the glue, the shrink and the GEMV
+// share one launch (sync holds its counters); otherwise the prep kernel (glue
+// and/or shrink) runs first, then one GEMV per quantisation type present.
+constexpr int kSpinLimit = 1 << 22;  // ~0.1 s of s_sleep(1) before a wait gives up
+
+// Launch numbers that tag the shrink results of fused launches: unique per
+// launch (mod 2^32), never 0, so a zeroed workspace holds no valid result.
+uint32_t next_tag() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return t;
+}
+
 qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, float* const* outs,
                      int nlin, const float* const* vin, int nv, int rms, int batch, int64_t v_stride,
-                     float* xin_buf, float* t_buf, hipStream_t st) {
+                     float* xin_buf, float* t_buf, hipStream_t st, bool sum_ok = false,
+                     bool* summed = nullptr) {
+  if (summed) *summed = false;
   const int64_t K = base->lin[(size_t)lin[0]].k;
   int T = 0;
-  qbl::PrepArgs p{};
+  qbl::PrepEntry ent[qbl::kMaxPrepEntries];
+  int n_ent = 0;
   for (int i = 0; i < nlin; ++i) {
     for (const LoraRef& r : L->plan[(size_t)lin[i]]) {
-      p.ent[p.n_ent++] = qbl::PrepEntry{r.A, r.rank, T};
+      ent[n_ent++] = qbl::PrepEntry{r.A, r.rank, T};
       T += r.rank;
     }
   }
-  const bool glue = rms || nv > 1;
-  const float* x = vin[0];
-  if (glue || T > 0) {
-    for (int i = 0; i < nv; ++i) p.v[i] = vin[i];
-    p.nv = nv;
-    p.rms = rms;
-    p.batch = batch;
-    p.k = (int)K;
-    p.v_stride = v_stride;
-    p.xin = glue ? xin_buf : nullptr;
-    p.t = T > 0 ? t_buf : nullptr;
-    p.T = T;
-    p.rows_total = T;
-    KernelTimer tm(1, st);
-    hipError_t e = qbl::launch_prep(p, tm.ctx());
-    if (e != hipSuccess) return hip_fail(e, "prep launch");
-    tm.stop();
-    if (glue) x = xin_buf;
-  }
-  for (int qt = QBL_Q8_0; qt <= QBL_Q4_SM; ++qt) {
-    qbl::GemvArgs a{};
+  bool same_type = true;
+  for (int i = 1; i < nlin; ++i) same_type &= base->lin[(size_t)lin[i]].qtype == base->lin[(size_t)lin[0]].qtype;
+
+  auto fill_segments = [&](qbl::GemvArgs& a, int qt) {
     int toff = 0;
     for (int i = 0; i < nlin; ++i) {
       const DevLinear& D = base->lin[(size_t)lin[i]];
@@ -737,6 +735,59 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
       }
       toff += this_rank;
     }
+  };
+
+  const int qt0 = base->lin[(size_t)lin[0]].qtype;
+  if (batch == 1 && same_type && qbl::fused_supported(qt0, (int)K) &&
+      (T == 0 || t_buf) && v_stride == K) {
+    qbl::FusedArgs f{};
+    fill_segments(f.g, qt0);
+    f.g.qtype = qt0;
+    f.g.k = (int)K;
+    f.g.batch = 1;
+    for (int i = 0; i < nv; ++i) f.v[i] = vin[i];
+    f.nv = nv;
+    f.rms = rms;
+    f.sum = sum_ok && nlin > 1;
+    f.n_ent = n_ent;
+    for (int i = 0; i < n_ent; ++i) f.ent[i] = ent[i];
+    f.rows_total = T;
+    f.spin_limit = kSpinLimit;
+    f.tag = next_tag();
+    f.t = reinterpret_cast<uint64_t*>(t_buf);
+    KernelTimer tm(0, st);
+    hipError_t e = qbl::launch_fused(f, tm.ctx());
+    if (e != hipSuccess) return hip_fail(e, "fused gemv launch");
+    tm.stop();
+    if (summed) *summed = f.sum != 0;
+    return QBL_OK;
+  }
+
+  qbl::PrepArgs p{};
+  for (int i = 0; i < n_ent; ++i) p.ent[i] = ent[i];
+  p.n_ent = n_ent;
+  const bool glue = rms || nv > 1;
+  const float* x = vin[0];
+  if (glue || T > 0) {
+    for (int i = 0; i < nv; ++i) p.v[i] = vin[i];
+    p.nv = nv;
+    p.rms = rms;
+    p.batch = batch;
+    p.k = (int)K;
+    p.v_stride = v_stride;
+    p.xin = glue ? xin_buf : nullptr;
+    p.t = T > 0 ? t_buf : nullptr;
+    p.T = T;
+    p.rows_total = T;
+    KernelTimer tm(1, st);
+    hipError_t e = qbl::launch_prep(p, tm.ctx());
+    if (e != hipSuccess) return hip_fail(e, "prep launch");
+    tm.stop();
+    if (glue) x = xin_buf;
+  }
+  for (int qt = QBL_Q8_0; qt <= QBL_Q4_SM; ++qt) {
+    qbl::GemvArgs a{};
+    fill_segments(a, qt);
     if (!a.nseg) continue;
     a.qtype = qt;
     a.k = (int)K;
@@ -775,29 +826,34 @@ qbl_status run_rms(const float* v, int64_t n, float* y, hipStream_t st) {
 qbl_status run_block(const qbl_base* base, const ListImpl* L, const Block& B, const float* in,
                      int rms_in, const BlockWs& w, hipStream_t st) {
   const int f = B.first;
+  // At batch 1 the parallel projections can be written as their sum (all the
+  // glue needs); then the next group reads one vector instead of three or two.
+  bool summed = false;
   {
     const int lin[3] = {f, f + 1, f + 2};
     float* outs[3] = {w.q, w.k, w.v};
     const float* v[1] = {in};
-    if (qbl_status s = run_group(base, L, lin, outs, 3, v, 1, rms_in, 1, B.d, w.xin, w.t, st)) return s;
+    if (qbl_status s = run_group(base, L, lin, outs, 3, v, 1, rms_in, 1, B.d, w.xin, w.t, st, true, &summed))
+      return s;
   }
   {
     const int lin[1] = {f + 3};
     float* outs[1] = {w.a};
     const float* v[3] = {w.q, w.k, w.v};
-    if (qbl_status s = run_group(base, L, lin, outs, 1, v, 3, 1, 1, B.d, w.xin, w.t, st)) return s;
+    if (qbl_status s = run_group(base, L, lin, outs, 1, v, summed ? 1 : 3, 1, 1, B.d, w.xin, w.t, st)) return s;
   }
   {
     const int lin[2] = {f + 4, f + 5};
     float* outs[2] = {w.g, w.u};
     const float* v[1] = {w.a};
-    if (qbl_status s = run_group(base, L, lin, outs, 2, v, 1, 1, 1, B.d, w.xin, w.t, st)) return s;
+    if (qbl_status s = run_group(base, L, lin, outs, 2, v, 1, 1, 1, B.d, w.xin, w.t, st, true, &summed))
+      return s;
   }
   {
     const int lin[1] = {f + 6};
     float* outs[1] = {w.dd};
     const float* v[2] = {w.g, w.u};
-    if (qbl_status s = run_group(base, L, lin, outs, 1, v, 2, 1, 1, B.h, w.xin, w.t, st)) return s;
+    if (qbl_status s = run_group(base, L, lin, outs, 1, v, summed ? 1 : 2, 1, 1, B.h, w.xin, w.t, st)) return s;
   }
   return QBL_OK;
 }
@@ -814,6 +870,12 @@ qbl_status check_ws(void* ws, int64_t ws_bytes, int64_t need) {
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
+// qbl_linear: the shrink results t, float per batch row, or one tagged 8-byte
+// word each at batch 1 (the fused launch).
+int64_t linear_ws_bytes(int64_t batch, int64_t T) {
+  return align_up(batch == 1 ? T * 8 : batch * T * 4);
+}
+
 }  // namespace
 
 extern "C" qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index,
@@ -825,7 +887,7 @@ extern "C" qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int3
     if (op == 0) {
       if (index < 0 || index >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", index);
       if (m < 1 || m > QBL_MAX_BATCH) return fail(QBL_E_LIMIT, "batch %d outside 1..%d", m, QBL_MAX_BATCH);
-      *bytes_out = align_up((int64_t)m * L->total_rank[(size_t)index] * 4);
+      *bytes_out = linear_ws_bytes(m, L->total_rank[(size_t)index]);
       return QBL_OK;
     }
     if (op == 1) {
@@ -864,7 +926,7 @@ extern "C" qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x,
     std::lock_guard<std::mutex> g(comp->mu);
     auto L = std::atomic_load(&comp->list);
     const int T = L->total_rank[(size_t)linear];
-    if (qbl_status s = check_ws(ws, ws_bytes, align_up((int64_t)batch * T * 4))) return s;
+    if (qbl_status s = check_ws(ws, ws_bytes, linear_ws_bytes(batch, T))) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int lin[1] = {linear};
     float* outs[1] = {y};

@@ -106,8 +106,10 @@ def test_small_stack_free_running_chain(torch_cuda):
         b.q.qbl_comp_clear(b.comp)
         b.attach([1])
         assert np.array_equal(_decode(b, torch, x0, nb, 4), yab)
-        # decode of a sub-range of blocks equals chained single-block calls
+        # decode of a sub-range of blocks equals chained single-block calls up to
+        # rounding (decode folds the RMS scale of the previous block's output
+        # into the next launch instead of writing the scaled vector)
         y2 = _decode(b, torch, x0, 2, 1, first=1)
-        assert np.array_equal(y2[0], _block(b, torch, 2, _block(b, torch, 1, x0)))
+        assert rel_l2(y2[0], _block(b, torch, 2, _block(b, torch, 1, x0))) <= 1e-5
     finally:
         b.close()

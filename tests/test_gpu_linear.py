@@ -127,8 +127,14 @@ def test_ragged_shapes_and_batches(torch_cuda, qtype, n, k, batch):
         ref0 = oracle.linear_dual(L.qtype, b.or_blocks[0], n, k, x)
         assert rel_l2(y0, ref0) <= TOL
         assert rel_l2(y - y0, ref - ref0) <= TOL
-        for r in range(batch):      # rows of a batch are independent
-            assert np.array_equal(_run(b, torch, 0, x[r:r + 1]), y0[r:r + 1])
+        # rows of a batch are independent: other rows' values never change a
+        # row's bits; a row run alone (the batch-1 kernel) agrees to rounding
+        if batch > 1:
+            x2 = x.copy()
+            x2[1:] = -2.0 * x2[1:] + 0.5
+            assert np.array_equal(_run(b, torch, 0, x2)[0], y0[0])
+        for r in range(batch):
+            assert rel_l2(_run(b, torch, 0, x[r:r + 1]), y0[r:r + 1]) <= 1e-5
     finally:
         b.close()
 
