@@ -489,12 +489,11 @@ __device__ __forceinline__ float tagged_get(const uint64_t* p, uint32_t tag, int
 
 constexpr int kB1MaxSlots = 64;   // output rows (over all segments) per workgroup
 constexpr int kB1MaxT = kMaxSegs * 512;
-constexpr int kB1PrefetchPerThread = 8;  // B values a thread loads ahead of the row loop
 
 template <int QT, int CPW>
 struct B1Shape {
   static constexpr int kNS = Fmt<QT>::kSlots;
-  static constexpr int kG = CPW >= 2 ? 2 : 4;                                   // rows per load group
+  static constexpr int kG = CPW >= 3 ? 1 : 2;                                   // rows per load group
   static constexpr int kRS = CPW * kNS >= 16 ? 1 : 16 / (CPW * kNS);           // A rows per shrink workgroup
 };
 
@@ -541,8 +540,13 @@ __device__ __forceinline__ void reduce_rows16(float (&p)[8], int lane) {
   }
 }
 
+// waves per SIMD the register budget targets: 4 waves, one q8_0 block of chunks
+// per lane and two-row groups fit in 96 VGPRs, which lets 5 waves share a SIMD
+template <int QT, int W, int CPW>
+constexpr int b1_min_waves() { return W == 4 && CPW * Fmt<QT>::kSlots <= 4 ? 5 : 1; }
+
 template <int QT, int W, int CPW, int G>
-__global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
+__global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_kernel(FusedArgs f) {
   using F = Fmt<QT>;
   using S = B1Shape<QT, CPW>;
   constexpr int WPC = F::kWeightsPerChunk;
@@ -553,7 +557,6 @@ __global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
   __shared__ float red[W][kB1MaxSlots][4];  // per wave, slot, 16-lane row
   __shared__ float ssred[W];
   __shared__ float tl[kB1MaxT];
-  __shared__ float lb[kB1PrefetchPerThread * NT];
   __shared__ float outl[kB1MaxSlots];
 
   const GemvArgs& a = f.g;
@@ -604,28 +607,6 @@ __global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
       }
       xr[u][j] = t4;
     }
-
-  const int tm = f.tmax_seg;
-  const bool bpf = !shrinker && f.n_ent > 0 && nslots * tm <= kB1PrefetchPerThread * NT;
-  float bq[kB1PrefetchPerThread];
-#pragma unroll
-  for (int m = 0; m < kB1PrefetchPerThread; ++m) {
-    bq[m] = 0.0f;
-    const int fl = tid + m * NT;
-    if (bpf && fl < nslots * tm) {
-      const int s = fl / tm, j = fl - s * tm;
-      const GemvSeg& g = a.seg[slot_seg(s)];
-      const int row = min(slot_row(s), g.n - 1);
-      int jj = j;
-      for (int i = 0; i < g.lora.n_ad; ++i) {
-        if (jj < g.lora.rank[i]) {
-          bq[m] = g.lora.B[i][(int64_t)row * g.lora.rank[i] + jj];
-          break;
-        }
-        jj -= g.lora.rank[i];
-      }
-    }
-  }
 
   uint4 qa[G][CPW], qb[G][CPW];
   uint32_t sa[G][CPW], sb[G][CPW];
@@ -692,10 +673,6 @@ __global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
     }
     xsm[u] = sum;
   }
-  if (bpf) {
-#pragma unroll
-    for (int m = 0; m < kB1PrefetchPerThread; ++m) lb[tid + m * NT] = bq[m];
-  }
   float cscale = 1.0f;
   if (f.rms) {
     const float w = wave_sum(ss);
@@ -730,7 +707,9 @@ __global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
 #pragma unroll
       for (int i = 0; i < W; ++i) p += red[i][tid][0];
       const uint64_t word = ((uint64_t)f.tag << 32) | __float_as_uint(cscale * p);
-      __hip_atomic_store(f.t + arow, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int c = 0; c < kTCopies; ++c)
+        __hip_atomic_store(f.t + (int64_t)c * f.t_copy_stride + arow, word, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
@@ -758,7 +737,24 @@ __global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
     const int s = grp * G + r;
     if ((lane & ((16 >> LG) - 1)) == 0 && s < nslots) red[wave][s][lane >> 4] = p[0];
   };
+  // the first read of the shrink words goes out halfway through the row loop
+  // (the shrink workgroups, dispatched first, are done by then), so its round
+  // trip overlaps the remaining groups; a word still stale is read again at
+  // the end
+  constexpr int kTW = 2;
+  const uint64_t* tcopy = f.t + (int64_t)(wg % kTCopies) * f.t_copy_stride;
+  uint64_t tw[kTW];
+  bool tw_out = false;
+  auto issue_t = [&] {
+#pragma unroll
+    for (int m = 0; m < kTW; ++m) {
+      const int j = tid + m * NT;
+      tw[m] = j < f.rows_total ? __hip_atomic_load(tcopy + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    }
+    tw_out = true;
+  };
   for (int grp = 0; grp < ngroups; grp += 2) {
+    if (!tw_out && 2 * grp + 2 >= ngroups) issue_t();
     compute_group(qa, sa, grp);
     if (grp + 2 < ngroups) load_group(qa, sa, grp + 2);
     if (grp + 1 < ngroups) {
@@ -768,7 +764,14 @@ __global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
   }
 
   // ---- shrink values of this launch, then the row outputs
-  for (int j = tid; j < f.rows_total; j += NT) tl[j] = tagged_get(f.t + j, f.tag, f.spin_limit);
+  if (!tw_out) issue_t();
+#pragma unroll
+  for (int m = 0; m < kTW; ++m) {
+    const int j = tid + m * NT;
+    if (j < f.rows_total)
+      tl[j] = (uint32_t)(tw[m] >> 32) == f.tag ? __uint_as_float((uint32_t)tw[m]) : tagged_get(tcopy + j, f.tag, f.spin_limit);
+  }
+  for (int j = tid + kTW * NT; j < f.rows_total; j += NT) tl[j] = tagged_get(tcopy + j, f.tag, f.spin_limit);
   __syncthreads();
   if (tid < nslots) {
     const int s = tid;
@@ -778,20 +781,14 @@ __global__ __launch_bounds__(W * 64) void gemv_b1_kernel(FusedArgs f) {
 #pragma unroll
     for (int i = 0; i < W; ++i) v += (red[i][s][0] + red[i][s][1]) + (red[i][s][2] + red[i][s][3]);
     v *= cscale;
-    int off = 0;
     for (int i = 0; i < g.lora.n_ad; ++i) {
       const int rk = g.lora.rank[i];
       const float* ti = tl + g.lora.toff[i];
+      const float* Br = g.lora.B[i] + (int64_t)min(row, g.n - 1) * rk;
       float p = 0.0f;
-      if (bpf) {
-        const float* bl = lb + s * tm + off;
-        for (int j = 0; j < rk; ++j) p = fmaf(bl[j], ti[j], p);
-      } else {
-        const float* Br = g.lora.B[i] + (int64_t)min(row, g.n - 1) * rk;
-        for (int j = 0; j < rk; ++j) p = fmaf(Br[j], ti[j], p);
-      }
+#pragma unroll 8
+      for (int j = 0; j < rk; ++j) p = fmaf(Br[j], ti[j], p);
       v = fmaf(g.lora.scale[i], p, v);
-      off += rk;
     }
     if (f.sum) outl[s] = v;
     else if (row < g.n) g.y[row] = v;
@@ -866,19 +863,14 @@ template <int QT>
 hipError_t launch_b1_q(FusedArgs& f, const LaunchCtx& lc) {
   const int blocks = (f.g.k / Fmt<QT>::kWeightsPerChunk + 63) / 64;
   constexpr int kMaxCpw = QT == QBL_FMT_Q8 ? 4 : 2;  // input registers per lane: 64 floats
-  const int w = (blocks + 3) / 4 <= kMaxCpw ? 4 : 8;
-  const int cpw = (blocks + w - 1) / w;
-  if (w == 4) {
-    if (cpw <= 1) return launch_b1_t<QT, 4, 1>(f, lc);
-    if (cpw <= 2) return launch_b1_t<QT, 4, 2>(f, lc);
-    if constexpr (kMaxCpw >= 3) if (cpw <= 3) return launch_b1_t<QT, 4, 3>(f, lc);
-    if constexpr (kMaxCpw >= 4) if (cpw <= 4) return launch_b1_t<QT, 4, 4>(f, lc);
-  } else {
-    if (cpw <= 1) return launch_b1_t<QT, 8, 1>(f, lc);
-    if (cpw <= 2) return launch_b1_t<QT, 8, 2>(f, lc);
-    if constexpr (kMaxCpw >= 3) if (cpw <= 3) return launch_b1_t<QT, 8, 3>(f, lc);
-    if constexpr (kMaxCpw >= 4) if (cpw <= 4) return launch_b1_t<QT, 8, 4>(f, lc);
-  }
+  // up to one block of chunks per lane: 4 waves; past that, more waves beat
+  // more blocks per lane (fewer registers, more rows in flight)
+  if (blocks <= 4) return launch_b1_t<QT, 4, 1>(f, lc);
+  const int cpw = (blocks + 7) / 8;
+  if (cpw <= 1) return launch_b1_t<QT, 8, 1>(f, lc);
+  if (cpw <= 2) return launch_b1_t<QT, 8, 2>(f, lc);
+  if constexpr (kMaxCpw >= 3) if (cpw <= 3) return launch_b1_t<QT, 8, 3>(f, lc);
+  if constexpr (kMaxCpw >= 4) if (cpw <= 4) return launch_b1_t<QT, 8, 4>(f, lc);
   return hipErrorInvalidValue;
 }
 
@@ -964,14 +956,8 @@ hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc) {
   (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   GemvArgs& a = f.g;
   if (a.batch != 1 || !fused_supported(a.qtype, a.k) || f.rows_total > kB1MaxT) return hipErrorInvalidValue;
-  int tmax = 0;
-  for (int i = 0; i < a.nseg; ++i) {
-    int t = 0;
-    for (int j = 0; j < a.seg[i].lora.n_ad; ++j) t += a.seg[i].lora.rank[j];
-    tmax = t > tmax ? t : tmax;
+  for (int i = 0; i < a.nseg; ++i)
     if (f.sum && a.seg[i].n != a.seg[0].n) return hipErrorInvalidValue;
-  }
-  f.tmax_seg = tmax;
   f.rows_per_wg = 0;  // chosen by the launcher from the kernel's occupancy
   return a.qtype == QBL_FMT_Q8 ? launch_b1_q<QBL_FMT_Q8>(f, lc) : launch_b1_q<QBL_FMT_Q4>(f, lc);
 }

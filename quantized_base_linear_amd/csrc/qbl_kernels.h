@@ -95,13 +95,13 @@ struct FusedArgs {
   int rms;
   int sum;             // 1: segments of equal height summed into seg[0].y
   int rows_per_wg;     // set by the launcher
-  int tmax_seg;        // set by the launcher: largest total rank of one segment
   int n_ent;
   int rows_total;      // A rows = shrink results
   int shrink_wgs;      // set by the launcher
   int spin_limit;      // bound on the sleeps of one wait for a shrink result
   uint32_t tag;        // this launch's number, never 0
-  uint64_t* t;         // [rows_total] shrink results, (tag << 32) | float bits
+  uint64_t* t;         // kTCopies copies of the rows_total shrink results, (tag << 32) | float bits
+  int64_t t_copy_stride;  // words between copies (see t_copy_stride())
   PrepEntry ent[kMaxPrepEntries];
 };
 
@@ -135,6 +135,13 @@ hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc);
 // false when the fused path cannot serve this shape (the caller then uses prep + gemv)
 bool fused_supported(int qtype, int k);
 hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc);
+// The shrink results of a fused launch are stored kTCopies times, copy c read by
+// GEMV workgroups c, c + kTCopies, ...: every workgroup reads them, and one copy
+// would put all those reads on one memory channel.  Copies sit t_copy_stride(T)
+// words apart (a 256-byte multiple plus 256 bytes, so they fall on different
+// channels).
+constexpr int kTCopies = 8;
+inline int64_t t_copy_stride(int64_t rows) { return (rows + 31) / 32 * 32 + 32; }
 hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc);
 int64_t jit_workspace_bytes(int n, int k, int total_rank);
 

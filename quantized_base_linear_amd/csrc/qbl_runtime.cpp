@@ -646,7 +646,7 @@ BlockWs block_ws(void* ws, int64_t d, int64_t h, int64_t tmax) {
   };
   const int64_t m = std::max(d, h);
   w.xin = take(m);
-  w.t = take(2 * std::max<int64_t>(tmax, 1));  // batch-1 shrink results, 8 bytes each
+  w.t = take(std::max<int64_t>(2 * qbl::kTCopies * qbl::t_copy_stride(tmax), tmax));  // tagged 8-byte words
   w.q = take(d);
   w.k = take(d);
   w.v = take(d);
@@ -678,8 +678,9 @@ int blocks_tmax(const ListImpl* L, int first_block, int n_blocks) {
 
 // One launch group: linears sharing one input.  Input = c * (v0 + v1 + v2) with
 // c the RMS scale when rms != 0.  At batch 1 the glue, the shrink and the GEMV
-// share one launch (sync holds its counters); otherwise the prep kernel (glue
-// and/or shrink) runs first, then one GEMV per quantisation type present.
+// share one launch (the shrink results pass through t_buf as tagged words);
+// otherwise the prep kernel (glue and/or shrink) runs first, then one GEMV per
+// quantisation type present.
 constexpr int kSpinLimit = 1 << 22;  // ~0.1 s of s_sleep(1) before a wait gives up
 
 // Launch numbers that tag the shrink results of fused launches: unique per
@@ -755,6 +756,7 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     f.spin_limit = kSpinLimit;
     f.tag = next_tag();
     f.t = reinterpret_cast<uint64_t*>(t_buf);
+    f.t_copy_stride = qbl::t_copy_stride(T);
     KernelTimer tm(0, st);
     hipError_t e = qbl::launch_fused(f, tm.ctx());
     if (e != hipSuccess) return hip_fail(e, "fused gemv launch");
@@ -870,10 +872,11 @@ qbl_status check_ws(void* ws, int64_t ws_bytes, int64_t need) {
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
-// qbl_linear: the shrink results t, float per batch row, or one tagged 8-byte
-// word each at batch 1 (the fused launch).
+// qbl_linear: the shrink results t, float per batch row, or at batch 1 (the
+// fused launch) kTCopies copies of one tagged 8-byte word each.
 int64_t linear_ws_bytes(int64_t batch, int64_t T) {
-  return align_up(batch == 1 ? T * 8 : batch * T * 4);
+  if (T == 0) return 0;
+  return align_up(batch == 1 ? qbl::kTCopies * qbl::t_copy_stride(T) * 8 : batch * T * 4);
 }
 
 }  // namespace
