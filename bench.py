@@ -49,6 +49,19 @@ def linear_bytes(wl, i, with_a=True):
     return b
 
 
+def group_bytes(wl, lins):
+    """Algorithmic bytes of one batch-1 launch over linears `lins` sharing one
+    input: their quantised bases and LoRA factors, the input read once, one
+    output vector written."""
+    r = sum(a.rank for a in wl.adapters)
+    L0 = wl.linears[lins[0]]
+    b = 4 * (L0.k_in + L0.n_out)
+    for i in lins:
+        L = wl.linears[i]
+        b += wl.base_bytes(i) + 4 * r * (L.n_out + L.k_in)
+    return b
+
+
 def build_copies(q, wl, copies, adapter_idx):
     """One base holding `copies` copies of the workload's linears, one adapter
     per workload adapter covering every copy; returns (base, adapters, comp, blocks)."""
@@ -136,17 +149,17 @@ def bench_block(torch, q, workloads, args):
     n_gemv, ms_gemv = q.qbl_profile_read(q.KIND_GEMV)
     n_prep, ms_prep = q.qbl_profile_read(q.KIND_PREP)
     q.qbl_profile_enable(False)
-    # GEMV algorithmic bytes per step: base + B + x + y of the 7 linears plus
-    # the shrink results it reads (t), over the 4 fused launches
-    gemv_bytes_step = sum(linear_bytes(wl, i, with_a=False) for i in range(7))
-    gemv_bytes_step += 4 * (3 * 16 + 16 + 2 * 16 + 16)
+    # algorithmic bytes of the 4 batch-1 launches of a step: each reads its
+    # linears' quantised base, A and B factors and its input vector once, and
+    # writes one output vector (q+k+v and gate+up are written as their sums)
+    gemv_bytes_step = sum(group_bytes(wl, g) for g in ([0, 1, 2], [3], [4, 5], [6]))
     launches_per_step = n_gemv / args.steps
     avg_us = ms_gemv / max(n_gemv, 1) * 1e3
     achieved = gemv_bytes_step / launches_per_step / (avg_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counter_traffic("gemv_block7b_q8_r16_counters.md"),
-            "kernel": "gemv_kernel (fused q8_0 dequant-GEMV + LoRA expand)",
+            "kernel": "gemv_b1_kernel (batch-1 launch: glue + LoRA shrink + q8_0 dequant-GEMV + expand)",
             "timing": "HIP events attached to each GEMV dispatch (hipExtLaunchKernelGGL) on the launch stream",
             "launches_per_step": launches_per_step, "avg_launch_us": round(avg_us, 2),
             "bytes_per_launch": int(gemv_bytes_step / launches_per_step),
