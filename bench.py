@@ -163,7 +163,7 @@ def bench_block(torch, q, workloads, args):
             "timing": "HIP events attached to each GEMV dispatch (hipExtLaunchKernelGGL) on the launch stream",
             "launches_per_step": launches_per_step, "avg_launch_us": round(avg_us, 2),
             "bytes_per_launch": int(gemv_bytes_step / launches_per_step),
-            "prep_avg_launch_us": round(ms_prep / max(n_prep, 1) * 1e3, 2),
+            "prep_avg_launch_us": round(ms_prep / max(n_prep, 1) * 1e3, 2) if n_prep else None,
             "step_us_with_timing_events": round(ms_prof * 1e3, 1)}
     free_all(q, base, ads, comp)
     return wl, blocks, ms, step_bytes, gbs, roof

@@ -262,8 +262,9 @@ qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_blocks, con
 /* Kernel timing for measurement tools.  While enabled (on != 0), every launch
  * of the library's kernels is bracketed by a pair of HIP events recorded on the
  * launch stream.  Enabling clears earlier records.  qbl_profile_read waits for
- * the recorded events and returns, per kernel kind (0 = fused dequant-GEMV,
- * 1 = glue/shrink prep, 2 = JIT prefill GEMM), the number of launches and their
+ * the recorded events and returns, per kernel kind (0 = batch-1 / batched
+ * dequant-GEMV, 1 = glue/shrink prep, 2 = JIT prefill GEMM), the number of
+ * launches and their
  * summed duration in milliseconds.  Timing adds host work per launch: leave it
  * off in production. */
 qbl_status qbl_profile_enable(int32_t on);

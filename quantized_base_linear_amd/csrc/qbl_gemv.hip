@@ -19,6 +19,7 @@
 
 #include <atomic>
 
+#include "qbl_device.h"
 #include "qbl_kernels.h"
 
 namespace qbl {
@@ -30,27 +31,6 @@ constexpr int kLdsFloats = 16384;      // GEMV x tile budget per workgroup (64 K
 constexpr int kPrepLdsFloats = 36864;  // prep input staging budget (144 KiB)
 constexpr int kPrepAPre = 12;          // float4 of the A row held in registers per thread
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float lane_value(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-// Sum over the 64 lanes of a wave, returned to every lane.  Within each row of
-// 16 lanes: mirror, half-mirror and two quad permutations (each pair of lanes
-// adds the same two operands, so all 16 lanes end with the same value); the
-// four row sums are then combined in a fixed order.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_mov<0x140>(v);  // row_mirror
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
-}
-
 // Workgroup-wide sum in a fixed order; every thread receives it.  `red` holds
 // kWaves floats of LDS.
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -60,29 +40,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   const float s = (red[0] + red[1]) + (red[2] + red[3]);
   __syncthreads();
   return s;
-}
-
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-  return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xFFFFu)));
-}
-
-__device__ __forceinline__ float ub(uint32_t v, int byte) {
-  return (float)((v >> (8 * byte)) & 0xFFu);  // selected into v_cvt_f32_ubyteN
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte streaming load of weight bytes: read once, not worth keeping in cache.
-__device__ __forceinline__ uint4 stream_load16(const uint8_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ float4 add4(float4 a, float4 b) {
-  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-__device__ __forceinline__ float4 mul4(float c, float4 a) {
-  return make_float4(c * a.x, c * a.y, c * a.z, c * a.w);
 }
 
 // ---------------------------------------------------------------------------
@@ -220,56 +177,6 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 // slots of each chunk are rotated so that the 8 lanes served together by an
 // LDS read touch 8 different bank groups.
 // ---------------------------------------------------------------------------
-template <int QT>
-struct Fmt {
-  static constexpr int kWeightsPerChunk = QT == QBL_FMT_Q8 ? 16 : 32;
-  static constexpr int kSlots = kWeightsPerChunk / 4;
-  __device__ static __forceinline__ int slot(int c, int j) {
-    return (j + (QT == QBL_FMT_Q8 ? (c >> 1) : c)) & (kSlots - 1);
-  }
-};
-
-// Sum_j q_j x_j over one q8_0 chunk of 16 weights.  The device stores q8_0
-// bytes offset-binary (u = q + 128), which convert with v_cvt_f32_ubyte; the
-// offset is removed with the chunk's x sum: sum (u-128) x = sum u x - 128 sum x.
-__device__ __forceinline__ float dot_q8(const uint4 q, const float4* xv, float xsum) {
-  const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-  float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-  for (int w = 0; w < 4; w += 2) {
-    s0 = fmaf(ub(u[w], 0), xv[w].x, s0);
-    s0 = fmaf(ub(u[w], 1), xv[w].y, s0);
-    s0 = fmaf(ub(u[w], 2), xv[w].z, s0);
-    s0 = fmaf(ub(u[w], 3), xv[w].w, s0);
-    s1 = fmaf(ub(u[w + 1], 0), xv[w + 1].x, s1);
-    s1 = fmaf(ub(u[w + 1], 1), xv[w + 1].y, s1);
-    s1 = fmaf(ub(u[w + 1], 2), xv[w + 1].z, s1);
-    s1 = fmaf(ub(u[w + 1], 3), xv[w + 1].w, s1);
-  }
-  return fmaf(-128.0f, xsum, s0 + s1);
-}
-
-// Sum_j q_j x_j over one q4_sm block: byte i holds q_{2i} (low nibble) and
-// q_{2i+1} (high nibble), so 32-bit word w covers weights 8w .. 8w+7.
-__device__ __forceinline__ float dot_q4(const uint4 q, const float4* xv) {
-  const uint32_t v[4] = {q.x, q.y, q.z, q.w};
-  float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = v[w] & 0x0F0F0F0Fu, hi = (v[w] >> 4) & 0x0F0F0F0Fu;
-    const float4 xa = xv[2 * w], xb = xv[2 * w + 1];
-    s0 = fmaf(ub(lo, 0), xa.x, s0);
-    s1 = fmaf(ub(hi, 0), xa.y, s1);
-    s0 = fmaf(ub(lo, 1), xa.z, s0);
-    s1 = fmaf(ub(hi, 1), xa.w, s1);
-    s0 = fmaf(ub(lo, 2), xb.x, s0);
-    s1 = fmaf(ub(hi, 2), xb.y, s1);
-    s0 = fmaf(ub(lo, 3), xb.z, s0);
-    s1 = fmaf(ub(hi, 3), xb.w, s1);
-  }
-  return s0 + s1;
-}
-
 constexpr int kPrefetchAdapters = 2;  // B rows prefetched for lists of <= 2 adapters of rank <= 64
 
 template <int QT, int BB, int CPL, int RPW>
@@ -478,15 +385,6 @@ hipError_t allow_dyn_lds(const void* fn, size_t bytes) {
 // maintenance and nothing is reset afterwards.  A violated assumption shows as
 // wrong values, never as a hang.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float tagged_get(const uint64_t* p, uint32_t tag, int spin_limit) {
-  uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int spins = 0; (uint32_t)(w >> 32) != tag && spins < spin_limit; ++spins) {
-    __builtin_amdgcn_s_sleep(1);
-    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return __uint_as_float((uint32_t)w);
-}
-
 constexpr int kB1MaxSlots = 64;   // output rows (over all segments) per workgroup
 constexpr int kB1MaxT = kMaxSegs * 512;
 
@@ -496,49 +394,6 @@ struct B1Shape {
   static constexpr int kG = CPW >= 3 ? 1 : 2;                                   // rows per load group
   static constexpr int kRS = CPW * kNS >= 16 ? 1 : 16 / (CPW * kNS);           // A rows per shrink workgroup
 };
-
-// One DPP exchange-and-add step of the transposed row reduction: lanes whose
-// bit (the partner distance) is clear keep the first half of the values, the
-// others the second half; each adds its partner's copy of the half it keeps.
-template <int CTRL, int N>
-__device__ __forceinline__ void fold_half(float (&p)[8], bool upper) {
-#pragma unroll
-  for (int k = 0; k < N / 2; ++k) {
-    const float send = upper ? p[k] : p[k + N / 2];
-    const float keep = upper ? p[k + N / 2] : p[k];
-    p[k] = keep + dpp_mov<CTRL>(send);
-  }
-}
-
-// Reduces G per-lane partials (one per row) over each 16-lane row of the wave.
-// Afterwards lane i of a 16-lane row holds the partial of row (i >> (4 - log2 G))
-// in p[0]: lanes 0, 16/G, 2*16/G, ... hold rows 0, 1, 2, ...
-template <int G>
-__device__ __forceinline__ void reduce_rows16(float (&p)[8], int lane) {
-  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G");
-  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
-  if constexpr (G == 8) {
-    fold_half<0x140, 8>(p, b3);  // row_mirror: partner 15 - i
-    fold_half<0x141, 4>(p, b2);  // row_half_mirror: partner 7 - i
-    fold_half<0x4E, 2>(p, b1);   // quad_perm [2,3,0,1]: partner i ^ 2
-    p[0] += dpp_mov<0xB1>(p[0]);  // quad_perm [1,0,3,2]
-  } else if constexpr (G == 4) {
-    fold_half<0x140, 4>(p, b3);
-    fold_half<0x141, 2>(p, b2);
-    p[0] += dpp_mov<0x4E>(p[0]);
-    p[0] += dpp_mov<0xB1>(p[0]);
-  } else if constexpr (G == 2) {
-    fold_half<0x140, 2>(p, b3);
-    p[0] += dpp_mov<0x141>(p[0]);
-    p[0] += dpp_mov<0x4E>(p[0]);
-    p[0] += dpp_mov<0xB1>(p[0]);
-  } else {
-    p[0] += dpp_mov<0x140>(p[0]);
-    p[0] += dpp_mov<0x141>(p[0]);
-    p[0] += dpp_mov<0x4E>(p[0]);
-    p[0] += dpp_mov<0xB1>(p[0]);
-  }
-}
 
 // waves per SIMD the register budget targets: 4 waves, one q8_0 block of chunks
 // per lane and two-row groups fit in 96 VGPRs, which lets 5 waves share a SIMD

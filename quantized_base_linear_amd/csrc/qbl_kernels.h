@@ -143,6 +143,7 @@ hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc);
 constexpr int kTCopies = 8;
 inline int64_t t_copy_stride(int64_t rows) { return (rows + 31) / 32 * 32 + 32; }
 hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc);
+
 int64_t jit_workspace_bytes(int n, int k, int total_rank);
 
 }  // namespace qbl

@@ -130,6 +130,7 @@ struct ListImpl {
   std::mutex ev_mu;
   std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
 
+
   void mark_use(hipStream_t st) {
     std::lock_guard<std::mutex> g(ev_mu);
     for (auto& u : uses)
@@ -683,8 +684,9 @@ int blocks_tmax(const ListImpl* L, int first_block, int n_blocks) {
 // quantisation type present.
 constexpr int kSpinLimit = 1 << 22;  // ~0.1 s of s_sleep(1) before a wait gives up
 
-// Launch numbers that tag the shrink results of fused launches: unique per
-// launch (mod 2^32), never 0, so a zeroed workspace holds no valid result.
+// Numbers that tag the shrink results one workgroup hands to others within a
+// launch: unique per launch (mod 2^32), never 0, so a zeroed workspace holds
+// no valid value.
 uint32_t next_tag() {
   static std::atomic<uint32_t> counter{0};
   uint32_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
