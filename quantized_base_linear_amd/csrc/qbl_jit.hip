@@ -85,17 +85,37 @@ __global__ void stage_lora_kernel(JitArgs a, int tp) {
 // ---------------------------------------------------------------------------
 // The fused JIT GEMM.  RS = rank steps of 16 (0: no adapters; 1..JRMAX: held
 // in registers; JRMAX+1: more, streamed 64 ranks at a time).
+//
+// The X and W_eff tiles are double-buffered in LDS: during K-step k every wave
+// issues its MFMAs on buffer k & 1 and, in the same stretch of code, builds its
+// block of W_eff(k+1) and stages X(k+1) into the other buffer, so the matrix
+// cores and the dequantisation arithmetic overlap; one barrier per K-step.
+// bf16 rounding (round to nearest even) uses the hardware conversion.
 // ---------------------------------------------------------------------------
+constexpr int kXsElems = JBM * JLD;
+constexpr int kWsElems = JBN * JLD;
+constexpr int kALD = 16 * JRMAX + 8;         // LDS pitch of a staged At row (bf16)
+constexpr int kAsElems = JBK * kALD;         // one K-step of At (rank <= 64)
+constexpr size_t kJitLds = 2 * (size_t)(kXsElems + kWsElems + kAsElems) * sizeof(uint16_t);
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
 template <int QT, int RS>
 __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[JBM * JLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[JBN * JLD];
+  extern __shared__ __attribute__((aligned(16))) uint16_t jit_lds[];
+  uint16_t* Xs0 = jit_lds;
+  uint16_t* Ws0 = jit_lds + 2 * kXsElems;
+  uint16_t* As0 = Ws0 + 2 * kWsElems;  // At rows of a K-step, staged once per workgroup
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int col = lane & 31, h = lane >> 5;
   const int N = a.n, K = a.k, M = a.m;
   const int n0 = blockIdx.x * JBN, m0 = blockIdx.y * JBM;
   const int nblk = K / 32;
+  const int nk = (K + JBK - 1) / JBK;
 
   // W-tile construction role: 32 k x 32 n block (kb, nb) of the 64 x 128 tile
   const int kb = w & 1, nb = w >> 1;
@@ -114,38 +134,113 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
     for (int r = 0; r < RS; ++r) sbf[r] = ld_bf16x8(sB + (int64_t)nrow * tp + 16 * r + 8 * h);
   }
 
-  // prefetched operands of the next K-step
-  uint4 xr[4];
-  uint32_t qd[4];
-  uint32_t scv = 0;
-  bf16x8 atf[RREG > 0 ? RREG : 1];
+  // Operands of a K-step in registers: two sets, so the loads of step k + 3 are
+  // issued while step k + 1 is built and step k + 2's are in flight (X and the
+  // quantised weights); At is loaded one step before it is staged in LDS.
+  struct Ops {
+    uint4 xr[4];
+    uint4 qv;  // 16 consecutive weights of this lane's row: 16 bytes (q8_0) or 8 (q4_sm)
+    uint32_t scv;
+  };
+  Ops opa, opb;
+  uint4 atr = make_uint4(0u, 0u, 0u, 0u);
+  // At of a K-step: 64 rows of tp bf16, one 16-byte piece per thread
+  const int arow = tid / (tp > 0 ? tp / 8 : 1), apiece = tid % (tp > 0 ? tp / 8 : 1);
+  const bool aload = RS > 0 && RS <= JRMAX && tid < 8 * tp;
+  auto load_at = [&](int k0) {
+    if (aload) {
+      const int k = min(k0 + arow, K - 1);
+      atr = *reinterpret_cast<const uint4*>(At + (int64_t)k * tp + 8 * apiece);
+    }
+  };
+  // At row k_local = 16 h' + v of a 32-row half goes to LDS row 8 (v / 4) + 4 h' + v % 4:
+  // the LoRA MFMA's output row r then holds k_local = perm(r), and lane (col, h)
+  // holds k_local = 16 h + v in dsum[v], 16 contiguous k, the same k its single
+  // 16-byte load of quantised weights covers.
+  auto store_at = [&](int b) {
+    const int half = arow >> 5, kl = arow & 31, hh = kl >> 4, v = kl & 15;
+    const int lrow = 32 * half + 8 * (v >> 2) + 4 * hh + (v & 3);
+    if (aload) *reinterpret_cast<uint4*>(As0 + b * kAsElems + lrow * kALD + 8 * apiece) = atr;
+  };
 
-  auto prefetch = [&](int k0) {
+  // Loads are unconditional (clamped in-bounds addresses; what lies outside the
+  // matrix is zeroed or skipped where it is used), so the loop has no branches
+  // around them.
+  auto prefetch = [&](Ops& o, int k0) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int idx = tid + JTHREADS * c;
       const int row = idx >> 3, c16 = idx & 7;
-      const int m = m0 + row, kk = k0 + 8 * c16;
-      xr[c] = (m < M && kk < K) ? *reinterpret_cast<const uint4*>(a.X + (int64_t)m * K + kk)
-                                : make_uint4(0u, 0u, 0u, 0u);
+      const int m = min(m0 + row, M - 1), kk = min(k0 + 8 * c16, K - 8);
+      o.xr[c] = *reinterpret_cast<const uint4*>(a.X + (int64_t)m * K + kk);
     }
-    const int kbase = k0 + 32 * kb;
-    if (kbase < K) {
-      if (QT == QBL_FMT_Q8) {
+    const int kbase = min(k0 + 32 * kb, K - 32);
+    if (QT == QBL_FMT_Q8) {
+      o.qv = *reinterpret_cast<const uint4*>(a.qs + (int64_t)nrow * K + kbase + 16 * h);
+      o.scv = reinterpret_cast<const uint16_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+    } else {
+      const uint2 q2 = *reinterpret_cast<const uint2*>(a.qs + (int64_t)nrow * (K / 2) + (kbase + 16 * h) / 2);
+      o.qv = make_uint4(q2.x, q2.y, 0u, 0u);
+      o.scv = reinterpret_cast<const uint32_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+    }
+  };
+
+  // this wave's 32 x 32 block of W_eff for K-step at k0, and the X tile, into buffer b
+  auto build = [&](const Ops& o, int k0, int b) {
+    const uint4* xr = o.xr;
+    const uint32_t qw[4] = {o.qv.x, o.qv.y, o.qv.z, o.qv.w};
+    const uint32_t scv = o.scv;
+    uint16_t* wrow = Ws0 + b * kWsElems + (32 * nb + col) * JLD + 32 * kb + 16 * h;
+    f32x16 dsum;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          qd[g] = *reinterpret_cast<const uint32_t*>(a.qs + (int64_t)nrow * K + kbase + 8 * g + 4 * h);
-        scv = reinterpret_cast<const uint16_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
-      } else {
+    for (int v = 0; v < 16; ++v) dsum[v] = 0.0f;
+    if constexpr (RS > 0 && RS <= JRMAX) {
+      const uint16_t* arow_p = As0 + b * kAsElems + (32 * kb + col) * kALD + 8 * h;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          qd[g] = *reinterpret_cast<const uint16_t*>(a.qs + (int64_t)nrow * (K / 2) + (kbase + 8 * g + 4 * h) / 2);
-        scv = reinterpret_cast<const uint32_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+      for (int r = 0; r < RS; ++r)
+        dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(arow_p + 16 * r), sbf[r], dsum, 0, 0, 0);
+    } else if constexpr (RS > JRMAX) {
+      const int kbase = min(k0 + 32 * kb, K - 32);
+      const int prow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);  // the same row permutation
+      for (int r = 0; r < tp / 16; ++r) {
+        const bf16x8 af = ld_bf16x8(At + (int64_t)(kbase + prow) * tp + 16 * r + 8 * h);
+        const bf16x8 bf = ld_bf16x8(sB + (int64_t)nrow * tp + 16 * r + 8 * h);
+        dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, dsum, 0, 0, 0);
       }
-      if constexpr (RS > 0 && RS <= JRMAX) {
+    }
+    // a K block past the matrix contributes zeros (d = m = 0 and no adapter term)
+    const bool kin = k0 + 32 * kb < K;
+    const float d = kin ? h2f(scv) : 0.0f;
+    const float mn = QT == QBL_FMT_Q8 ? -128.0f * d : (kin ? h2f(scv >> 16) : 0.0f);
+    // lane (col, h): weights k = 16 h + v, v = 0..15, of row col
+    uint32_t packed[8];
 #pragma unroll
-        for (int r = 0; r < RS; ++r) atf[r] = ld_bf16x8(At + (int64_t)(kbase + col) * tp + 16 * r + 8 * h);
+    for (int v = 0; v < 16; v += 2) {
+      float wv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // q8_0: d (u - 128) = fma(d, u, -128 d), u the offset-binary byte; q4_sm: fma(d, q, m).
+        // Both are exact in float32 (a product of at most 19 significant bits, then
+        // one rounding for q4_sm), as in the recipe.
+        const int e = v + j;
+        float deq;
+        if (QT == QBL_FMT_Q8)
+          deq = d * (float)((qw[e >> 2] >> (8 * (e & 3))) & 0xFFu) + mn;
+        else
+          deq = fmaf(d, (float)((qw[e >> 3] >> (4 * (e & 7))) & 0xFu), mn);
+        wv[j] = RS > 0 && kin ? deq + dsum[e] : deq;
       }
+      packed[v >> 1] = pack_bf16(wv[0], wv[1]);
+    }
+    *reinterpret_cast<uint4*>(wrow) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *reinterpret_cast<uint4*>(wrow + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    uint16_t* xs = Xs0 + b * kXsElems;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = tid + JTHREADS * c;
+      const int row = idx >> 3, c16 = idx & 7;
+      const bool xin = m0 + row < M && k0 + 8 * c16 < K;
+      *reinterpret_cast<uint4*>(xs + row * JLD + 8 * c16) = xin ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
     }
   };
 
@@ -157,71 +252,49 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  prefetch(0);
-  for (int k0 = 0; k0 < K; k0 += JBK) {
-    // ---- build this wave's 32 x 32 block of W_eff in LDS
-    const int kbase = k0 + 32 * kb;
-    uint16_t* wrow = Ws + (32 * nb + col) * JLD + 32 * kb + 4 * h;
-    if (kbase < K) {
-      f32x16 dsum;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) dsum[v] = 0.0f;
-      if constexpr (RS > 0 && RS <= JRMAX) {
-#pragma unroll
-        for (int r = 0; r < RS; ++r) dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(atf[r], sbf[r], dsum, 0, 0, 0);
-      } else if constexpr (RS > JRMAX) {
-        for (int r = 0; r < tp / 16; ++r) {
-          const bf16x8 af = ld_bf16x8(At + (int64_t)(kbase + col) * tp + 16 * r + 8 * h);
-          const bf16x8 bf = ld_bf16x8(sB + (int64_t)nrow * tp + 16 * r + 8 * h);
-          dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, dsum, 0, 0, 0);
-        }
-      }
-      const float d = h2f(scv);
-      const float mn = QT == QBL_FMT_Q8 ? 0.0f : h2f(scv >> 16);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float wv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float deq;
-          if (QT == QBL_FMT_Q8)
-            deq = d * (float)((int)((qd[g] >> (8 * j)) & 0xFFu) - 128);  // offset-binary byte; exact in float32
-          else
-            deq = fmaf(d, (float)((qd[g] >> (4 * j)) & 0xFu), mn);           // float32(d q + m)
-          wv[j] = RS > 0 ? deq + dsum[4 * g + j] : deq;
-        }
-        const uint32_t lo = (uint32_t)bf16_rne(wv[0]) | ((uint32_t)bf16_rne(wv[1]) << 16);
-        const uint32_t hi = (uint32_t)bf16_rne(wv[2]) | ((uint32_t)bf16_rne(wv[3]) << 16);
-        *reinterpret_cast<uint2*>(wrow + 8 * g) = make_uint2(lo, hi);
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) *reinterpret_cast<uint2*>(wrow + 8 * g) = make_uint2(0u, 0u);
-    }
-    // ---- stage the X tile
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + JTHREADS * c;
-      const int row = idx >> 3, c16 = idx & 7;
-      *reinterpret_cast<uint4*>(Xs + row * JLD + 8 * c16) = xr[c];
-    }
-    __syncthreads();
-    if (k0 + JBK < K) prefetch(k0 + JBK);  // overlaps the MFMA phase below
+  // At of steps 0 and 1 into LDS first; then step 0's tiles
+  load_at(0);
+  store_at(0);
+  load_at(JBK);
+  store_at(1);
+  __syncthreads();
+  prefetch(opa, 0);
+  build(opa, 0, 0);
+  prefetch(opa, JBK);
+  prefetch(opb, 2 * JBK);
+  load_at(2 * JBK);
+  __syncthreads();
 
-    // ---- main MFMA: 64 x 64 per wave, 4 k-steps of 16
+  // One K-step: MFMAs on buffer cur; build step ks + 1 from `next`, then reload
+  // `next` with step ks + 3 (`after` holds step ks + 2 meanwhile).
+  auto step = [&](int ks, Ops& next) {
+    const int cur = ks & 1;
+    const uint16_t* xs = Xs0 + cur * kXsElems;
+    const uint16_t* ws = Ws0 + cur * kWsElems;
 #pragma unroll
-    for (int ks = 0; ks < JBK / 16; ++ks) {
+    for (int kk = 0; kk < JBK / 16; ++kk) {
       bf16x8 af[2], bf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = ld_bf16x8(Xs + (64 * wm + 32 * i + col) * JLD + 16 * ks + 8 * h);
+      for (int i = 0; i < 2; ++i) af[i] = ld_bf16x8(xs + (64 * wm + 32 * i + col) * JLD + 16 * kk + 8 * h);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = ld_bf16x8(Ws + (64 * wn + 32 * j + col) * JLD + 16 * ks + 8 * h);
+      for (int j = 0; j < 2; ++j) bf[j] = ld_bf16x8(ws + (64 * wn + 32 * j + col) * JLD + 16 * kk + 8 * h);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
+    // next K-step's tiles into the other buffer (unconditional, so the body is
+    // one block the scheduler can interleave with the MFMAs; past the end they
+    // build tiles nobody reads)
+    build(next, (ks + 1) * JBK, cur ^ 1);  // reads At(ks + 1) in As[cur ^ 1]
+    store_at(cur);                         // At(ks + 2): As[cur] was last read by build(ks)
+    prefetch(next, (ks + 3) * JBK);
+    load_at((ks + 3) * JBK);
     __syncthreads();
+  };
+  for (int ks = 0; ks < nk; ks += 2) {
+    step(ks, opa);
+    if (ks + 1 < nk) step(ks + 1, opb);
   }
 
   // ---- write Y (float32)
@@ -241,19 +314,28 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
 
 int rank_pad(int t) { return t <= 0 ? 0 : t <= 16 * JRMAX ? (t + 15) / 16 * 16 : (t + 63) / 64 * 64; }
 
+template <int QT, int RS>
+hipError_t launch_rs(const JitArgs& a, int tp, const LaunchCtx& lc) {
+  // (the two M-blocks of an N tile are 112 = 0 mod 8 workgroups apart for the
+  // prefill shape, so they share an XCD and its L2 copy of the weight rows)
+  const dim3 grid((a.n + JBN - 1) / JBN, (a.m + JBM - 1) / JBM);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&jit_kernel<QT, RS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kJitLds);
+  if (e != hipSuccess) return e;
+  QBL_LAUNCH((jit_kernel<QT, RS>), grid, dim3(JTHREADS), kJitLds, lc, a, tp);
+  return hipGetLastError();
+}
+
 template <int QT>
 hipError_t launch_q(const JitArgs& a, int tp, const LaunchCtx& lc) {
-  const dim3 grid((a.n + JBN - 1) / JBN, (a.m + JBM - 1) / JBM);
-  const int rs = tp / 16;
-  switch (rs) {
-    case 0: QBL_LAUNCH((jit_kernel<QT, 0>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
-    case 1: QBL_LAUNCH((jit_kernel<QT, 1>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
-    case 2: QBL_LAUNCH((jit_kernel<QT, 2>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
-    case 3: QBL_LAUNCH((jit_kernel<QT, 3>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
-    case 4: QBL_LAUNCH((jit_kernel<QT, 4>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
-    default: QBL_LAUNCH((jit_kernel<QT, JRMAX + 1>), grid, dim3(JTHREADS), 0, lc, a, tp); break;
+  switch (tp / 16) {
+    case 0: return launch_rs<QT, 0>(a, tp, lc);
+    case 1: return launch_rs<QT, 1>(a, tp, lc);
+    case 2: return launch_rs<QT, 2>(a, tp, lc);
+    case 3: return launch_rs<QT, 3>(a, tp, lc);
+    case 4: return launch_rs<QT, 4>(a, tp, lc);
+    default: return launch_rs<QT, JRMAX + 1>(a, tp, lc);
   }
-  return hipGetLastError();
 }
 
 }  // namespace
