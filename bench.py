@@ -16,6 +16,8 @@ Also reported on the same JSON line:
   stack         32 such blocks, two adapters (r16@1.0 then r64@0.5), 256 tokens
   q4_mlp        70B-style q4_sm MLP linears at batch 1 and 8
   prefill       the JIT-materialisation prefill GEMM (when available)
+  stack.lifecycle  load (staging + verification + digest), attach, rollback and
+                base-hash costs on the stack
 """
 from __future__ import annotations
 
@@ -62,21 +64,31 @@ def group_bytes(wl, lins):
     return b
 
 
-def build_copies(q, wl, copies, adapter_idx):
+def build_copies(q, wl, copies, adapter_idx, timing=None):
     """One base holding `copies` copies of the workload's linears, one adapter
-    per workload adapter covering every copy; returns (base, adapters, comp, blocks)."""
+    per workload adapter covering every copy; returns (base, adapters, comp, blocks).
+    With a `timing` dict, records the wall time and bytes of the base load and
+    of the adapter loads (each: staging, upload, read-back verification, digest)."""
     blocks = [q.qbl_quantize(L.qtype, wl.weight(i)) for i, L in enumerate(wl.linears)]
     descs = []
     for c in range(copies):
         for i, L in enumerate(wl.linears):
             descs.append((L.qtype, L.n_out, L.k_in, blocks[i]))
+    t0 = time.time()
     base = q.qbl_base_load(descs)
+    if timing is not None:
+        timing["base_load_s"] = time.time() - t0
+        timing["base_bytes"] = sum(int(d[3].nbytes) for d in descs)
     n = len(wl.linears)
     ads = []
     for a in adapter_idx:
         fac = [(wl.lora_a(i, a), wl.lora_b(i, a)) for i in range(n)]
-        ads.append(q.qbl_adapter_load(base, [(c * n + i, A, B) for c in range(copies)
-                                             for i, (A, B) in enumerate(fac)]))
+        entries = [(c * n + i, A, B) for c in range(copies) for i, (A, B) in enumerate(fac)]
+        t0 = time.time()
+        ads.append(q.qbl_adapter_load(base, entries))
+        if timing is not None:
+            timing["adapter_load_s"] = timing.get("adapter_load_s", 0.0) + time.time() - t0
+            timing["adapter_bytes"] = timing.get("adapter_bytes", 0) + sum(A.nbytes + B.nbytes for _, A, B in entries)
     comp = q.qbl_comp_create(base)
     q.qbl_comp_attach(comp, ads, [wl.adapters[a].scale for a in adapter_idx])
     return base, ads, comp, blocks
@@ -196,7 +208,8 @@ def bench_stack(torch, q, workloads, args):
     wl = workloads.stack(tokens=args.stack_tokens)
     log("[stack] building 32 blocks (6.9 GB q8_0) + r16/r64 adapters")
     t0 = time.time()
-    base, ads, comp, _ = build_copies(q, wl, 1, [0, 1])
+    timing = {}
+    base, ads, comp, _ = build_copies(q, wl, 1, [0, 1], timing)
     log(f"[stack] built in {time.time() - t0:.1f}s")
     d = 4096
     x0 = torch.from_numpy(wl.x0()[0]).cuda()
@@ -218,14 +231,48 @@ def bench_stack(torch, q, workloads, args):
     q.qbl_decode(comp, 0, 32, x0, y, wl.tokens, ws)
     torch.cuda.synchronize()
     changed = not torch.equal(y, y_ab)
+    t0 = time.time()
     same_hash = q.qbl_base_hash(base) == h0
+    hash_s = time.time() - t0
+    life = bench_lifecycle(q, base, ads, comp, timing, hash_s)
     free_all(q, base, ads, comp)
     log(f"[stack] {tok_s:.0f} tok/s, order swap changes output: {changed}, hash unchanged: {same_hash}")
     return {"tokens_per_s": round(tok_s, 1), "tokens": wl.tokens, "ms_per_token": round(ms / wl.tokens, 4),
             "GB_per_s": round(per_tok / (ms / wl.tokens * 1e-3) / 1e9, 1),
             "frac_hbm": round(per_tok / (ms / wl.tokens * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_token": per_tok, "order_swap_changes_output": changed,
-            "base_hash_unchanged": same_hash}
+            "base_hash_unchanged": same_hash, "lifecycle": life}
+
+
+def bench_lifecycle(q, base, ads, comp, timing, hash_s):
+    """Host-side cost of the lifecycle on the 32-block stack (224 linears, two
+    adapters): loads with staging, read-back verification and digests; list
+    changes (validation + new list + atomic exchange); rollback; the base hash
+    re-read from the device."""
+    n = 400
+    lists = ([ads[0], ads[1]], [1.0, 0.5]), ([ads[1], ads[0]], [0.5, 1.0])
+    t0 = time.perf_counter()
+    for i in range(n):
+        q.qbl_comp_attach(comp, *lists[i % 2])
+    attach_us = (time.perf_counter() - t0) / n * 1e6
+    t0 = time.perf_counter()
+    for _ in range(n):
+        q.qbl_comp_rollback(comp)
+    rollback_us = (time.perf_counter() - t0) / n * 1e6
+    t0 = time.perf_counter()
+    for _ in range(n):
+        q.qbl_comp_digest(comp)
+    digest_us = (time.perf_counter() - t0) / n * 1e6
+    q.qbl_comp_attach(comp, *lists[0])
+    out = {"base_load_GB_per_s": round(timing["base_bytes"] / timing["base_load_s"] / 1e9, 2),
+           "base_bytes": timing["base_bytes"],
+           "adapter_load_GB_per_s": round(timing["adapter_bytes"] / timing["adapter_load_s"] / 1e9, 2),
+           "adapter_bytes": timing["adapter_bytes"],
+           "attach_us": round(attach_us, 1), "rollback_us": round(rollback_us, 1),
+           "comp_digest_us": round(digest_us, 2),
+           "base_hash_GB_per_s": round(timing["base_bytes"] / hash_s / 1e9, 2)}
+    log(f"[lifecycle] {out}")
+    return out
 
 
 def bench_q4(torch, q, workloads, args):

@@ -10,13 +10,16 @@
  *
  * The operations follow three pages on quantized-base adapter overlays:
  *  [overlay]  mikekappel.com, "We propose a content-addressed overlay system"
- *             (sections "Runtime Strategy Comparison Matrix", "Native/WASM Kernel
- *             Implications", "Proposed Activation/Deactivation State Machine",
- *             "Clean Replacement Plan and Rejection Criteria");
+ *             (sections "Composition Identity and Manifest Schema", "Explicit
+ *             Correctness and Atomicity Invariants", "Proposed Activation/
+ *             Deactivation State Machine", "TDD and Fault-Injection Matrix",
+ *             "Runtime Strategy Comparison Matrix", "Native/WASM Kernel
+ *             Implications", "Clean Replacement Plan and Rejection Criteria");
  *  [design]   mikekappel.com, "Deep Technical Design: Exact, Atomic, Reversible
  *             Specialist Overlays" (sections 1, 2, 5, 6, 8, 9, 11);
  *  [lora]     contenox.com, "LoRA adapters" blueprint ("Backend Support
- *             Position", llama.cpp adapter API and its shape rules).
+ *             Position", llama.cpp adapter API and its shape rules, "Runtime
+ *             Identity and Cache Safety").
  *
  * Conventions for every call:
  *  - Every function returns a qbl_status (0 = QBL_OK, negative = error) unless
@@ -42,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QBL_ABI_VERSION 1
+#define QBL_ABI_VERSION 2
 
 typedef int32_t qbl_status;
 #define QBL_OK 0
@@ -51,12 +54,15 @@ typedef int32_t qbl_status;
 #define QBL_E_FORMAT (-3)     /* unknown quantisation type, k not a multiple of 32, bad byte count */
 #define QBL_E_NONFINITE (-4)  /* NaN/Inf in weights, adapter factors or scales */
 #define QBL_E_NOMEM (-5)      /* device or host allocation failed */
-#define QBL_E_BUDGET (-6)     /* workspace too small */
+#define QBL_E_BUDGET (-6)     /* workspace too small, or a base's device-memory budget exceeded */
 #define QBL_E_BUSY (-7)       /* object still referenced */
 #define QBL_E_DEVICE (-8)     /* a HIP runtime call failed */
 #define QBL_E_FOREIGN (-9)    /* adapter bound to another base */
 #define QBL_E_DUPLICATE (-10) /* the same handle twice in one list, or one linear twice in one adapter */
 #define QBL_E_LIMIT (-11)     /* above a documented limit */
+#define QBL_E_CHECKSUM (-12)  /* a device copy read back differs from the bytes sent */
+#define QBL_E_INJECTED (-13)  /* a failure armed with qbl_fault_inject fired */
+#define QBL_E_STATE (-14)     /* the call does not apply to the object's state */
 
 /* Quantisation types.
  * QBL_Q8_0: blocks of 32 weights along k: one fp16 scale d and 32 int8 q,
@@ -123,15 +129,28 @@ typedef struct {
  * linears 7b..7b+6 in the order q, k, v, o, gate, up, down; qbl_block and
  * qbl_decode check those shapes when called.  The library copies the blocks
  * (the caller may free them on return), repacks them into its device layout,
- * and seals them: no kernel ever receives a writable pointer to base bytes
+ * uploads them, reads every device copy back and compares it byte for byte with
+ * what it sent (QBL_E_CHECKSUM on a difference: [design] section 6, checksum
+ * verification of a staged block), records the base digest (qbl_base_digest)
+ * and seals the bytes: no kernel ever receives a writable pointer to base bytes
  * ([design] section 2, the oracle invariant: base bytes stay bit-identical).
- * *out receives the handle. */
+ * On any failure every allocation made so far is freed.  *out receives the
+ * handle. */
 qbl_status qbl_base_load(const qbl_linear_desc* descs, int32_t n_linears, qbl_base** out);
 
-/* SHA-256 (FIPS 180-4) over the base's device bytes, re-read from the GPU on
- * every call: the digest of the concatenation, in linear order, of each
- * linear's SHA-256 over its device arrays.  Equal before and after any attach,
- * clear or run ([overlay] "Checksum Verification"; [design] section 2). */
+/* The base digest recorded at load, from the canonical blocks it was given:
+ * SHA-256 (FIPS 180-4) over the concatenation, in linear order, of each
+ * linear's SHA-256 over the 24-byte little-endian header
+ * [int32 qtype][int32 0][int64 n_out][int64 k_in] followed by its canonical
+ * blocks.  It names the exact quantised bytes and their format, the first
+ * fields of a composition's identity ([overlay] "Composition Identity and
+ * Manifest Schema": base hash and quantisation profile). */
+qbl_status qbl_base_digest(const qbl_base* base, uint8_t sha256_out[32]);
+
+/* The same digest computed now from the device bytes, re-read from the GPU and
+ * translated back to canonical blocks.  It equals qbl_base_digest as long as
+ * the device copy is intact, before and after any attach, clear or run
+ * ([overlay] "Checksum Verification"; [design] section 2). */
 qbl_status qbl_base_hash(qbl_base* base, uint8_t sha256_out[32]);
 
 /* Number of linears, and one linear's type and shape. */
@@ -142,6 +161,19 @@ qbl_status qbl_base_info(const qbl_base* base, int32_t linear, int32_t* qtype, i
 /* Free a base.  QBL_E_BUSY while any adapter or composition still refers to it
  * (adapters are owned by the base they were loaded against, as in [lora]). */
 qbl_status qbl_base_free(qbl_base* base);
+
+/* Device-memory budget of a base: a cap on the device bytes held on its behalf,
+ * its own arrays plus the arena of every adapter loaded against it that is
+ * still alive.  0 = no cap (the default).  An adapter load that would take the
+ * total above the cap fails with QBL_E_BUDGET before it allocates anything
+ * ([overlay] "Bounded Resources" and the state machine's validation: the
+ * composition must fit a fixed memory budget; [design] section 6 ALLOCATION: abort when the request exceeds what is
+ * available).  Setting a cap below the bytes already held fails with
+ * QBL_E_BUDGET and keeps the old cap. */
+qbl_status qbl_base_set_budget(qbl_base* base, int64_t budget_bytes);
+
+/* Bytes held now (base arrays + live adapter arenas) and the cap (0 = none). */
+qbl_status qbl_base_memory(const qbl_base* base, int64_t* held_bytes, int64_t* budget_bytes);
 
 /* ------------------------------------------------------------- adapters --- */
 
@@ -157,15 +189,21 @@ typedef struct {
   const float* B;
 } qbl_lora_desc;
 
-/* Validate and upload an adapter touching n >= 1 linears of base (no linear
- * twice).  Rejects non-finite values and unknown linears ([design] section 11
- * deep compatibility checks; [lora]: an adapter that matches zero layers is
- * rejected).  The adapter is bound to base.  *out receives the handle. */
+/* Validate, stage and verify an adapter touching n >= 1 linears of base (no
+ * linear twice), following [design] section 6: validation (shapes, ranks,
+ * finite values, known linears: [design] section 11 deep compatibility checks;
+ * [lora]: an adapter that matches zero layers is rejected), allocation of one
+ * device arena within the base's budget, staging of every A and B into it, and
+ * verification: each device copy is read back and compared byte for byte with
+ * what was sent (QBL_E_CHECKSUM on a difference).  Any failure frees the arena
+ * and leaves nothing behind.  The adapter is bound to base.  *out receives the
+ * handle. */
 qbl_status qbl_adapter_load(qbl_base* base, const qbl_lora_desc* descs, int32_t n,
                             qbl_adapter** out);
 
-/* SHA-256 of the adapter content: for each entry in order, the little-endian
- * int32 linear and rank, then A's and B's float32 bytes. */
+/* SHA-256 of the adapter content: over the concatenation, in entry order, of
+ * each entry's SHA-256 over [int32 linear][int32 rank] (little-endian) followed
+ * by A's and then B's float32 bytes. */
 qbl_status qbl_adapter_digest(const qbl_adapter* adapter, uint8_t sha256_out[32]);
 
 /* Drop the caller's reference.  Device memory lives on while an attached list
@@ -185,21 +223,74 @@ qbl_status qbl_comp_create(qbl_base* base, qbl_comp** out);
  * base (QBL_E_FOREIGN), no handle twice (QBL_E_DUPLICATE), scales finite, the
  * summed rank per linear within QBL_MAX_TOTAL_RANK.  Then a new immutable list
  * replaces the old one in a single atomic exchange ([overlay] "Atomic Update";
- * [design] section 6 COMMIT/SWAP).  Entries with scale 0 are dropped, so an
- * all-zero list runs exactly the base-only instructions.  Runs already
- * enqueued keep the list they captured.  Attaching the list already in place
- * changes nothing ([overlay] "Idempotency"). */
+ * [design] section 6 COMMIT/SWAP), and the replaced list is kept as the
+ * composition's previous list (qbl_comp_rollback).  Entries with scale 0 are
+ * dropped, so an all-zero list runs exactly the base-only instructions.  Runs
+ * already enqueued keep the list they captured.  Attaching the list already in
+ * place changes nothing, not even the previous list ([overlay] "Idempotency"). */
 qbl_status qbl_comp_attach(qbl_comp* comp, const qbl_adapter* const* list, const float* scales,
                            int32_t n);
 
 /* Empty the list (deactivation: drop the adapter references, the base is
- * untouched; [design] section 6 "Exact Deactivation Flow"). */
+ * untouched; [design] section 6 "Exact Deactivation Flow").  Like an attach,
+ * it keeps the replaced list as the previous list; clearing an empty list
+ * changes nothing. */
 qbl_status qbl_comp_clear(qbl_comp* comp);
+
+/* Exchange the current and the previous list in one atomic step: the list that
+ * the last successful attach, clear or rollback replaced becomes current again
+ * ([overlay] state machine: the old state may be kept, and rollback restores
+ * it).  A second rollback returns to the list the first one left.  QBL_E_STATE
+ * when there is no previous list. */
+qbl_status qbl_comp_rollback(qbl_comp* comp);
+
+/* Release the previous list, and with it any adapter memory that only it still
+ * holds.  Rollback is then unavailable until the next change. */
+qbl_status qbl_comp_drop_previous(qbl_comp* comp);
 
 /* Number of effective (non-zero-scale) entries in the current list. */
 qbl_status qbl_comp_count(const qbl_comp* comp, int32_t* n);
 
+/* Identity of the current composition: qbl_identity_digest of the base digest
+ * and the current list.  Equal compositions (same base bytes, same effective
+ * adapters, order and scales) have equal digests; a change of any of them
+ * changes it. */
+qbl_status qbl_comp_digest(const qbl_comp* comp, uint8_t sha256_out[32]);
+
+/* The composition identity digest, defined on its own so that a caller can
+ * compute it for a manifest before attaching ([overlay] "Composition Identity
+ * and Manifest Schema": base hash, ordered adapter hashes, mixing weights and
+ * the runtime version; [lora] "Runtime Identity and Cache Safety": adapter
+ * order, digests and scales).  SHA-256 over, little-endian:
+ *   [int32 QBL_ABI_VERSION][base_digest: 32 B][int32 m]
+ *   then for each of the m entries i with scales[i] != 0, in list order:
+ *   [adapter_digests[32*i .. 32*i+32)][float32 scales[i]]
+ * Zero-scale entries (either sign of zero) are skipped, as attach drops them.
+ * adapter_digests holds n digests of 32 B (host).  QBL_E_NONFINITE for a NaN or
+ * infinite scale; 0 <= n <= QBL_MAX_ADAPTERS. */
+qbl_status qbl_identity_digest(const uint8_t base_digest[32], const uint8_t* adapter_digests,
+                               const float* scales, int32_t n, uint8_t sha256_out[32]);
+
 qbl_status qbl_comp_free(qbl_comp* comp);
+
+/* ------------------------------------------------------ fault injection --- */
+
+/* For tests only: production code never calls this ([overlay] "TDD and
+ * Fault-Injection Matrix": force a failure in each phase of an activation and
+ * check that the previous state is intact).  Arms `point` to fire once, on its
+ * `after`-th hit from now (1 = the next hit); after = 0 disarms it.  Points are
+ * process-wide and thread-safe.
+ *   QBL_FAULT_DEVICE_ALLOC: a device allocation by qbl_base_load (one per
+ *     linear) or qbl_adapter_load (one per adapter) fails: QBL_E_NOMEM.
+ *   QBL_FAULT_CORRUPT: after one upload (a base linear, or one adapter entry's
+ *     A and B) the library changes one byte of the device copy before reading
+ *     it back: QBL_E_CHECKSUM.
+ *   QBL_FAULT_SWAP: an attach, clear or rollback fails after its new list is
+ *     built and just before the exchange: QBL_E_INJECTED. */
+#define QBL_FAULT_DEVICE_ALLOC 1
+#define QBL_FAULT_CORRUPT 2
+#define QBL_FAULT_SWAP 3
+qbl_status qbl_fault_inject(int32_t point, int32_t after);
 
 /* ------------------------------------------------------------------ runs --- */
 

@@ -182,6 +182,24 @@ void repack_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, uint8_t
   });
 }
 
+void unpack_rows(int qtype, const uint8_t* qs, const uint8_t* sc, int64_t n, int64_t k,
+                 uint8_t* blocks) {
+  const int64_t bb = qbl_block_bytes(qtype);
+  const int64_t nb = k / 32;
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      uint8_t* p = blocks + (r * nb + b) * bb;
+      if (qtype == QBL_Q8_0) {
+        std::memcpy(p, sc + (r * nb + b) * 2, 2);
+        const uint8_t* src = qs + r * k + 32 * b;
+        for (int j = 0; j < 32; ++j) p[2 + j] = (uint8_t)(src[j] ^ 0x80u);
+      } else {
+        std::memcpy(p, sc + (r * nb + b) * 4, 4);
+        std::memcpy(p + 4, qs + r * (k / 2) + 16 * b, 16);
+      }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // SHA-256, FIPS 180-4 section 6.2.
 // ---------------------------------------------------------------------------

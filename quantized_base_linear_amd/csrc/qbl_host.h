@@ -35,6 +35,9 @@ int dequantize_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, floa
 //   q4_sm: qs packed nibbles [n][k/2] and dm uint32 (d | m << 16) [n][k/32]
 void repack_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, uint8_t* qs, uint8_t* sc,
                  int nthreads);
+// The inverse of repack_rows: device-layout arrays back to canonical blocks.
+void unpack_rows(int qtype, const uint8_t* qs, const uint8_t* sc, int64_t n, int64_t k,
+                 uint8_t* blocks);
 int64_t qs_bytes(int qtype, int64_t n, int64_t k);
 int64_t sc_bytes(int qtype, int64_t n, int64_t k);
 

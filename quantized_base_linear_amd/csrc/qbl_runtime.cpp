@@ -73,12 +73,17 @@ struct DevLinear {
   uint8_t* sc;
   int64_t qs_bytes, sc_bytes;
   void* mem;
+  int64_t mem_bytes;
 };
 
 struct qbl_base {
   int device = 0;
   std::vector<DevLinear> lin;
   std::atomic<int> refs{0};
+  uint8_t digest[32] = {};  // recorded at load from the canonical blocks
+  mutable std::mutex mem_mu;  // guards held and budget
+  int64_t held = 0;         // device bytes: base arrays + live adapter arenas
+  int64_t budget = 0;       // 0 = no cap
 };
 
 struct AdEntry {
@@ -94,6 +99,7 @@ struct AdapterImpl {
   std::vector<int> slot;  // per base linear: index into ent, or -1
   uint8_t digest[32] = {};
   void* mem = nullptr;
+  int64_t reserved = 0;  // bytes counted in base->held
   ~AdapterImpl() {
     if (mem) {
       int cur = 0;
@@ -101,6 +107,10 @@ struct AdapterImpl {
       hipSetDevice(base->device);
       hipFree(mem);
       hipSetDevice(cur);
+    }
+    if (reserved) {
+      std::lock_guard<std::mutex> g(base->mem_mu);
+      base->held -= reserved;
     }
     if (base) base->refs.fetch_sub(1);
   }
@@ -126,10 +136,10 @@ struct ListImpl {
   std::vector<float> in_scales;
   std::vector<std::vector<LoraRef>> plan;         // per linear, in list order
   std::vector<int> total_rank;                    // per linear
+  uint8_t digest[32] = {};                        // composition identity
   int device = 0;
   std::mutex ev_mu;
   std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
-
 
   void mark_use(hipStream_t st) {
     std::lock_guard<std::mutex> g(ev_mu);
@@ -154,19 +164,74 @@ struct ListImpl {
   }
 };
 
+// Records, at scope exit, that work enqueued on `st` may read list L, so that
+// L (and the adapter memory it holds) outlives that work even when a run
+// returns an error after enqueuing part of it.
+struct ListUse {
+  ListImpl* L;
+  hipStream_t st;
+  bool on;
+  ~ListUse() {
+    if (on) L->mark_use(st);
+  }
+};
+
 struct qbl_comp {
   qbl_base* base = nullptr;
-  std::mutex mu;
-  std::shared_ptr<ListImpl> list;  // read and replaced with std::atomic_load / atomic_store
+  std::mutex mu;                   // serialises list changes
+  std::shared_ptr<ListImpl> list;  // read and replaced with std::atomic_load / atomic_exchange
+  std::shared_ptr<ListImpl> prev;  // the list the last change replaced (under mu)
 };
 
 namespace {
+
+void put_le32(uint8_t* p, uint32_t v) {
+  for (int i = 0; i < 4; ++i) p[i] = (uint8_t)(v >> (8 * i));
+}
+void put_le64(uint8_t* p, uint64_t v) {
+  for (int i = 0; i < 8; ++i) p[i] = (uint8_t)(v >> (8 * i));
+}
+
+// SHA-256 of one linear as a file: 24-byte header, then its canonical blocks.
+void linear_digest(int qtype, int64_t n, int64_t k, const void* blocks, int64_t nbytes,
+                   uint8_t out[32]) {
+  uint8_t hdr[24];
+  put_le32(hdr, (uint32_t)qtype);
+  put_le32(hdr + 4, 0);
+  put_le64(hdr + 8, (uint64_t)n);
+  put_le64(hdr + 16, (uint64_t)k);
+  qbl::Sha256 h;
+  h.update(hdr, sizeof hdr);
+  h.update(blocks, (size_t)nbytes);
+  h.final(out);
+}
+
+// The composition identity over the effective entries (scale != 0).
+void identity(const uint8_t base_digest[32], const std::vector<const uint8_t*>& ads,
+              const std::vector<float>& scales, uint8_t out[32]) {
+  uint8_t w[4];
+  qbl::Sha256 h;
+  put_le32(w, (uint32_t)QBL_ABI_VERSION);
+  h.update(w, 4);
+  h.update(base_digest, 32);
+  put_le32(w, (uint32_t)ads.size());
+  h.update(w, 4);
+  for (size_t i = 0; i < ads.size(); ++i) {
+    h.update(ads[i], 32);
+    uint32_t bits;
+    std::memcpy(&bits, &scales[i], 4);
+    put_le32(w, bits);
+    h.update(w, 4);
+  }
+  h.final(out);
+}
 
 std::shared_ptr<ListImpl> empty_list(const qbl_base* b) {
   auto L = std::make_shared<ListImpl>();
   L->device = b->device;
   L->plan.assign(b->lin.size(), {});
   L->total_rank.assign(b->lin.size(), 0);
+  identity(b->digest, {}, {}, L->digest);
   return L;
 }
 
@@ -177,6 +242,68 @@ qbl_status check_device(const qbl_base* b) {
     return fail(QBL_E_ARG, "current HIP device %d is not the base's device %d", cur, b->device);
   return QBL_OK;
 }
+
+// -- test-only fault points (qbl_fault_inject) --
+constexpr int kFaultPoints = QBL_FAULT_SWAP + 1;
+std::atomic<int> g_fault[kFaultPoints];
+
+// True once: on the hit that `point` was armed for.
+bool fault_fires(int point) {
+  int v = g_fault[point].load();
+  while (v > 0)
+    if (g_fault[point].compare_exchange_weak(v, v - 1)) return v == 1;
+  return false;
+}
+
+hipError_t dev_alloc(void** p, int64_t bytes) {
+  *p = nullptr;
+  if (fault_fires(QBL_FAULT_DEVICE_ALLOC)) return hipErrorOutOfMemory;
+  return hipMalloc(p, (size_t)bytes);
+}
+
+// One host-to-device copy of a staged upload.
+struct Part {
+  void* dst;
+  const void* src;
+  int64_t n;
+};
+
+// Copies every part to the device, then reads each device copy back and
+// compares it byte for byte with its source.  Runs on worker threads, so the
+// message goes to *msg instead of the thread's error text.
+qbl_status upload_verified(const Part* parts, int np, std::string* msg) {
+  for (int i = 0; i < np; ++i) {
+    const hipError_t e = hipMemcpy(parts[i].dst, parts[i].src, (size_t)parts[i].n, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      *msg = std::string("upload: ") + hipGetErrorString(e);
+      return QBL_E_DEVICE;
+    }
+  }
+  if (np > 0 && parts[0].n > 0 && fault_fires(QBL_FAULT_CORRUPT)) {
+    uint8_t* at = static_cast<uint8_t*>(parts[0].dst) + parts[0].n / 2;
+    uint8_t byte = 0;
+    if (hipMemcpy(&byte, at, 1, hipMemcpyDeviceToHost) == hipSuccess) {
+      byte ^= 0x01;
+      hipMemcpy(at, &byte, 1, hipMemcpyHostToDevice);
+    }
+  }
+  std::vector<uint8_t> back;
+  for (int i = 0; i < np; ++i) {
+    back.resize((size_t)parts[i].n);
+    const hipError_t e = hipMemcpy(back.data(), parts[i].dst, (size_t)parts[i].n, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+      *msg = std::string("read-back: ") + hipGetErrorString(e);
+      return QBL_E_DEVICE;
+    }
+    if (std::memcmp(back.data(), parts[i].src, (size_t)parts[i].n) != 0) {
+      *msg = "the device copy read back differs from the bytes sent";
+      return QBL_E_CHECKSUM;
+    }
+  }
+  return QBL_OK;
+}
+
+int loader_threads() { return std::min(qbl::default_threads(), 16); }
 
 }  // namespace
 
@@ -232,6 +359,7 @@ extern "C" qbl_status qbl_base_load(const qbl_linear_desc* descs, int32_t n_line
                                     qbl_base** out) {
   QBL_TRY({
     if (!descs || !out || n_linears <= 0) return fail(QBL_E_ARG, "need descs, out and n_linears >= 1");
+    // -- validation
     for (int i = 0; i < n_linears; ++i) {
       const qbl_linear_desc& d = descs[i];
       if (qbl_status s = check_qshape(d.qtype, d.n_out, d.k_in))
@@ -253,7 +381,8 @@ extern "C" qbl_status qbl_base_load(const qbl_linear_desc* descs, int32_t n_line
       for (auto& L : b->lin) hipFree(L.mem);
       b->lin.clear();
     };
-    std::vector<uint8_t> stage;
+    // -- allocation: one device arena per linear
+    int64_t held = 0;
     for (int i = 0; i < n_linears; ++i) {
       const qbl_linear_desc& d = descs[i];
       DevLinear L{};
@@ -262,24 +391,42 @@ extern "C" qbl_status qbl_base_load(const qbl_linear_desc* descs, int32_t n_line
       L.k = d.k_in;
       L.qs_bytes = qbl::qs_bytes(d.qtype, d.n_out, d.k_in);
       L.sc_bytes = qbl::sc_bytes(d.qtype, d.n_out, d.k_in);
-      const int64_t total = align_up(L.qs_bytes) + align_up(L.sc_bytes);
-      e = hipMalloc(&L.mem, (size_t)total);
+      L.mem_bytes = align_up(L.qs_bytes) + align_up(L.sc_bytes);
+      e = dev_alloc(&L.mem, L.mem_bytes);
       if (e != hipSuccess) {
         release();
-        return fail(QBL_E_NOMEM, "linear %d: hipMalloc(%lld): %s", i, (long long)total, hipGetErrorString(e));
+        return fail(QBL_E_NOMEM, "linear %d: device allocation of %lld bytes: %s", i,
+                    (long long)L.mem_bytes, hipGetErrorString(e));
       }
       L.qs = static_cast<uint8_t*>(L.mem);
       L.sc = L.qs + align_up(L.qs_bytes);
       b->lin.push_back(L);
-      stage.resize((size_t)total);
-      qbl::repack_rows(d.qtype, static_cast<const uint8_t*>(d.blocks), d.n_out, d.k_in, stage.data(),
-                       stage.data() + align_up(L.qs_bytes), 0);
-      e = hipMemcpy(L.mem, stage.data(), (size_t)total, hipMemcpyHostToDevice);
-      if (e != hipSuccess) {
-        release();
-        return hip_fail(e, "hipMemcpy of base linear");
-      }
+      held += L.mem_bytes;
     }
+    // -- staging (repack), upload, verification and digest, linears in parallel
+    std::vector<uint8_t> digests((size_t)n_linears * 32);
+    std::vector<qbl_status> st((size_t)n_linears, QBL_OK);
+    std::vector<std::string> msg((size_t)n_linears);
+    qbl::parallel_for(n_linears, loader_threads(), [&](int64_t i) {
+      hipSetDevice(dev);
+      const qbl_linear_desc& d = descs[i];
+      const DevLinear& L = b->lin[(size_t)i];
+      linear_digest(d.qtype, d.n_out, d.k_in, d.blocks, d.nbytes, &digests[(size_t)i * 32]);
+      std::vector<uint8_t> stage((size_t)L.mem_bytes, 0);
+      qbl::repack_rows(d.qtype, static_cast<const uint8_t*>(d.blocks), d.n_out, d.k_in, stage.data(),
+                       stage.data() + align_up(L.qs_bytes), 1);
+      const Part p{L.mem, stage.data(), L.mem_bytes};
+      st[(size_t)i] = upload_verified(&p, 1, &msg[(size_t)i]);
+    });
+    for (int i = 0; i < n_linears; ++i)
+      if (st[(size_t)i] != QBL_OK) {
+        release();
+        return fail(st[(size_t)i], "linear %d: %s", i, msg[(size_t)i].c_str());
+      }
+    qbl::Sha256 h;
+    h.update(digests.data(), digests.size());
+    h.final(b->digest);
+    b->held = held;
     *out = b.release();
     return QBL_OK;
   })
@@ -302,6 +449,12 @@ extern "C" qbl_status qbl_base_info(const qbl_base* base, int32_t linear, int32_
   return QBL_OK;
 }
 
+extern "C" qbl_status qbl_base_digest(const qbl_base* base, uint8_t sha256_out[32]) {
+  if (!base || !sha256_out) return fail(QBL_E_ARG, "null pointer");
+  std::memcpy(sha256_out, base->digest, 32);
+  return QBL_OK;
+}
+
 extern "C" qbl_status qbl_base_hash(qbl_base* base, uint8_t sha256_out[32]) {
   QBL_TRY({
     if (!base || !sha256_out) return fail(QBL_E_ARG, "null pointer");
@@ -309,7 +462,7 @@ extern "C" qbl_status qbl_base_hash(qbl_base* base, uint8_t sha256_out[32]) {
     const int64_t n = (int64_t)base->lin.size();
     std::vector<uint8_t> digests((size_t)n * 32);
     std::vector<int> err((size_t)n, 0);
-    qbl::parallel_for(n, std::min(qbl::default_threads(), 16), [&](int64_t i) {
+    qbl::parallel_for(n, loader_threads(), [&](int64_t i) {
       hipSetDevice(base->device);
       const DevLinear& L = base->lin[(size_t)i];
       std::vector<uint8_t> buf((size_t)(L.qs_bytes + L.sc_bytes));
@@ -319,9 +472,10 @@ extern "C" qbl_status qbl_base_hash(qbl_base* base, uint8_t sha256_out[32]) {
         err[(size_t)i] = 1;
         return;
       }
-      qbl::Sha256 h;
-      h.update(buf.data(), buf.size());
-      h.final(&digests[(size_t)i * 32]);
+      const int64_t nbytes = L.n * (L.k / 32) * qbl_block_bytes(L.qtype);
+      std::vector<uint8_t> blocks((size_t)nbytes);
+      qbl::unpack_rows(L.qtype, buf.data(), buf.data() + L.qs_bytes, L.n, L.k, blocks.data());
+      linear_digest(L.qtype, L.n, L.k, blocks.data(), nbytes, &digests[(size_t)i * 32]);
     });
     for (int x : err)
       if (x) return fail(QBL_E_DEVICE, "reading base bytes back failed");
@@ -330,6 +484,25 @@ extern "C" qbl_status qbl_base_hash(qbl_base* base, uint8_t sha256_out[32]) {
     h.final(sha256_out);
     return QBL_OK;
   })
+}
+
+extern "C" qbl_status qbl_base_set_budget(qbl_base* base, int64_t budget_bytes) {
+  if (!base) return fail(QBL_E_ARG, "null base");
+  if (budget_bytes < 0) return fail(QBL_E_ARG, "negative budget");
+  std::lock_guard<std::mutex> g(base->mem_mu);
+  if (budget_bytes > 0 && budget_bytes < base->held)
+    return fail(QBL_E_BUDGET, "budget %lld below the %lld bytes already held", (long long)budget_bytes,
+                (long long)base->held);
+  base->budget = budget_bytes;
+  return QBL_OK;
+}
+
+extern "C" qbl_status qbl_base_memory(const qbl_base* base, int64_t* held_bytes, int64_t* budget_bytes) {
+  if (!base) return fail(QBL_E_ARG, "null base");
+  std::lock_guard<std::mutex> g(base->mem_mu);
+  if (held_bytes) *held_bytes = base->held;
+  if (budget_bytes) *budget_bytes = base->budget;
+  return QBL_OK;
 }
 
 extern "C" qbl_status qbl_base_free(qbl_base* base) {
@@ -353,6 +526,7 @@ extern "C" qbl_status qbl_adapter_load(qbl_base* base, const qbl_lora_desc* desc
     if (!base || !descs || !out) return fail(QBL_E_ARG, "null pointer");
     if (n <= 0) return fail(QBL_E_ARG, "an adapter must target at least one linear");
     if (qbl_status s = check_device(base)) return s;
+    // -- validation: targets, ranks and shapes first, then the values
     const int nl = (int)base->lin.size();
     std::vector<char> seen((size_t)nl, 0);
     int64_t total = 0;
@@ -366,18 +540,33 @@ extern "C" qbl_status qbl_adapter_load(qbl_base* base, const qbl_lora_desc* desc
         return fail(QBL_E_LIMIT, "entry %d: rank %d outside 1..%d", i, d.rank, QBL_MAX_RANK);
       if (!d.A || !d.B) return fail(QBL_E_ARG, "entry %d: null factor", i);
       const DevLinear& L = base->lin[(size_t)d.linear];
-      if (!all_finite(d.A, (int64_t)d.rank * L.k) || !all_finite(d.B, L.n * d.rank))
-        return fail(QBL_E_NONFINITE, "entry %d: non-finite value in A or B", i);
       total += align_up((int64_t)d.rank * L.k * 4) + align_up(L.n * d.rank * 4);
     }
+    std::vector<char> bad((size_t)n, 0);
+    qbl::parallel_for(n, loader_threads(), [&](int64_t i) {
+      const qbl_lora_desc& d = descs[i];
+      const DevLinear& L = base->lin[(size_t)d.linear];
+      bad[(size_t)i] = !all_finite(d.A, (int64_t)d.rank * L.k) || !all_finite(d.B, L.n * d.rank);
+    });
+    for (int i = 0; i < n; ++i)
+      if (bad[(size_t)i]) return fail(QBL_E_NONFINITE, "entry %d: non-finite value in A or B", i);
+    // -- allocation: reserve the arena within the base's budget, then allocate
     auto impl = std::make_shared<AdapterImpl>();
-    hipError_t e = hipMalloc(&impl->mem, (size_t)total);
-    if (e != hipSuccess) return fail(QBL_E_NOMEM, "hipMalloc(%lld): %s", (long long)total, hipGetErrorString(e));
     impl->base = base;
     base->refs.fetch_add(1);
+    {
+      std::lock_guard<std::mutex> g(base->mem_mu);
+      if (base->budget > 0 && base->held + total > base->budget)
+        return fail(QBL_E_BUDGET, "adapter needs %lld bytes; %lld of the budget of %lld are held",
+                    (long long)total, (long long)base->held, (long long)base->budget);
+      base->held += total;
+      impl->reserved = total;
+    }
+    hipError_t e = dev_alloc(&impl->mem, total);
+    if (e != hipSuccess)
+      return fail(QBL_E_NOMEM, "device allocation of %lld bytes: %s", (long long)total, hipGetErrorString(e));
     impl->slot.assign((size_t)nl, -1);
     uint8_t* p = static_cast<uint8_t*>(impl->mem);
-    qbl::Sha256 h;
     for (int i = 0; i < n; ++i) {
       const qbl_lora_desc& d = descs[i];
       const DevLinear& L = base->lin[(size_t)d.linear];
@@ -385,17 +574,35 @@ extern "C" qbl_status qbl_adapter_load(qbl_base* base, const qbl_lora_desc* desc
       p += align_up((int64_t)d.rank * L.k * 4);
       en.B = reinterpret_cast<float*>(p);
       p += align_up(L.n * d.rank * 4);
-      const size_t abytes = (size_t)d.rank * L.k * 4, bbytes = (size_t)L.n * d.rank * 4;
-      e = hipMemcpy(en.A, d.A, abytes, hipMemcpyHostToDevice);
-      if (e == hipSuccess) e = hipMemcpy(en.B, d.B, bbytes, hipMemcpyHostToDevice);
-      if (e != hipSuccess) return hip_fail(e, "hipMemcpy of adapter");  // impl frees itself
-      const int32_t hdr[2] = {d.linear, d.rank};
-      h.update(hdr, sizeof hdr);
-      h.update(d.A, abytes);
-      h.update(d.B, bbytes);
       impl->slot[(size_t)d.linear] = (int)impl->ent.size();
       impl->ent.push_back(en);
     }
+    // -- staging, verification and digests, entries in parallel
+    std::vector<uint8_t> digests((size_t)n * 32);
+    std::vector<qbl_status> st((size_t)n, QBL_OK);
+    std::vector<std::string> msg((size_t)n);
+    qbl::parallel_for(n, loader_threads(), [&](int64_t i) {
+      hipSetDevice(base->device);
+      const qbl_lora_desc& d = descs[i];
+      const DevLinear& L = base->lin[(size_t)d.linear];
+      const AdEntry& en = impl->ent[(size_t)i];
+      const int64_t abytes = (int64_t)d.rank * L.k * 4, bbytes = L.n * d.rank * 4;
+      uint8_t hdr[8];
+      put_le32(hdr, (uint32_t)d.linear);
+      put_le32(hdr + 4, (uint32_t)d.rank);
+      qbl::Sha256 h;
+      h.update(hdr, sizeof hdr);
+      h.update(d.A, (size_t)abytes);
+      h.update(d.B, (size_t)bbytes);
+      h.final(&digests[(size_t)i * 32]);
+      const Part parts[2] = {{en.A, d.A, abytes}, {en.B, d.B, bbytes}};
+      st[(size_t)i] = upload_verified(parts, 2, &msg[(size_t)i]);
+    });
+    for (int i = 0; i < n; ++i)
+      if (st[(size_t)i] != QBL_OK)  // impl frees its arena and its reservation
+        return fail(st[(size_t)i], "entry %d: %s", i, msg[(size_t)i].c_str());
+    qbl::Sha256 h;
+    h.update(digests.data(), digests.size());
     h.final(impl->digest);
     auto* a = new qbl_adapter;
     a->impl = std::move(impl);
@@ -417,6 +624,18 @@ extern "C" qbl_status qbl_adapter_free(qbl_adapter* adapter) {
 }
 
 // ---------------------------------------------------------- compositions ---
+
+namespace {
+
+// The exchange of a list change (comp->mu held): the new list becomes current
+// in one atomic step and the replaced one is kept as the previous list.
+qbl_status swap_in(qbl_comp* comp, std::shared_ptr<ListImpl> L) {
+  if (fault_fires(QBL_FAULT_SWAP)) return fail(QBL_E_INJECTED, "injected failure before the exchange");
+  comp->prev = std::atomic_exchange(&comp->list, std::move(L));
+  return QBL_OK;
+}
+
+}  // namespace
 
 extern "C" qbl_status qbl_comp_create(qbl_base* base, qbl_comp** out) {
   QBL_TRY({
@@ -465,26 +684,28 @@ extern "C" qbl_status qbl_comp_attach(qbl_comp* comp, const qbl_adapter* const* 
         same = cur->in_ads[(size_t)i] == list[i]->impl.get() && cur->in_scales[(size_t)i] == scales[i];
       if (same) return QBL_OK;
     }
-    // -- staging: build the new immutable list
+    // -- staging: build the new immutable list and its identity
     auto L = empty_list(base);
+    std::vector<const uint8_t*> eff_digests;
     for (int i = 0; i < n; ++i) {
       L->in_ads.push_back(list[i]->impl.get());
       L->in_scales.push_back(scales[i]);
       if (scales[i] == 0.0f) continue;  // a zero-scale entry contributes nothing
       L->ads.push_back(list[i]->impl);
       L->scales.push_back(scales[i]);
+      eff_digests.push_back(list[i]->impl->digest);
       for (const AdEntry& e : list[i]->impl->ent) {
         L->plan[(size_t)e.linear].push_back(LoraRef{e.A, e.B, e.rank, scales[i]});
         L->total_rank[(size_t)e.linear] += e.rank;
       }
     }
-    // keep the refs of adapters in in_ads alive via ads only for non-zero entries;
-    // zero-scale entries are compared by address, so hold them as well
+    identity(base->digest, eff_digests, L->scales, L->digest);
+    // zero-scale entries are compared by address in the idempotency check, so
+    // hold them as well
     for (int i = 0; i < n; ++i)
       if (scales[i] == 0.0f) L->ads.push_back(list[i]->impl);
     // -- commit: one atomic exchange; the old list retires when its last user drops it
-    std::atomic_store(&comp->list, std::move(L));
-    return QBL_OK;
+    return swap_in(comp, std::move(L));
   })
 }
 
@@ -493,8 +714,29 @@ extern "C" qbl_status qbl_comp_clear(qbl_comp* comp) {
     if (!comp) return fail(QBL_E_ARG, "null composition");
     std::lock_guard<std::mutex> g(comp->mu);
     if (std::atomic_load(&comp->list)->in_ads.empty()) return QBL_OK;
-    std::atomic_store(&comp->list, empty_list(comp->base));
-    return QBL_OK;
+    return swap_in(comp, empty_list(comp->base));
+  })
+}
+
+extern "C" qbl_status qbl_comp_rollback(qbl_comp* comp) {
+  QBL_TRY({
+    if (!comp) return fail(QBL_E_ARG, "null composition");
+    std::lock_guard<std::mutex> g(comp->mu);
+    if (!comp->prev) return fail(QBL_E_STATE, "no previous list to return to");
+    std::shared_ptr<ListImpl> back = comp->prev;
+    return swap_in(comp, std::move(back));
+  })
+}
+
+extern "C" qbl_status qbl_comp_drop_previous(qbl_comp* comp) {
+  QBL_TRY({
+    if (!comp) return fail(QBL_E_ARG, "null composition");
+    std::shared_ptr<ListImpl> old;
+    {
+      std::lock_guard<std::mutex> g(comp->mu);
+      old.swap(comp->prev);
+    }
+    return QBL_OK;  // `old` retires here, after the work that used it
   })
 }
 
@@ -504,14 +746,47 @@ extern "C" qbl_status qbl_comp_count(const qbl_comp* comp, int32_t* n) {
   return QBL_OK;
 }
 
+extern "C" qbl_status qbl_comp_digest(const qbl_comp* comp, uint8_t sha256_out[32]) {
+  if (!comp || !sha256_out) return fail(QBL_E_ARG, "null pointer");
+  std::memcpy(sha256_out, std::atomic_load(&comp->list)->digest, 32);
+  return QBL_OK;
+}
+
+extern "C" qbl_status qbl_identity_digest(const uint8_t base_digest[32], const uint8_t* adapter_digests,
+                                          const float* scales, int32_t n, uint8_t sha256_out[32]) {
+  QBL_TRY({
+    if (!base_digest || !sha256_out) return fail(QBL_E_ARG, "null pointer");
+    if (n < 0 || n > QBL_MAX_ADAPTERS) return fail(QBL_E_LIMIT, "list of %d adapters; at most %d", n, QBL_MAX_ADAPTERS);
+    if (n > 0 && (!adapter_digests || !scales)) return fail(QBL_E_ARG, "null digests or scales");
+    std::vector<const uint8_t*> ads;
+    std::vector<float> sc;
+    for (int i = 0; i < n; ++i) {
+      if (!std::isfinite(scales[i])) return fail(QBL_E_NONFINITE, "scale %d is not finite", i);
+      if (scales[i] == 0.0f) continue;
+      ads.push_back(adapter_digests + 32 * i);
+      sc.push_back(scales[i]);
+    }
+    identity(base_digest, ads, sc, sha256_out);
+    return QBL_OK;
+  })
+}
+
 extern "C" qbl_status qbl_comp_free(qbl_comp* comp) {
   if (!comp) return fail(QBL_E_ARG, "null composition");
   {
     std::lock_guard<std::mutex> g(comp->mu);
     std::atomic_store(&comp->list, std::shared_ptr<ListImpl>());
+    comp->prev.reset();
   }
   comp->base->refs.fetch_sub(1);
   delete comp;
+  return QBL_OK;
+}
+
+extern "C" qbl_status qbl_fault_inject(int32_t point, int32_t after) {
+  if (point < 1 || point >= kFaultPoints) return fail(QBL_E_ARG, "unknown fault point %d", point);
+  if (after < 0) return fail(QBL_E_ARG, "negative count");
+  g_fault[point].store(after);
   return QBL_OK;
 }
 
@@ -937,11 +1212,8 @@ extern "C" qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x,
     float* outs[1] = {y};
     const float* v[1] = {x};
     const DevLinear& D = b->lin[(size_t)linear];
-    if (qbl_status s = run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr,
-                                 static_cast<float*>(ws), st))
-      return s;
-    if (T > 0) L->mark_use(st);
-    return QBL_OK;
+    const ListUse use{L.get(), st, T > 0};
+    return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), st);
   })
 }
 
@@ -979,11 +1251,11 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
     a.total_rank = T;
     a.ws = static_cast<uint16_t*>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const ListUse use{L.get(), st, T > 0};
     KernelTimer tm(2, st);
     hipError_t e = qbl::launch_jit(a, tm.ctx());
     if (e != hipSuccess) return hip_fail(e, "jit launch");
     tm.stop();
-    if (T > 0) L->mark_use(st);
     return QBL_OK;
   })
 }
@@ -1003,10 +1275,9 @@ extern "C" qbl_status qbl_block(qbl_comp* comp, int32_t block, const float* x, f
     if (qbl_status s = check_ws(ws, ws_bytes, need.bytes)) return s;
     const BlockWs w = block_ws(ws, B.d, B.h, blocks_tmax(L.get(), block, 1));
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const ListUse use{L.get(), st, true};
     if (qbl_status s = run_block(b, L.get(), B, x, 0, w, st)) return s;
-    if (qbl_status s = run_rms(w.dd, B.d, y, st)) return s;
-    L->mark_use(st);
-    return QBL_OK;
+    return run_rms(w.dd, B.d, y, st);
   })
 }
 
@@ -1034,6 +1305,7 @@ extern "C" qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_
     if (qbl_status s = check_ws(ws, ws_bytes, block_ws(nullptr, d, h, tmax).bytes)) return s;
     const BlockWs w = block_ws(ws, d, h, tmax);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const ListUse use{L.get(), st, true};
     for (int t = 0; t < n_tokens; ++t) {
       const float* in = t == 0 ? x0 : y_tokens + (int64_t)(t - 1) * d;
       for (int i = 0; i < n_blocks; ++i) {
@@ -1042,7 +1314,6 @@ extern "C" qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_
       }
       if (qbl_status s = run_rms(w.dd, d, y_tokens + (int64_t)t * d, st)) return s;
     }
-    L->mark_use(st);
     return QBL_OK;
   })
 }

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_block_bytes():
-    assert q.qbl_abi_version() == 1
+    assert q.qbl_abi_version() == 2
     assert q.qbl_block_bytes(q.QBL_Q8_0) == 34 and q.qbl_block_bytes(q.QBL_Q4_SM) == 20
     assert q.qbl_block_bytes(7) == 0
 
