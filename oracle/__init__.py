@@ -22,6 +22,7 @@ _lib = None
 
 Q8_0 = 1
 Q4_SM = 2
+Q4_K = 3
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
 
@@ -61,6 +62,7 @@ def _load():
             "or_bf16_from_f64": (ctypes.c_uint16, [ctypes.c_double]),
             "or_f32_from_bf16": (ctypes.c_float, [ctypes.c_uint16]),
             "or_block_bytes": (i32, [i32]),
+            "or_block_weights": (i32, [i32]),
             "or_quantize": (i32, [i32, vp, i64, i64, vp]),
             "or_dequantize": (i32, [i32, vp, i64, i64, vp]),
             "or_linear_dual": (i32, [i32, vp, i64, i64, vp, i32, vp, i32, vp, i64, vp, i32]),
@@ -130,11 +132,18 @@ def block_bytes(qtype: int) -> int:
     return int(_load().or_block_bytes(qtype))
 
 
+def block_weights(qtype: int) -> int:
+    return int(_load().or_block_weights(qtype))
+
+
 def quantize(qtype: int, w) -> np.ndarray:
-    """Canonical block bytes (uint8, n x (k/32*block_bytes)) of a float32 matrix."""
+    """Canonical block bytes (uint8, n x (k/block_weights*block_bytes)) of a float32 matrix."""
     w = _c(w, np.float32)
     n, k = w.shape
-    out = np.empty((n, k // 32 * block_bytes(qtype)), np.uint8)
+    bw = block_weights(qtype)
+    if bw == 0:
+        raise ValueError(f"unknown quantisation type {qtype}")
+    out = np.empty((n, k // bw * block_bytes(qtype)), np.uint8)
     if _load().or_quantize(qtype, w.ctypes.data, n, k, out.ctypes.data) != 0:
         raise ValueError("or_quantize rejected its arguments")
     return out

@@ -111,7 +111,11 @@ uint16_t or_bf16_from_f64(double v) {
 /* ------------------------------------------------------------------------ */
 
 int32_t or_block_bytes(int32_t qtype) {
-  return qtype == OR_Q8_0 ? 34 : qtype == OR_Q4_SM ? 20 : 0;
+  return qtype == OR_Q8_0 ? 34 : qtype == OR_Q4_SM ? 20 : qtype == OR_Q4_K ? 144 : 0;
+}
+
+int32_t or_block_weights(int32_t qtype) {
+  return qtype == OR_Q8_0 || qtype == OR_Q4_SM ? 32 : qtype == OR_Q4_K ? 256 : 0;
 }
 
 static void put16(uint8_t* p, uint16_t v) {
@@ -156,6 +160,79 @@ static void quantize_q4_sm_block(const float* w, uint8_t* blk) {
   for (int i = 0; i < 16; ++i) blk[4 + i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
 }
 
+/* ------------------------------------------------------------------------ */
+/* q4_K: a super-block of 256 weights in 8 sub-blocks of 32, each with a     */
+/* 6-bit scale and a 6-bit minimum, under two fp16 super-scales (Deep        */
+/* Technical Design, section 5: 4.5 bits per weight).  The page gives no     */
+/* more than that; the reading taken here:                                   */
+/*   sub-block j has step D_j = d * sc_j and offset M_j = dmin * m_j, with   */
+/*   sc_j, m_j in 0..63, and a weight is w = D_j * q - M_j, q in 0..15;       */
+/*   bytes (144): [d fp16][dmin fp16][12 B of sixteen 6-bit codes: code i    */
+/*   in bits 6i..6i+5 of the 96-bit little-endian field, codes 0..7 are      */
+/*   sc_0..sc_7 and 8..15 are m_0..m_7][128 B: sub-block j's 16 bytes at     */
+/*   offset 16 + 16j, byte i = q[32j + 2i] | q[32j + 2i + 1] << 4].           */
+/* Quantiser, per sub-block: lo = min(0, min w), hi = max w,                  */
+/* s = (hi - lo)/15, t = 0 - lo; then d = fp16(max s / 63),                   */
+/* dmin = fp16(max t / 63); sc = min(63, ceil(s/d)) (the smallest code whose */
+/* step covers the range), m = min(63, round(t/dmin)) (codes 0 when their    */
+/* super-scale is 0); q = clamp(round((w + M)/D), 0, 15), or 0 when D = 0.   */
+/* ------------------------------------------------------------------------ */
+
+static void put_code6(uint8_t* field, int i, unsigned v) {
+  for (int b = 0; b < 6; ++b)
+    if ((v >> b) & 1u) {
+      const int bit = 6 * i + b;
+      field[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+    }
+}
+
+static unsigned get_code6(const uint8_t* field, int i) {
+  unsigned v = 0;
+  for (int b = 0; b < 6; ++b) {
+    const int bit = 6 * i + b;
+    v |= (unsigned)((field[bit >> 3] >> (bit & 7)) & 1u) << b;
+  }
+  return v;
+}
+
+static void quantize_q4_k_block(const float* w, uint8_t* blk) {
+  float s[8], t[8], smax = 0.0f, tmax = 0.0f;
+  for (int j = 0; j < 8; ++j) {
+    float lo = 0.0f, hi = w[32 * j];
+    for (int i = 0; i < 32; ++i) {
+      lo = fminf(lo, w[32 * j + i]);
+      hi = fmaxf(hi, w[32 * j + i]);
+    }
+    s[j] = (hi - lo) / 15.0f;
+    t[j] = 0.0f - lo; /* +0 for lo = 0, so a zero block stores dmin = +0 */
+    smax = fmaxf(smax, s[j]);
+    tmax = fmaxf(tmax, t[j]);
+  }
+  const uint16_t dh = or_f16_from_f32(smax / 63.0f);
+  const uint16_t mh = or_f16_from_f32(tmax / 63.0f);
+  const float d = or_f32_from_f16(dh), dmin = or_f32_from_f16(mh);
+  memset(blk, 0, 144);
+  put16(blk, dh);
+  put16(blk + 2, mh);
+  for (int j = 0; j < 8; ++j) {
+    float sc = d == 0.0f ? 0.0f : ceilf(s[j] / d);
+    float mc = dmin == 0.0f ? 0.0f : roundf(t[j] / dmin);
+    if (sc > 63.0f) sc = 63.0f;
+    if (mc > 63.0f) mc = 63.0f;
+    put_code6(blk + 4, j, (unsigned)sc);
+    put_code6(blk + 4, 8 + j, (unsigned)mc);
+    const float D = d * sc, M = dmin * mc;
+    uint8_t q[32];
+    for (int i = 0; i < 32; ++i) {
+      float v = D == 0.0f ? 0.0f : roundf((w[32 * j + i] + M) / D);
+      if (v < 0.0f) v = 0.0f;
+      if (v > 15.0f) v = 15.0f;
+      q[i] = (uint8_t)v;
+    }
+    for (int i = 0; i < 16; ++i) blk[16 + 16 * j + i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
+  }
+}
+
 typedef struct {
   int32_t qtype;
   const float* w;
@@ -166,15 +243,18 @@ typedef struct {
 static void quant_row(void* vc, int64_t r, double* unused) {
   const quant_ctx* c = (const quant_ctx*)vc;
   (void)unused;
-  const int64_t nb = c->k / 32;
+  const int32_t bw = or_block_weights(c->qtype);
+  const int64_t nb = c->k / bw;
   const int32_t bb = or_block_bytes(c->qtype);
   for (int64_t b = 0; b < nb; ++b) {
-    const float* src = c->w + r * c->k + b * 32;
+    const float* src = c->w + r * c->k + b * bw;
     uint8_t* dst = c->blocks + (r * nb + b) * bb;
     if (c->qtype == OR_Q8_0)
       quantize_q8_0_block(src, dst);
-    else
+    else if (c->qtype == OR_Q4_SM)
       quantize_q4_sm_block(src, dst);
+    else
+      quantize_q4_k_block(src, dst);
   }
 }
 
@@ -183,22 +263,35 @@ static int32_t for_rows(int64_t n_rows, int32_t nthreads, int64_t scratch_len,
 
 int32_t or_quantize(int32_t qtype, const float* w, int64_t n, int64_t k, uint8_t* blocks) {
   const int32_t bb = or_block_bytes(qtype);
-  if (!bb || !w || !blocks || n < 0 || k <= 0 || k % 32) return -1;
+  if (!bb || !w || !blocks || n < 0 || k <= 0 || k % or_block_weights(qtype)) return -1;
   quant_ctx c = {qtype, w, k, blocks};
   return for_rows(n, 0, 0, quant_row, &c);
 }
 
 /* Dequantise one row into float64: exact, since d*q has at most 15
- * significant bits and d*q + m fits easily in 53. */
+ * significant bits and d*q + m fits easily in 53 (q4_K: d*sc*q has at most
+ * 21 and dmin*m at most 17). */
 static void dequant_row(int32_t qtype, const uint8_t* blocks, int64_t row, int64_t k,
                         double* out) {
-  const int64_t nb = k / 32;
+  const int32_t bw = or_block_weights(qtype);
+  const int64_t nb = k / bw;
   const int32_t bb = or_block_bytes(qtype);
   for (int64_t b = 0; b < nb; ++b) {
     const uint8_t* blk = blocks + (row * nb + b) * bb;
     const double d = (double)or_f32_from_f16(get16(blk));
     if (qtype == OR_Q8_0) {
       for (int j = 0; j < 32; ++j) out[b * 32 + j] = d * (double)(int8_t)blk[2 + j];
+    } else if (qtype == OR_Q4_K) {
+      const double dmin = (double)or_f32_from_f16(get16(blk + 2));
+      for (int j = 0; j < 8; ++j) {
+        const double D = d * (double)get_code6(blk + 4, j);
+        const double M = dmin * (double)get_code6(blk + 4, 8 + j);
+        for (int i = 0; i < 16; ++i) {
+          const uint8_t byte = blk[16 + 16 * j + i];
+          out[b * 256 + 32 * j + 2 * i] = D * (double)(byte & 0x0F) - M;
+          out[b * 256 + 32 * j + 2 * i + 1] = D * (double)(byte >> 4) - M;
+        }
+      }
     } else {
       const double m = (double)or_f32_from_f16(get16(blk + 2));
       for (int i = 0; i < 16; ++i) {
@@ -210,7 +303,8 @@ static void dequant_row(int32_t qtype, const uint8_t* blocks, int64_t row, int64
 }
 
 int32_t or_dequantize(int32_t qtype, const uint8_t* blocks, int64_t n, int64_t k, double* out) {
-  if (!or_block_bytes(qtype) || !blocks || !out || n < 0 || k <= 0 || k % 32) return -1;
+  if (!or_block_bytes(qtype) || !blocks || !out || n < 0 || k <= 0 || k % or_block_weights(qtype))
+    return -1;
   for (int64_t r = 0; r < n; ++r) dequant_row(qtype, blocks, r, k, out + r * k);
   return 0;
 }
@@ -343,7 +437,9 @@ static void dual_row(void* vc, int64_t i, double* wrow) {
 
 static int32_t check_lin(int32_t qtype, const uint8_t* blocks, int64_t n, int64_t k,
                          const or_lora* ads, int32_t n_ads, const int64_t* rows, int64_t n_rows) {
-  if (!or_block_bytes(qtype) || !blocks || n <= 0 || k <= 0 || k % 32 || n_ads < 0) return -1;
+  if (!or_block_bytes(qtype) || !blocks || n <= 0 || k <= 0 || k % or_block_weights(qtype) ||
+      n_ads < 0)
+    return -1;
   if (n_ads && !ads) return -1;
   for (int32_t a = 0; a < n_ads; ++a)
     if (ads[a].rank <= 0 || !ads[a].A || !ads[a].B) return -1;

@@ -20,7 +20,7 @@
 extern "C" {
 #endif
 
-enum { OR_Q8_0 = 1, OR_Q4_SM = 2 };
+enum { OR_Q8_0 = 1, OR_Q4_SM = 2, OR_Q4_K = 3 };
 
 /* IEEE 754 binary16 / bfloat16 conversions, round to nearest even. */
 uint16_t or_f16_from_f32(float f);
@@ -29,13 +29,17 @@ uint16_t or_bf16_from_f32(float f);
 uint16_t or_bf16_from_f64(double v);
 float or_f32_from_bf16(uint16_t b);
 
-/* Bytes of one 32-weight block: q8_0 34, q4_sm 20; 0 for an unknown type. */
+/* Bytes of one block: q8_0 34, q4_sm 20, q4_K 144; 0 for an unknown type. */
 int32_t or_block_bytes(int32_t qtype);
+/* Weights of one block: 32 (q8_0, q4_sm) or 256 (q4_K); 0 for an unknown type. */
+int32_t or_block_weights(int32_t qtype);
 
-/* Quantise a row-major n x k float32 matrix (k a multiple of 32) into
- * canonical blocks: rows in order, blocks along k within a row.
+/* Quantise a row-major n x k float32 matrix (k a multiple of the block's
+ * weights) into canonical blocks: rows in order, blocks along k within a row.
  *   q8_0 block : [fp16 d little-endian][32 x int8 q]                   34 B
  *   q4_sm block: [fp16 d][fp16 m][16 B, byte i = q[2i] | q[2i+1] << 4]  20 B
+ *   q4_K block : [fp16 d][fp16 dmin][12 B of 6-bit codes][128 B nibbles] 144 B
+ *                (256 weights; the layout and quantiser are spelled out in oracle.c)
  * Returns 0, or -1 on a bad argument. */
 int32_t or_quantize(int32_t qtype, const float* w, int64_t n, int64_t k, uint8_t* blocks);
 

@@ -202,4 +202,4 @@ def test_quantize_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.quantize(oracle.Q8_0, np.zeros((4, 48), np.float32))
     with pytest.raises(ValueError):
-        oracle.quantize(3, np.zeros((4, 64), np.float32))
+        oracle.quantize(7, np.zeros((4, 64), np.float32))
