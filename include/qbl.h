@@ -73,6 +73,16 @@ typedef int32_t qbl_status;
  *   Canonical block bytes: [d][m][16 B; byte i = q[2i] | q[2i+1] << 4] = 20 B. */
 #define QBL_Q8_0 1
 #define QBL_Q4_SM 2
+/* QBL_Q4_K: super-blocks of 256 weights in 8 sub-blocks of 32 ([design]
+ *   section 5: a 6-bit scale and a 6-bit minimum per sub-block under two f16
+ *   super-scales, 4.5 bits per weight).  Sub-block j has step D_j = d * sc_j and
+ *   offset M_j = dmin * m_j (sc_j, m_j in 0..63) and w = D_j * q - M_j, q in 0..15.
+ *   Canonical block bytes (144): [d fp16][dmin fp16][12 B: sixteen 6-bit codes,
+ *   code i in bits 6i..6i+5 of the 96-bit little-endian field, codes 0..7 =
+ *   sc_0..sc_7, 8..15 = m_0..m_7][128 B: sub-block j's 16 bytes at offset
+ *   16 + 16j, byte i = q[32j + 2i] | q[32j + 2i + 1] << 4].  The page names the
+ *   parts but not their bit layout; this layout is the library's. */
+#define QBL_Q4_K 3
 
 /* Limits. */
 #define QBL_MAX_ADAPTERS 8     /* entries in one attached list */
@@ -91,17 +101,27 @@ const char* qbl_last_error(void);
 /* QBL_ABI_VERSION of the built library (not a status). */
 int32_t qbl_abi_version(void);
 
-/* Bytes of one 32-weight block of qtype (34 or 20); 0 for an unknown type. */
+/* Bytes of one block of qtype (q8_0 34, q4_sm 20, q4_K 144); 0 for an unknown type. */
 int64_t qbl_block_bytes(int32_t qtype);
 
-/* Quantise a host float32 matrix w (n x k, k a multiple of 32) into canonical
- * blocks (host, n*k/32*qbl_block_bytes bytes, caller-owned).
+/* Weights of one block of qtype (32, or 256 for q4_K); 0 for an unknown type.
+ * A linear's k_in must be a multiple of it. */
+int64_t qbl_block_weights(int32_t qtype);
+
+/* Quantise a host float32 matrix w (n x k, k a multiple of qbl_block_weights)
+ * into canonical blocks (host, n*k/qbl_block_weights*qbl_block_bytes bytes,
+ * caller-owned).
  * q8_0: d = fp16(max|w|/127), q = round-half-away(w / d) with the stored d, clamped
  *   to [-127, 127]; an all-zero block gives d = 0, q = 0.
  * q4_sm: m = fp16(min w), d = fp16((max w - m)/15), q = round-half-away((w - m)/d)
  *   clamped to [0, 15]; q = 0 where d = 0.
- * nthreads <= 0 uses the online cores.  QBL_E_NONFINITE on NaN/Inf input,
- * QBL_E_LIMIT if a q8_0 scale would overflow fp16. */
+ * q4_K: per sub-block lo = min(0, min w), hi = max w, s = (hi - lo)/15, t = 0 - lo;
+ *   d = fp16(max s / 63), dmin = fp16(max t / 63); sc = min(63, ceil(s / d)),
+ *   m = min(63, round-half-away(t / dmin)) (0 where the super-scale is 0);
+ *   q = round-half-away((w + M)/D) clamped to [0, 15]; q = 0 where D = 0.
+ * All arithmetic in float32.  nthreads <= 0 uses the online cores.
+ * QBL_E_NONFINITE on NaN/Inf input, QBL_E_LIMIT if a scale, minimum or
+ * super-scale would overflow fp16. */
 qbl_status qbl_quantize(int32_t qtype, const float* w, int64_t n, int64_t k, void* blocks_out,
                         int32_t nthreads);
 
@@ -109,7 +129,8 @@ qbl_status qbl_quantize(int32_t qtype, const float* w, int64_t n, int64_t k, voi
  * qbl_adapter_digest. */
 qbl_status qbl_sha256(const void* data, int64_t n, uint8_t sha256_out[32]);
 
-/* Dequantise canonical blocks (host) to float32 (host, n x k). */
+/* Dequantise canonical blocks (host) to float32 (host, n x k); q4_K as
+ * fma(D, q, -M) in float32. */
 qbl_status qbl_dequantize(int32_t qtype, const void* blocks, int64_t n, int64_t k, float* w_out);
 
 /* ---------------------------------------------------------------- base --- */
@@ -120,7 +141,7 @@ typedef struct {
   int32_t reserved; /* must be 0 */
   int64_t n_out;
   int64_t k_in;
-  const void* blocks; /* host, n_out * k_in/32 * qbl_block_bytes(qtype) bytes */
+  const void* blocks; /* host, n_out * k_in/qbl_block_weights * qbl_block_bytes(qtype) bytes */
   int64_t nbytes;     /* must equal that size */
 } qbl_linear_desc;
 
@@ -327,7 +348,7 @@ qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x, float* y, 
  *   W_eff = bf16( float32(deq(W)) + sum_i bf16(s_i B_i) bf16(A_i) )    (tile by tile, on chip)
  *   Y = X W_eff^T with float32 accumulation.
  * X: device bfloat16 bit patterns, m x k_in; Y: device float32 m x n_out;
- * q8_0 and q4_sm bases; m >= 1. */
+ * q8_0 and q4_sm bases (QBL_E_FORMAT for q4_K); m >= 1. */
 qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint16_t* x_bf16, float* y,
                           int32_t m, void* ws, int64_t ws_bytes, void* stream);
 

@@ -32,6 +32,7 @@ import torch  # noqa: E402,F401
 QBL_OK = 0
 QBL_Q8_0 = 1
 QBL_Q4_SM = 2
+QBL_Q4_K = 3
 QBL_MAX_ADAPTERS = 8
 QBL_MAX_RANK = 256
 QBL_MAX_TOTAL_RANK = 512
@@ -70,6 +71,7 @@ EXPORTS = {
     "qbl_last_error": (ctypes.c_char_p, []),
     "qbl_abi_version": (_i32, []),
     "qbl_block_bytes": (_i64, [_i32]),
+    "qbl_block_weights": (_i64, [_i32]),
     "qbl_quantize": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32]),
     "qbl_dequantize": (_i32, [_i32, _vp, _i64, _i64, _vp]),
     "qbl_sha256": (_i32, [_vp, _i64, _vp]),
@@ -160,11 +162,15 @@ class Library:
     def qbl_block_bytes(self, qtype: int) -> int:
         return int(self._lib.qbl_block_bytes(qtype))
 
+    def qbl_block_weights(self, qtype: int) -> int:
+        return int(self._lib.qbl_block_weights(qtype))
+
     def qbl_quantize(self, qtype: int, w, nthreads: int = 0) -> np.ndarray:
-        """Canonical blocks (uint8, n x k/32*block_bytes) of a host float32 matrix."""
+        """Canonical blocks (uint8, n x k/block_weights*block_bytes) of a host float32 matrix."""
         w = _host(w, np.float32)
         n, k = w.shape
-        out = np.empty((n, max(0, k // 32) * max(1, self.qbl_block_bytes(qtype))), np.uint8)
+        bw = max(1, self.qbl_block_weights(qtype))
+        out = np.empty((n, max(0, k // bw) * max(1, self.qbl_block_bytes(qtype))), np.uint8)
         self._check(self._lib.qbl_quantize(qtype, w.ctypes.data, n, k, out.ctypes.data, nthreads))
         return out
 

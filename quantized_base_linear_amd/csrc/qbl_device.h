@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "qbl_kernels.h"
 
@@ -77,18 +78,48 @@ __device__ __forceinline__ float4 mul4(float c, float4 a) {
 
 // ---------------------------------------------------------------------------
 // 16-byte weight chunks: a q8_0 chunk is 16 weights (half a block), a q4_sm
-// chunk is one whole 32-weight block.  In LDS the four 16-byte slots of a
-// chunk's input are rotated per chunk so that the lanes served together by an
-// LDS read touch different bank groups.
+// chunk is one whole 32-weight block, a q4_K chunk one 32-weight sub-block.
+// In LDS the 16-byte slots of a chunk's input are rotated per chunk so that the
+// lanes served together by an LDS read touch different bank groups.
+//
+// Scale data per chunk (Sc): q8_0 the block's fp16 d, q4_sm the block's
+// (d | m << 16); q4_K the whole 16-byte header of the chunk's super-block (the
+// 8 lanes of one super-block read the same 16 bytes: one cache line per 64
+// lanes), from which the chunk's step and offset are decoded.
 // ---------------------------------------------------------------------------
 template <int QT>
 struct Fmt {
   static constexpr int kWeightsPerChunk = QT == QBL_FMT_Q8 ? 16 : 32;
   static constexpr int kSlots = kWeightsPerChunk / 4;
+  using Sc = std::conditional_t<QT == QBL_FMT_Q4K, uint4, uint32_t>;
   __device__ static __forceinline__ int slot(int c, int j) {
     return (j + (QT == QBL_FMT_Q8 ? (c >> 1) : c)) & (kSlots - 1);
   }
+  static constexpr int64_t row_bytes(int k) { return QT == QBL_FMT_Q8 ? (int64_t)k : (int64_t)k / 2; }
+  // scale data of chunk c (global chunk index along k) of a row
+  __device__ static __forceinline__ Sc load_sc(const void* sc, int row, int k, int c) {
+    if constexpr (QT == QBL_FMT_Q8)
+      return reinterpret_cast<const uint16_t*>(sc)[(int64_t)row * (k / 32) + (c >> 1)];
+    else if constexpr (QT == QBL_FMT_Q4)
+      return reinterpret_cast<const uint32_t*>(sc)[(int64_t)row * (k / 32) + c];
+    else {
+      const u32x4 v = *gp(reinterpret_cast<const u32x4*>(sc) + (int64_t)row * (k / 256) + (c >> 3));
+      return make_uint4(v.x, v.y, v.z, v.w);
+    }
+  }
 };
+
+// Step D and offset M of sub-block j of a q4_K super-block header h (w = D*q - M):
+// h.x = d | dmin << 16; h.y, h.z, h.w = the 96-bit code field, scale code j at
+// field bits 6j.., min code j at field bits 48 + 6j...  D and M are exact in float32.
+__device__ __forceinline__ void q4k_step_offset(const uint4 h, int j, float& D, float& M) {
+  const uint64_t lo = (uint64_t)h.y | ((uint64_t)h.z << 32);  // field bits 0..63
+  const uint64_t hi = (uint64_t)h.z | ((uint64_t)h.w << 32);  // field bits 32..95
+  const uint32_t sc = (uint32_t)(lo >> (6 * j)) & 63u;
+  const uint32_t mc = (uint32_t)(hi >> (16 + 6 * j)) & 63u;
+  D = h2f(h.x) * (float)sc;
+  M = h2f(h.x >> 16) * (float)mc;
+}
 
 // Sum_j q_j x_j over one q8_0 chunk of 16 weights.  The device stores q8_0
 // bytes offset-binary (u = q + 128), which convert with v_cvt_f32_ubyte; the
@@ -129,6 +160,27 @@ __device__ __forceinline__ float dot_q4(const uint4 q, const float4* xv) {
     s1 = fmaf(ub(hi, 3), xb.w, s1);
   }
   return s0 + s1;
+}
+
+// p + (the chunk's dequantised weights . x) for chunk c (global index along k)
+// with weights q, inputs xv, input sum xsum and scale data sc:
+//   q8_0  p + d * (sum q x)                    (offset-binary bytes, see dot_q8)
+//   q4_sm p + d * (sum q x) + m * (sum x)
+//   q4_K  p + D * (sum q x) - M * (sum x)      (D, M of the chunk's sub-block)
+template <int QT>
+__device__ __forceinline__ float chunk_dot(float p, const uint4 q, const float4* xv, float xsum,
+                                           const typename Fmt<QT>::Sc sc, int c) {
+  if constexpr (QT == QBL_FMT_Q8) {
+    return fmaf(h2f(sc), dot_q8(q, xv, xsum), p);
+  } else if constexpr (QT == QBL_FMT_Q4) {
+    p = fmaf(h2f(sc), dot_q4(q, xv), p);
+    return fmaf(h2f(sc >> 16), xsum, p);
+  } else {
+    float D, M;
+    q4k_step_offset(sc, c & 7, D, M);
+    p = fmaf(D, dot_q4(q, xv), p);
+    return fmaf(-M, xsum, p);
+  }
 }
 
 // A value handed from one workgroup to others in the same launch: one 64-bit

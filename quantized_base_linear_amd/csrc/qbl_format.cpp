@@ -107,11 +107,82 @@ bool q4_block(const float* w, uint8_t* out) {
   return true;
 }
 
+// One q4_K super-block of 256 weights (include/qbl.h gives the layout): per
+// 32-weight sub-block the smallest 6-bit scale code whose step covers the
+// sub-block's range down to min(0, min w), the nearest 6-bit code for that
+// offset, then 4-bit q.  Returns false if a super-scale overflows fp16.
+bool q4k_block(const float* w, uint8_t* out) {
+  float span[8], off[8], span_max = 0.0f, off_max = 0.0f;
+  for (int j = 0; j < 8; ++j) {
+    const float* v = w + 32 * j;
+    float lo = 0.0f, hi = v[0];
+    for (int i = 0; i < 32; ++i) {
+      lo = std::min(lo, v[i]);
+      hi = std::max(hi, v[i]);
+    }
+    span[j] = (hi - lo) / 15.0f;
+    off[j] = 0.0f - lo;
+    span_max = std::max(span_max, span[j]);
+    off_max = std::max(off_max, off[j]);
+  }
+  const uint16_t dh = to_half_bits(span_max / 63.0f), mh = to_half_bits(off_max / 63.0f);
+  if (!half_finite(dh) || !half_finite(mh)) return false;
+  const float d = from_half_bits(dh), dmin = from_half_bits(mh);
+  uint64_t field_lo = 0, field_hi = 0;  // the 96-bit code field, bits 0..63 and 64..95
+  auto put_code = [&](int i, uint32_t c) {
+    const int bit = 6 * i;
+    if (bit < 64) field_lo |= (uint64_t)c << bit;
+    if (bit + 6 > 64) field_hi |= bit >= 64 ? (uint64_t)c << (bit - 64) : (uint64_t)c >> (64 - bit);
+  };
+  out[0] = (uint8_t)(dh & 0xFF);
+  out[1] = (uint8_t)(dh >> 8);
+  out[2] = (uint8_t)(mh & 0xFF);
+  out[3] = (uint8_t)(mh >> 8);
+  for (int j = 0; j < 8; ++j) {
+    const float sc = d != 0.0f ? std::min(63.0f, std::ceil(span[j] / d)) : 0.0f;
+    const float mc = dmin != 0.0f ? std::min(63.0f, std::round(off[j] / dmin)) : 0.0f;
+    put_code(j, (uint32_t)sc);
+    put_code(8 + j, (uint32_t)mc);
+    const float step = d * sc, offset = dmin * mc;
+    uint8_t* nib = out + 16 + 16 * j;
+    for (int i = 0; i < 16; ++i) {
+      uint8_t pair = 0;
+      for (int h = 0; h < 2; ++h) {
+        float q = step != 0.0f ? std::round((w[32 * j + 2 * i + h] + offset) / step) : 0.0f;
+        q = std::min(15.0f, std::max(0.0f, q));
+        pair |= (uint8_t)((int)q << (4 * h));
+      }
+      nib[i] = pair;
+    }
+  }
+  for (int b = 0; b < 8; ++b) out[4 + b] = (uint8_t)(field_lo >> (8 * b));
+  for (int b = 0; b < 4; ++b) out[12 + b] = (uint8_t)(field_hi >> (8 * b));
+  return true;
+}
+
 }  // namespace
+
+int64_t block_weights(int qtype) { return qtype == QBL_Q4_K ? 256 : 32; }
+
+// The 6-bit codes of sub-block j (scale, min) from a q4_K block's 12 code bytes.
+void q4k_codes(const uint8_t* field, int j, uint32_t* sc, uint32_t* m) {
+  uint64_t lo = 0, hi = 0;
+  for (int b = 0; b < 8; ++b) lo |= (uint64_t)field[b] << (8 * b);
+  for (int b = 0; b < 4; ++b) hi |= (uint64_t)field[8 + b] << (8 * b);
+  auto code = [&](int i) -> uint32_t {
+    const int bit = 6 * i;
+    uint64_t v = bit < 64 ? lo >> bit : 0;
+    if (bit + 6 > 64) v |= bit >= 64 ? hi >> (bit - 64) : hi << (64 - bit);
+    return (uint32_t)(v & 63u);
+  };
+  *sc = code(j);
+  *m = code(8 + j);
+}
 
 int quantize_rows(int qtype, const float* w, int64_t n, int64_t k, uint8_t* blocks, int nthreads) {
   const int64_t bb = qbl_block_bytes(qtype);
-  const int64_t nb = k / 32;
+  const int64_t bw = block_weights(qtype);
+  const int64_t nb = k / bw;
   std::vector<char> bad((size_t)n, 0);
   parallel_for(n, nthreads, [&](int64_t r) {
     const float* row = w + r * k;
@@ -121,8 +192,10 @@ int quantize_rows(int qtype, const float* w, int64_t n, int64_t k, uint8_t* bloc
         return;
       }
     for (int64_t b = 0; b < nb; ++b) {
-      const bool ok = qtype == QBL_Q8_0 ? q8_block(row + 32 * b, blocks + (r * nb + b) * bb)
-                                        : q4_block(row + 32 * b, blocks + (r * nb + b) * bb);
+      uint8_t* dst = blocks + (r * nb + b) * bb;
+      const float* src = row + bw * b;
+      const bool ok = qtype == QBL_Q8_0 ? q8_block(src, dst) : qtype == QBL_Q4_SM ? q4_block(src, dst)
+                                                                                 : q4k_block(src, dst);
       if (!ok) {
         bad[(size_t)r] = 2;
         return;
@@ -138,13 +211,26 @@ int quantize_rows(int qtype, const float* w, int64_t n, int64_t k, uint8_t* bloc
 
 int dequantize_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, float* out) {
   const int64_t bb = qbl_block_bytes(qtype);
-  const int64_t nb = k / 32;
+  const int64_t bw = block_weights(qtype);
+  const int64_t nb = k / bw;
   parallel_for(n, 0, [&](int64_t r) {
     for (int64_t b = 0; b < nb; ++b) {
       const uint8_t* p = blocks + (r * nb + b) * bb;
       const float d = from_half_bits((uint16_t)(p[0] | (p[1] << 8)));
-      float* o = out + r * k + 32 * b;
-      if (qtype == QBL_Q8_0) {
+      float* o = out + r * k + bw * b;
+      if (qtype == QBL_Q4_K) {
+        const float dmin = from_half_bits((uint16_t)(p[2] | (p[3] << 8)));
+        for (int j = 0; j < 8; ++j) {
+          uint32_t sc, m;
+          q4k_codes(p + 4, j, &sc, &m);
+          const float step = d * (float)sc, offset = dmin * (float)m;
+          for (int i = 0; i < 16; ++i) {
+            const uint8_t byte = p[16 + 16 * j + i];
+            o[32 * j + 2 * i] = std::fma(step, (float)(byte & 0x0F), -offset);
+            o[32 * j + 2 * i + 1] = std::fma(step, (float)(byte >> 4), -offset);
+          }
+        }
+      } else if (qtype == QBL_Q8_0) {
         for (int j = 0; j < 32; ++j) o[j] = d * (float)(int8_t)p[2 + j];
       } else {
         const float m = from_half_bits((uint16_t)(p[2] | (p[3] << 8)));
@@ -160,17 +246,20 @@ int dequantize_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, floa
 
 int64_t qs_bytes(int qtype, int64_t n, int64_t k) { return qtype == QBL_Q8_0 ? n * k : n * k / 2; }
 int64_t sc_bytes(int qtype, int64_t n, int64_t k) {
-  return qtype == QBL_Q8_0 ? n * (k / 32) * 2 : n * (k / 32) * 4;
+  return qtype == QBL_Q8_0 ? n * (k / 32) * 2 : qtype == QBL_Q4_SM ? n * (k / 32) * 4 : n * (k / 256) * 16;
 }
 
 void repack_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, uint8_t* qs, uint8_t* sc,
                  int nthreads) {
   const int64_t bb = qbl_block_bytes(qtype);
-  const int64_t nb = k / 32;
+  const int64_t nb = k / block_weights(qtype);
   parallel_for(n, nthreads, [&](int64_t r) {
     for (int64_t b = 0; b < nb; ++b) {
       const uint8_t* p = blocks + (r * nb + b) * bb;
-      if (qtype == QBL_Q8_0) {  // offset-binary on the device: u = q + 128
+      if (qtype == QBL_Q4_K) {  // nibbles as they are; the 16-byte header beside them
+        std::memcpy(qs + r * (k / 2) + 128 * b, p + 16, 128);
+        std::memcpy(sc + (r * nb + b) * 16, p, 16);
+      } else if (qtype == QBL_Q8_0) {  // offset-binary on the device: u = q + 128
         uint8_t* dst = qs + r * k + 32 * b;
         for (int j = 0; j < 32; ++j) dst[j] = (uint8_t)(p[2 + j] ^ 0x80u);
         std::memcpy(sc + (r * nb + b) * 2, p, 2);
@@ -185,11 +274,14 @@ void repack_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, uint8_t
 void unpack_rows(int qtype, const uint8_t* qs, const uint8_t* sc, int64_t n, int64_t k,
                  uint8_t* blocks) {
   const int64_t bb = qbl_block_bytes(qtype);
-  const int64_t nb = k / 32;
+  const int64_t nb = k / block_weights(qtype);
   for (int64_t r = 0; r < n; ++r)
     for (int64_t b = 0; b < nb; ++b) {
       uint8_t* p = blocks + (r * nb + b) * bb;
-      if (qtype == QBL_Q8_0) {
+      if (qtype == QBL_Q4_K) {
+        std::memcpy(p, sc + (r * nb + b) * 16, 16);
+        std::memcpy(p + 16, qs + r * (k / 2) + 128 * b, 128);
+      } else if (qtype == QBL_Q8_0) {
         std::memcpy(p, sc + (r * nb + b) * 2, 2);
         const uint8_t* src = qs + r * k + 32 * b;
         for (int j = 0; j < 32; ++j) p[2 + j] = (uint8_t)(src[j] ^ 0x80u);

@@ -197,8 +197,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   float* xsum = xs + BB * KT;             // [BB][KT / WPC]
   float* ts = xsum + BB * tile_chunks;    // [B][T]
   const int T = a.t_stride;
-  const int nblk = K / 32;
-  const int64_t row_bytes = QT == QBL_FMT_Q8 ? (int64_t)K : (int64_t)K / 2;
+  const int64_t row_bytes = F::row_bytes(K);
   const int n_ad = g.lora.n_ad;
   const bool prefetch = g.lora.prefetch != 0;
 
@@ -244,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     }
 
     uint4 q[RPW][CPL];
-    uint32_t sc[RPW][CPL];
+    typename F::Sc sc[RPW][CPL];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const uint8_t* qrow = g.qs + (int64_t)lrow[r] * row_bytes;
@@ -252,10 +251,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
       for (int u = 0; u < CPL; ++u) {
         const int c = min(lane + 64 * u, CT - 1);
         q[r][u] = stream_load16(qrow + (int64_t)(c0 + c) * 16);
-        if (QT == QBL_FMT_Q8)
-          sc[r][u] = reinterpret_cast<const uint16_t*>(g.sc)[(int64_t)lrow[r] * nblk + ((c0 + c) >> 1)];
-        else
-          sc[r][u] = reinterpret_cast<const uint32_t*>(g.sc)[(int64_t)lrow[r] * nblk + c0 + c];
+        sc[r][u] = F::load_sc(g.sc, lrow[r], K, c0 + c);
       }
     }
 
@@ -304,15 +300,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
           for (int j = 0; j < NS; ++j) xv[j] = *reinterpret_cast<const float4*>(xc + 4 * F::slot(c, j));
           const float xsc = xsum[b * tile_chunks + c];
 #pragma unroll
-          for (int r = 0; r < RPW; ++r) {
-            const float d = h2f(sc[r][u]);
-            if (QT == QBL_FMT_Q8) {
-              acc[r][b] = fmaf(d, dot_q8(q[r][u], xv, xsc), acc[r][b]);
-            } else {
-              acc[r][b] = fmaf(d, dot_q4(q[r][u], xv), acc[r][b]);
-              acc[r][b] = fmaf(h2f(sc[r][u] >> 16), xsc, acc[r][b]);
-            }
-          }
+          for (int r = 0; r < RPW; ++r) acc[r][b] = chunk_dot<QT>(acc[r][b], q[r][u], xv, xsc, sc[r][u], c0 + c);
         }
       }
     }
@@ -416,8 +404,8 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
 
   const GemvArgs& a = f.g;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int K = a.k, CT = K / WPC, nblk = K / 32;
-  const int64_t row_bytes = QT == QBL_FMT_Q8 ? (int64_t)K : (int64_t)K / 2;
+  const int K = a.k, CT = K / WPC;
+  const int64_t row_bytes = F::row_bytes(K);
   const bool shrinker = (int)blockIdx.x < f.shrink_wgs;
   const int wg = (int)blockIdx.x - f.shrink_wgs;
 
@@ -463,10 +451,11 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
       xr[u][j] = t4;
     }
 
+  using Sc = typename F::Sc;
   uint4 qa[G][CPW], qb[G][CPW];
-  uint32_t sa[G][CPW], sb[G][CPW];
+  Sc sa[G][CPW], sb[G][CPW];
   float4 av[RS][CPW][NS];
-  auto load_group = [&](uint4 (&q)[G][CPW], uint32_t (&sc)[G][CPW], int grp) {
+  auto load_group = [&](uint4 (&q)[G][CPW], Sc (&sc)[G][CPW], int grp) {
 #pragma unroll
     for (int r = 0; r < G; ++r) {
       const int s = grp * G + r;
@@ -477,10 +466,7 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
 #pragma unroll
         for (int u = 0; u < CPW; ++u) {
           q[r][u] = stream_load16(qrow + (int64_t)cidx[u] * 16);
-          if (QT == QBL_FMT_Q8)
-            sc[r][u] = reinterpret_cast<const uint16_t*>(g.sc)[(int64_t)row * nblk + (cidx[u] >> 1)];
-          else
-            sc[r][u] = reinterpret_cast<const uint32_t*>(g.sc)[(int64_t)row * nblk + cidx[u]];
+          sc[r][u] = F::load_sc(g.sc, row, K, cidx[u]);
         }
       }
     }
@@ -570,22 +556,14 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   }
 
   // ---- row loop: two groups in flight; each group's rows reduced together
-  auto compute_group = [&](const uint4 (&q)[G][CPW], const uint32_t (&sc)[G][CPW], int grp) {
+  auto compute_group = [&](const uint4 (&q)[G][CPW], const Sc (&sc)[G][CPW], int grp) {
     float p[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) p[r] = 0.0f;
 #pragma unroll
     for (int r = 0; r < G; ++r) {
 #pragma unroll
-      for (int u = 0; u < CPW; ++u) {
-        const float d = h2f(sc[r][u]);
-        if (QT == QBL_FMT_Q8) {
-          p[r] = fmaf(d, dot_q8(q[r][u], xr[u], xsm[u]), p[r]);
-        } else {
-          p[r] = fmaf(d, dot_q4(q[r][u], xr[u]), p[r]);
-          p[r] = fmaf(h2f(sc[r][u] >> 16), xsm[u], p[r]);
-        }
-      }
+      for (int u = 0; u < CPW; ++u) p[r] = chunk_dot<QT>(p[r], q[r][u], xr[u], xsm[u], sc[r][u], cidx[u]);
     }
     reduce_rows16<G>(p, lane);
     const int r = (lane & 15) >> (4 - LG);
@@ -804,7 +782,7 @@ hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc) {
 bool fused_supported(int qtype, int k) {
   const int wpc = qtype == QBL_FMT_Q8 ? 16 : 32;
   const int max_cpw = qtype == QBL_FMT_Q8 ? 4 : 2;
-  return k % 32 == 0 && (k / wpc + 63) / 64 <= 8 * max_cpw;
+  return k % (qtype == QBL_FMT_Q4K ? 256 : 32) == 0 && (k / wpc + 63) / 64 <= 8 * max_cpw;
 }
 
 hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc) {
@@ -814,7 +792,12 @@ hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc) {
   for (int i = 0; i < a.nseg; ++i)
     if (f.sum && a.seg[i].n != a.seg[0].n) return hipErrorInvalidValue;
   f.rows_per_wg = 0;  // chosen by the launcher from the kernel's occupancy
-  return a.qtype == QBL_FMT_Q8 ? launch_b1_q<QBL_FMT_Q8>(f, lc) : launch_b1_q<QBL_FMT_Q4>(f, lc);
+  switch (a.qtype) {
+    case QBL_FMT_Q8: return launch_b1_q<QBL_FMT_Q8>(f, lc);
+    case QBL_FMT_Q4: return launch_b1_q<QBL_FMT_Q4>(f, lc);
+    case QBL_FMT_Q4K: return launch_b1_q<QBL_FMT_Q4K>(f, lc);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc) {
@@ -833,8 +816,12 @@ hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc) {
     for (int j = 0; j < L.n_ad; ++j)
       if (L.rank[j] > 64) L.prefetch = 0;
   }
-  return a.qtype == QBL_FMT_Q8 ? launch_batch<QBL_FMT_Q8>(a, bb, cpl, lc)
-                               : launch_batch<QBL_FMT_Q4>(a, bb, cpl, lc);
+  switch (a.qtype) {
+    case QBL_FMT_Q8: return launch_batch<QBL_FMT_Q8>(a, bb, cpl, lc);
+    case QBL_FMT_Q4: return launch_batch<QBL_FMT_Q4>(a, bb, cpl, lc);
+    case QBL_FMT_Q4K: return launch_batch<QBL_FMT_Q4K>(a, bb, cpl, lc);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qbl

@@ -30,9 +30,14 @@ int default_threads();
 int quantize_rows(int qtype, const float* w, int64_t n, int64_t k, uint8_t* blocks, int nthreads);
 int dequantize_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, float* out);
 
+// Weights per canonical block: 32, or 256 for q4_K.
+int64_t block_weights(int qtype);
+
 // Canonical blocks -> device layout (host staging buffers):
 //   q8_0 : qs offset-binary bytes u = q + 128 [n][k] and d fp16 [n][k/32]
 //   q4_sm: qs packed nibbles [n][k/2] and dm uint32 (d | m << 16) [n][k/32]
+//   q4_K : qs packed nibbles [n][k/2] and the 16-byte super-block header
+//          (d, dmin, 12 code bytes) [n][k/256]
 void repack_rows(int qtype, const uint8_t* blocks, int64_t n, int64_t k, uint8_t* qs, uint8_t* sc,
                  int nthreads);
 // The inverse of repack_rows: device-layout arrays back to canonical blocks.

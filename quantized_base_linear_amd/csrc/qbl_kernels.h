@@ -18,8 +18,9 @@ namespace qbl {
       hipLaunchKernelGGL(kernel, grid, block, lds, (lc).stream, __VA_ARGS__);                      \
   } while (0)
 
-constexpr int QBL_FMT_Q8 = 1;  // same values as QBL_Q8_0 / QBL_Q4_SM of the C ABI
+constexpr int QBL_FMT_Q8 = 1;  // same values as QBL_Q8_0 / QBL_Q4_SM / QBL_Q4_K of the C ABI
 constexpr int QBL_FMT_Q4 = 2;
+constexpr int QBL_FMT_Q4K = 3;
 constexpr int kMaxAdapters = 8;
 constexpr int kMaxSegs = 3;                        // linears sharing one input in one launch
 constexpr int kMaxPrepEntries = kMaxSegs * kMaxAdapters;
@@ -36,8 +37,9 @@ struct LoraSeg {
 
 // One linear of a fused GEMV launch.
 struct GemvSeg {
-  const uint8_t* qs;   // q8_0: offset-binary bytes q + 128 [n][k]; q4_sm: packed nibbles [n][k/2]
-  const void* sc;      // q8_0: fp16 d [n][k/32]; q4_sm: uint32 (d | m << 16) [n][k/32]
+  const uint8_t* qs;   // q8_0: offset-binary bytes q + 128 [n][k]; q4_sm, q4_K: packed nibbles [n][k/2]
+  const void* sc;      // q8_0: fp16 d [n][k/32]; q4_sm: uint32 (d | m << 16) [n][k/32];
+                       // q4_K: 16-byte super-block header (d, dmin, 12 code bytes) [n][k/256]
   float* y;            // [batch][y_stride]
   int64_t y_stride;
   int n;

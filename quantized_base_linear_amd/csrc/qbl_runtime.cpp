@@ -312,7 +312,10 @@ int loader_threads() { return std::min(qbl::default_threads(), 16); }
 extern "C" const char* qbl_last_error(void) { return g_err.c_str(); }
 extern "C" int32_t qbl_abi_version(void) { return QBL_ABI_VERSION; }
 extern "C" int64_t qbl_block_bytes(int32_t qtype) {
-  return qtype == QBL_Q8_0 ? 34 : qtype == QBL_Q4_SM ? 20 : 0;
+  return qtype == QBL_Q8_0 ? 34 : qtype == QBL_Q4_SM ? 20 : qtype == QBL_Q4_K ? 144 : 0;
+}
+extern "C" int64_t qbl_block_weights(int32_t qtype) {
+  return qtype == QBL_Q8_0 || qtype == QBL_Q4_SM ? 32 : qtype == QBL_Q4_K ? 256 : 0;
 }
 
 extern "C" qbl_status qbl_sha256(const void* data, int64_t n, uint8_t sha256_out[32]) {
@@ -326,7 +329,8 @@ extern "C" qbl_status qbl_sha256(const void* data, int64_t n, uint8_t sha256_out
 static qbl_status check_qshape(int32_t qtype, int64_t n, int64_t k) {
   if (!qbl_block_bytes(qtype)) return fail(QBL_E_FORMAT, "unknown quantisation type %d", qtype);
   if (n <= 0 || k <= 0) return fail(QBL_E_SHAPE, "non-positive shape %lld x %lld", (long long)n, (long long)k);
-  if (k % 32) return fail(QBL_E_FORMAT, "k_in=%lld is not a multiple of 32", (long long)k);
+  const int64_t bw = qbl_block_weights(qtype);
+  if (k % bw) return fail(QBL_E_FORMAT, "k_in=%lld is not a multiple of %lld", (long long)k, (long long)bw);
   if (k > QBL_MAX_K) return fail(QBL_E_LIMIT, "k_in=%lld above %d", (long long)k, QBL_MAX_K);
   if (n > (int64_t)1 << 30) return fail(QBL_E_LIMIT, "n_out=%lld too large", (long long)n);
   return QBL_OK;
@@ -366,7 +370,7 @@ extern "C" qbl_status qbl_base_load(const qbl_linear_desc* descs, int32_t n_line
         return fail(s, "linear %d: %s", i, qbl_last_error());
       if (d.reserved != 0) return fail(QBL_E_ARG, "linear %d: reserved field must be 0", i);
       if (!d.blocks) return fail(QBL_E_ARG, "linear %d: null blocks", i);
-      const int64_t want = d.n_out * (d.k_in / 32) * qbl_block_bytes(d.qtype);
+      const int64_t want = d.n_out * (d.k_in / qbl_block_weights(d.qtype)) * qbl_block_bytes(d.qtype);
       if (d.nbytes != want)
         return fail(QBL_E_FORMAT, "linear %d: nbytes %lld, expected %lld", i, (long long)d.nbytes,
                     (long long)want);
@@ -472,7 +476,7 @@ extern "C" qbl_status qbl_base_hash(qbl_base* base, uint8_t sha256_out[32]) {
         err[(size_t)i] = 1;
         return;
       }
-      const int64_t nbytes = L.n * (L.k / 32) * qbl_block_bytes(L.qtype);
+      const int64_t nbytes = L.n * (L.k / qbl_block_weights(L.qtype)) * qbl_block_bytes(L.qtype);
       std::vector<uint8_t> blocks((size_t)nbytes);
       qbl::unpack_rows(L.qtype, buf.data(), buf.data() + L.qs_bytes, L.n, L.k, blocks.data());
       linear_digest(L.qtype, L.n, L.k, blocks.data(), nbytes, &digests[(size_t)i * 32]);
@@ -1064,10 +1068,12 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     tm.stop();
     if (glue) x = xin_buf;
   }
-  for (int qt = QBL_Q8_0; qt <= QBL_Q4_SM; ++qt) {
+  int launched = 0;  // linears given to a GEMV launch: all of them, or an error
+  for (int qt = QBL_Q8_0; qt <= QBL_Q4_K; ++qt) {
     qbl::GemvArgs a{};
     fill_segments(a, qt);
     if (!a.nseg) continue;
+    launched += a.nseg;
     a.qtype = qt;
     a.k = (int)K;
     a.batch = batch;
@@ -1080,6 +1086,7 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     if (e != hipSuccess) return hip_fail(e, "gemv launch");
     tm.stop();
   }
+  if (launched != nlin) return fail(QBL_E_FORMAT, "a linear of an unsupported type got no GEMV launch");
   return QBL_OK;
 }
 
@@ -1229,6 +1236,7 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
     std::lock_guard<std::mutex> g(comp->mu);
     auto L = std::atomic_load(&comp->list);
     const DevLinear& D = b->lin[(size_t)linear];
+    if (D.qtype == QBL_Q4_K) return fail(QBL_E_FORMAT, "the prefill path takes q8_0 and q4_sm bases");
     const int T = L->total_rank[(size_t)linear];
     if (qbl_status s = check_ws(ws, ws_bytes, align_up(qbl::jit_workspace_bytes((int)D.n, (int)D.k, T))))
       return s;

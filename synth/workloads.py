@@ -35,6 +35,9 @@ BLOCK_LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
 
 Q8_0 = 1
 Q4_SM = 2
+Q4_K = 3
+# canonical bytes and weights of one block, per quantisation type
+BLOCK = {Q8_0: (34, 32), Q4_SM: (20, 32), Q4_K: (144, 256)}
 
 
 @dataclass(frozen=True)
@@ -98,8 +101,8 @@ class Workload:
     # -- accounting (algorithmic bytes) ---------------------------------------
     def base_bytes(self, i: int) -> int:
         L = self.linears[i]
-        per_block = 34 if L.qtype == Q8_0 else 20
-        return L.n_out * (L.k_in // 32) * per_block
+        nbytes, nweights = BLOCK[L.qtype]
+        return L.n_out * (L.k_in // nweights) * nbytes
 
     def lora_bytes(self, i: int) -> int:
         L = self.linears[i]
@@ -132,9 +135,9 @@ def stack(d: int = 4096, h: int = 11008, n_blocks: int = 32, tokens: int = 256,
 
 
 def mlp70b(d: int = 8192, h: int = 28672, batch: int = 1, name: str = "mlp70b",
-           rank: int = 32) -> Workload:
-    lin = [LinearSpec(f"{name}/gate", h, d, Q4_SM), LinearSpec(f"{name}/up", h, d, Q4_SM),
-           LinearSpec(f"{name}/down", d, h, Q4_SM)]
+           rank: int = 32, qtype: int = Q4_SM) -> Workload:
+    lin = [LinearSpec(f"{name}/gate", h, d, qtype), LinearSpec(f"{name}/up", h, d, qtype),
+           LinearSpec(f"{name}/down", d, h, qtype)]
     return Workload(name, lin, [AdapterSpec("A1", rank, 1.0)], batch=batch)
 
 
@@ -156,6 +159,11 @@ def small_stack() -> Workload:
 
 def small_mlp(batch: int = 1) -> Workload:
     return mlp70b(d=640, h=1696, batch=batch, name=f"small_mlp_b{batch}")
+
+
+# The 70B-style MLP with a q4_K base (k a multiple of the 256-weight super-block).
+def mlp70b_q4k(batch: int = 1) -> Workload:
+    return mlp70b(batch=batch, name="mlp70b_q4k", qtype=Q4_K)
 
 
 def small_prefill() -> Workload:

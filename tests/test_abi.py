@@ -36,23 +36,29 @@ def test_every_declared_symbol_is_exported():
 def test_abi_version_and_block_bytes():
     assert q.qbl_abi_version() == 2
     assert q.qbl_block_bytes(q.QBL_Q8_0) == 34 and q.qbl_block_bytes(q.QBL_Q4_SM) == 20
-    assert q.qbl_block_bytes(7) == 0
+    assert q.qbl_block_bytes(q.QBL_Q4_K) == 144 and q.qbl_block_weights(q.QBL_Q4_K) == 256
+    assert q.qbl_block_weights(q.QBL_Q8_0) == q.qbl_block_weights(q.QBL_Q4_SM) == 32
+    assert q.qbl_block_bytes(7) == 0 and q.qbl_block_weights(7) == 0
 
 
-@pytest.mark.parametrize("qtype", [q.QBL_Q8_0, q.QBL_Q4_SM])
+@pytest.mark.parametrize("qtype", [q.QBL_Q8_0, q.QBL_Q4_SM, q.QBL_Q4_K])
 def test_library_quantiser_bytes_equal_oracle(qtype):
     rng = np.random.default_rng(40 + qtype)
-    w = (rng.standard_normal((300, 640)) * 0.02).astype(np.float32)
+    k = 768 if qtype == q.QBL_Q4_K else 640
+    w = (rng.standard_normal((300, k)) * 0.02).astype(np.float32)
     w[0, :32] = 0.0                                   # zero block
     w[1, 32:64] = np.float32(0.125)                   # constant block
     w[2, :32] = np.arange(32, dtype=np.float32) - 16  # exact grid
     w[3, :] *= 1e-6                                   # tiny scales (fp16 subnormal range)
     w[4, :] *= 100                                    # large values
+    w[5, :256] = 0.0                                  # zero super-block
+    w[6, :] = np.abs(w[6, :]) + 0.01                  # all positive (no offset)
+    w[7, :] = -np.abs(w[7, :]) - 0.01                 # all negative
     lib = q.qbl_quantize(qtype, w)
     ref = oracle.quantize(qtype, w)
-    assert np.array_equal(lib, ref)
-    deq = q.qbl_dequantize(qtype, lib, 300, 640)
-    assert np.array_equal(deq, oracle.dequantize(qtype, ref, 300, 640).astype(np.float32))
+    assert lib.shape == ref.shape and np.array_equal(lib, ref)
+    deq = q.qbl_dequantize(qtype, lib, 300, k)
+    assert np.array_equal(deq, oracle.dequantize(qtype, ref, 300, k).astype(np.float32))
 
 
 def test_library_quantiser_on_workload_tensors():

@@ -5,7 +5,7 @@ benchmark times:
 * 32-block stack, r16@1.0 then r64@0.5, 256 tokens: the free-running chain for the
   first tokens, teacher-forced tokens later on (the oracle fed the GPU's previous
   token), the swapped order, and the base hash;
-* 70B MLP linears (q4_sm, r32) at batch 1 and 8: sampled output rows;
+* 70B MLP linears (q4_sm and q4_K, r32) at batch 1 and 8: sampled output rows;
 * prefill M=512, K=4096 -> N=14336 (q8_0, r64) through JIT materialisation:
   sampled output columns for all 512 tokens, against the bf16 recipe and within
   the bf16 bound of the dual path.
@@ -108,11 +108,11 @@ def test_stack_32_blocks_256_tokens(torch_cuda):
         b.close()
 
 
-@pytest.mark.parametrize("batch", [1, 8])
-def test_mlp70b_q4_sampled_rows(torch_cuda, batch):
+@pytest.mark.parametrize("qtype,batch", [(2, 1), (2, 8), (3, 1), (3, 8)])
+def test_mlp70b_q4_sampled_rows(torch_cuda, qtype, batch):
     torch = torch_cuda
-    wl = workloads.mlp70b(batch=batch)
-    log(f"70B MLP q4_sm r32 batch {batch}: building")
+    wl = workloads.mlp70b(batch=batch) if qtype == 2 else workloads.mlp70b_q4k(batch=batch)
+    log(f"70B MLP {'q4_sm' if qtype == 2 else 'q4_K'} r32 batch {batch}: building")
     b = Built(wl)
     q = b.q
     try:

@@ -106,7 +106,9 @@ def test_one_hot_and_block_indicator_are_exact(torch_cuda):
 
 @pytest.mark.parametrize("qtype,n,k,batch", [
     (1, 1000, 4128, 1), (1, 333, 1056, 3), (1, 96, 12288, 1), (1, 130, 20480, 2),
-    (2, 1000, 4160, 1), (2, 257, 1088, 8), (2, 64, 28672, 1), (2, 40, 9216, 5)])
+    (2, 1000, 4160, 1), (2, 257, 1088, 8), (2, 64, 28672, 1), (2, 40, 9216, 5),
+    (3, 1000, 4096, 1), (3, 257, 1280, 8), (3, 96, 28672, 1), (3, 130, 11008, 3), (3, 40, 9216, 5),
+    (3, 33, 256, 2)])
 def test_ragged_shapes_and_batches(torch_cuda, qtype, n, k, batch):
     torch = torch_cuda
     wl = workloads.Workload(f"ragged_{qtype}_{n}_{k}_{batch}",
@@ -135,6 +137,29 @@ def test_ragged_shapes_and_batches(torch_cuda, qtype, n, k, batch):
             assert np.array_equal(_run(b, torch, 0, x2)[0], y0[0])
         for r in range(batch):
             assert rel_l2(_run(b, torch, 0, x[r:r + 1]), y0[r:r + 1]) <= 1e-5
+    finally:
+        b.close()
+
+
+def test_q4k_one_hot_inputs_give_dequantised_columns(torch_cuda):
+    """x = e_c: every product but one is an exact zero, so each output is the
+    float32 rounding of D*q - M, the dequantised weight, at batch 1 and 4."""
+    torch = torch_cuda
+    n, k = 200, 768
+    wl = workloads.Workload("onehot_q4k", [workloads.LinearSpec("onehot/q4k", n, k, 3)],
+                            [workloads.AdapterSpec("A1", 8, 1.0)])
+    b = Built(wl)
+    try:
+        deq = oracle.dequantize(3, b.or_blocks[0], n, k).astype(np.float32)
+        cols = [0, 31, 32, 255, 256, 300, 511, 767]
+        for batch in (1, 4):
+            for i in range(0, len(cols), batch):
+                x = np.zeros((batch, k), np.float32)
+                for r, c in enumerate(cols[i:i + batch]):
+                    x[r, c] = 1.0
+                y = _run(b, torch, 0, x)
+                for r, c in enumerate(cols[i:i + batch]):
+                    assert np.array_equal(y[r], deq[:, c]), (batch, c)
     finally:
         b.close()
 
