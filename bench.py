@@ -15,6 +15,7 @@ Also reported on the same JSON line:
   cpu_baseline  the float64 C oracle on the host cores, same workload
   stack         32 such blocks, two adapters (r16@1.0 then r64@0.5), 256 tokens
   q4_mlp        70B-style q4_sm MLP linears at batch 1 and 8
+  q4k_mlp       the same MLP with a q4_K (256-weight super-block) base
   prefill       the JIT-materialisation prefill GEMM (when available)
   stack.lifecycle  load (staging + verification + digest), attach, rollback and
                 base-hash costs on the stack
@@ -275,10 +276,9 @@ def bench_lifecycle(q, base, ads, comp, timing, hash_s):
     return out
 
 
-def bench_q4(torch, q, workloads, args):
+def bench_q4(torch, q, wl, args, label):
     out = {}
-    wl = workloads.mlp70b()
-    log("[q4] building 70B MLP linears (q4_sm, r32)")
+    log(f"[{label}] building 70B MLP linears ({label}, r32)")
     base, ads, comp, _ = build_copies(q, wl, 1, [0])
     for batch in (1, 8):
         xs = [torch.from_numpy(wl.x(i, batch)).cuda() for i in range(3)]
@@ -295,7 +295,7 @@ def bench_q4(torch, q, workloads, args):
         gbs = byts / (ms * 1e-3) / 1e9
         out[f"batch{batch}"] = {"us_per_mlp": round(ms * 1e3, 1), "GB_per_s": round(gbs, 1),
                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": byts}
-        log(f"[q4] batch {batch}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+        log(f"[{label}] batch {batch}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
     free_all(q, base, ads, comp)
     return out
 
@@ -376,7 +376,8 @@ def main():
     }
     if not args.no_extras:
         result["stack"] = bench_stack(torch, q, workloads, args)
-        result["q4_mlp"] = bench_q4(torch, q, workloads, args)
+        result["q4_mlp"] = bench_q4(torch, q, workloads.mlp70b(), args, "q4_sm")
+        result["q4k_mlp"] = bench_q4(torch, q, workloads.mlp70b_q4k(), args, "q4_K")
         result["prefill"] = bench_prefill(torch, q, workloads, args)
     import oracle
     log("[cpu] timing the oracle")

@@ -17,6 +17,14 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// The value of lane (i of the quad) in every lane of each 4-lane quad:
+// quad_perm [i,i,i,i] (0x00, 0x55, 0xAA, 0xFF).  All four lanes of a quad must be
+// active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -83,15 +91,15 @@ __device__ __forceinline__ float4 mul4(float c, float4 a) {
 // lanes served together by an LDS read touch different bank groups.
 //
 // Scale data per chunk (Sc): q8_0 the block's fp16 d, q4_sm the block's
-// (d | m << 16); q4_K the whole 16-byte header of the chunk's super-block (the
-// 8 lanes of one super-block read the same 16 bytes: one cache line per 64
-// lanes), from which the chunk's step and offset are decoded.
+// (d | m << 16); q4_K dword (c & 3) of the chunk's 16-byte super-block header:
+// the 4 lanes of a quad (consecutive chunks of one super-block) hold the whole
+// header between them, and DPP quad broadcasts give every lane all of it.
 // ---------------------------------------------------------------------------
 template <int QT>
 struct Fmt {
   static constexpr int kWeightsPerChunk = QT == QBL_FMT_Q8 ? 16 : 32;
   static constexpr int kSlots = kWeightsPerChunk / 4;
-  using Sc = std::conditional_t<QT == QBL_FMT_Q4K, uint4, uint32_t>;
+  using Sc = uint32_t;
   __device__ static __forceinline__ int slot(int c, int j) {
     return (j + (QT == QBL_FMT_Q8 ? (c >> 1) : c)) & (kSlots - 1);
   }
@@ -102,10 +110,8 @@ struct Fmt {
       return reinterpret_cast<const uint16_t*>(sc)[(int64_t)row * (k / 32) + (c >> 1)];
     else if constexpr (QT == QBL_FMT_Q4)
       return reinterpret_cast<const uint32_t*>(sc)[(int64_t)row * (k / 32) + c];
-    else {
-      const u32x4 v = *gp(reinterpret_cast<const u32x4*>(sc) + (int64_t)row * (k / 256) + (c >> 3));
-      return make_uint4(v.x, v.y, v.z, v.w);
-    }
+    else  // dword (c & 3) of the super-block header; the quad's 4 lanes hold all four
+      return reinterpret_cast<const uint32_t*>(sc)[((int64_t)row * (k / 256) + (c >> 3)) * 4 + (c & 3)];
   }
 };
 
@@ -176,8 +182,10 @@ __device__ __forceinline__ float chunk_dot(float p, const uint4 q, const float4*
     p = fmaf(h2f(sc), dot_q4(q, xv), p);
     return fmaf(h2f(sc >> 16), xsum, p);
   } else {
+    const uint4 h = make_uint4(quad_bcast<0x00>(sc), quad_bcast<0x55>(sc), quad_bcast<0xAA>(sc),
+                               quad_bcast<0xFF>(sc));
     float D, M;
-    q4k_step_offset(sc, c & 7, D, M);
+    q4k_step_offset(h, c & 7, D, M);
     p = fmaf(D, dot_q4(q, xv), p);
     return fmaf(-M, xsum, p);
   }

@@ -416,7 +416,10 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   for (int u = 0; u < CPW; ++u) {
     const int c = 64 * (u * W + wave) + lane;
     cval[u] = c < CT;
-    cidx[u] = min(c, CT - 1);
+    // lanes past the row end read a valid chunk (their inputs are zero); for
+    // q4_K the same lane of the last super-block, so that every quad still
+    // holds one whole header (CT is a multiple of 8 there)
+    cidx[u] = c < CT ? c : QT == QBL_FMT_Q4K ? CT - 8 + (lane & 7) : CT - 1;
   }
 
   // ---- the workgroup's rows (GEMV role)
