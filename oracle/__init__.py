@@ -29,7 +29,8 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 
 class _Lora(ctypes.Structure):
     _fields_ = [("rank", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p)]
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("row_ptr", ctypes.c_void_p), ("col", ctypes.c_void_p), ("val", ctypes.c_void_p)]
 
 
 class _Linear(ctypes.Structure):
@@ -172,11 +173,31 @@ class Lora:
         return self.A.shape[0]
 
 
+class Sparse:
+    """One sparse delta on one linear, CSR: row_ptr (n+1), col, fp16 value bits, scale."""
+
+    def __init__(self, row_ptr, col, val_f16_bits, scale: float):
+        self.row_ptr = _c(row_ptr, np.uint32)
+        self.col = _c(col, np.uint32)
+        self.val = _c(val_f16_bits, np.uint16)
+        self.scale = float(scale)
+        assert self.col.size == self.val.size == int(self.row_ptr[-1])
+        # non-empty buffers, so that their pointers are never NULL
+        self._keep = [np.zeros(1, np.uint32), np.zeros(1, np.uint16)]
+
+    rank = 0
+
+
 def _lora_array(ads):
     arr = (_Lora * max(1, len(ads)))()
     for i, a in enumerate(ads):
         arr[i].rank, arr[i].scale = a.rank, a.scale
-        arr[i].A, arr[i].B = a.A.ctypes.data, a.B.ctypes.data
+        if a.rank == 0:
+            arr[i].row_ptr = a.row_ptr.ctypes.data
+            arr[i].col = (a.col if a.col.size else a._keep[0]).ctypes.data
+            arr[i].val = (a.val if a.val.size else a._keep[1]).ctypes.data
+        else:
+            arr[i].A, arr[i].B = a.A.ctypes.data, a.B.ctypes.data
     return arr
 
 

@@ -425,9 +425,14 @@ static void dual_row(void* vc, int64_t i, double* wrow) {
     int64_t off = 0;
     for (int32_t a = 0; a < c->n_ads; ++a) {
       const or_lora* ad = &c->ads[a];
-      const double* tb = c->t + off + (int64_t)b * ad->rank;
       double e = 0.0;
-      for (int32_t j = 0; j < ad->rank; ++j) e += (double)ad->B[r * ad->rank + j] * tb[j];
+      if (ad->rank == 0) { /* sparse delta: S[r] . x */
+        for (uint32_t p = ad->row_ptr[r]; p < ad->row_ptr[r + 1]; ++p)
+          e += (double)or_f32_from_f16(ad->val[p]) * xb[ad->col[p]];
+      } else {
+        const double* tb = c->t + off + (int64_t)b * ad->rank;
+        for (int32_t j = 0; j < ad->rank; ++j) e += (double)ad->B[r * ad->rank + j] * tb[j];
+      }
       acc += (double)ad->scale * e;
       off += (int64_t)c->batch * ad->rank;
     }
@@ -441,8 +446,17 @@ static int32_t check_lin(int32_t qtype, const uint8_t* blocks, int64_t n, int64_
       n_ads < 0)
     return -1;
   if (n_ads && !ads) return -1;
-  for (int32_t a = 0; a < n_ads; ++a)
-    if (ads[a].rank <= 0 || !ads[a].A || !ads[a].B) return -1;
+  for (int32_t a = 0; a < n_ads; ++a) {
+    if (ads[a].rank < 0) return -1;
+    if (ads[a].rank > 0 && (!ads[a].A || !ads[a].B)) return -1;
+    if (ads[a].rank == 0) {
+      if (!ads[a].row_ptr || (ads[a].row_ptr[n] && (!ads[a].col || !ads[a].val))) return -1;
+      for (int64_t r = 0; r < n; ++r)
+        if (ads[a].row_ptr[r] > ads[a].row_ptr[r + 1]) return -1;
+      for (uint32_t p = 0; p < ads[a].row_ptr[n]; ++p)
+        if ((int64_t)ads[a].col[p] >= k) return -1;
+    }
+  }
   if (!rows && n_rows != n) return -1;
   if (rows)
     for (int64_t i = 0; i < n_rows; ++i)
@@ -474,6 +488,9 @@ static void weff_row_f64(const lin_ctx* c, int64_t r, double* wrow) {
   dequant_row(c->qtype, c->blocks, r, c->k, wrow);
   for (int32_t a = 0; a < c->n_ads; ++a) {
     const or_lora* ad = &c->ads[a];
+    if (ad->rank == 0)
+      for (uint32_t p = ad->row_ptr[r]; p < ad->row_ptr[r + 1]; ++p)
+        wrow[ad->col[p]] += (double)ad->scale * (double)or_f32_from_f16(ad->val[p]);
     for (int32_t j = 0; j < ad->rank; ++j) {
       const double sb = (double)ad->scale * (double)ad->B[r * ad->rank + j];
       const float* arow = ad->A + (int64_t)j * c->k;
@@ -519,6 +536,9 @@ static void jit_row(void* vc, int64_t i, double* acc) {
   for (int64_t kk = 0; kk < c->k; ++kk) acc[kk] = (double)(float)acc[kk]; /* float32(deq) */
   for (int32_t a = 0; a < c->n_ads; ++a) {
     const or_lora* ad = &c->ads[a];
+    if (ad->rank == 0)
+      for (uint32_t p = ad->row_ptr[r]; p < ad->row_ptr[r + 1]; ++p)
+        acc[ad->col[p]] += (double)(ad->scale * or_f32_from_f16(ad->val[p]));
     for (int32_t j = 0; j < ad->rank; ++j) {
       const float sb32 = ad->scale * ad->B[r * ad->rank + j];
       const double sb = (double)or_f32_from_bf16(or_bf16_from_f32(sb32));

@@ -46,18 +46,27 @@ int32_t or_quantize(int32_t qtype, const float* w, int64_t n, int64_t k, uint8_t
 /* Dequantise to float64 (exact for both formats). */
 int32_t or_dequantize(int32_t qtype, const uint8_t* blocks, int64_t n, int64_t k, double* out);
 
-/* One LoRA adapter on one linear: A is rank x k_in, B is n_out x rank, both
- * row-major float32; scale is the single effective multiplier (alpha/r folded). */
+/* One adapter on one linear, applied with the single effective multiplier
+ * `scale` (alpha/r folded).
+ * rank >= 1: a LoRA pair, A rank x k_in and B n_out x rank, row-major float32.
+ * rank == 0: a sparse delta S (n_out x k_in) in CSR form (the design page's
+ *   "Sparse Overlay Bytes": 4-byte indices, 2-byte f16 values): row r holds
+ *   entries row_ptr[r] .. row_ptr[r+1]-1 with columns col[] and fp16 values
+ *   val[] (bit patterns).  A and B are unused. */
 typedef struct {
   int32_t rank;
   float scale;
   const float* A;
   const float* B;
+  const uint32_t* row_ptr;
+  const uint32_t* col;
+  const uint16_t* val;
 } or_lora;
 
 /* Dual path, float64:
  *   y[b][i] = sum_k deq(W)[row_i][k] x[b][k]
- *           + sum_a scale_a * sum_j B_a[row_i][j] * (sum_k A_a[j][k] x[b][k])
+ *           + sum_a scale_a * sum_j B_a[row_i][j] * (sum_k A_a[j][k] x[b][k])   (LoRA)
+ *           + sum_a scale_a * sum_p val_a[p] x[b][col_a[p]]  over row_i's entries (sparse)
  * with the base sum completed first and the adapters added in list order.
  * x is batch x k (float64).  rows lists the output rows to compute (NULL with
  * n_rows = n means all rows); y is batch x n_rows.  nthreads <= 0 picks the
@@ -75,7 +84,8 @@ int32_t or_linear_materialised(int32_t qtype, const uint8_t* blocks, int64_t n, 
 
 /* Per-layer just-in-time materialisation in bfloat16:
  *   weff[i][k] = bf16( f32(deq(W)[row_i][k])
- *                      + sum_a sum_j bf16(f32(scale_a*B_a[row_i][j])) * bf16(A_a[j][k]) )
+ *                      + sum_a sum_j bf16(f32(scale_a*B_a[row_i][j])) * bf16(A_a[j][k])   (LoRA)
+ *                      + sum_a f32(scale_a * val_a) at (row_i, col_a)                      (sparse) )
  * with the sum formed exactly (float64) and rounded once. weff is n_rows x k. */
 int32_t or_jit_weff(int32_t qtype, const uint8_t* blocks, int64_t n, int64_t k,
                     const or_lora* ads, int32_t n_ads, const int64_t* rows, int64_t n_rows,

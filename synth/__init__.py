@@ -39,6 +39,8 @@ def _load():
         lib.synth_splitmix64_at.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
         lib.synth_seed_from_tag.restype = ctypes.c_uint64
         lib.synth_seed_from_tag.argtypes = [ctypes.c_char_p]
+        lib.synth_uniform_f64.restype = ctypes.c_int
+        lib.synth_uniform_f64.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
         lib.synth_normal_f32.restype = ctypes.c_int
         lib.synth_normal_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
                                          ctypes.c_double, ctypes.c_double,
@@ -73,4 +75,14 @@ def normal(tag, shape, mean: float = 0.0, std: float = 1.0, offset: int = 0,
                                   out.ctypes.data, int(nthreads))
     if rc != 0:
         raise RuntimeError("synth_normal_f32 failed")
+    return out
+
+
+def uniform(tag, shape, offset: int = 0) -> np.ndarray:
+    """float64 array of uniform [0, 1) draws (53-bit) of the stream named by ``tag``."""
+    s = seed(tag) if isinstance(tag, str) else int(tag)
+    shape = tuple(int(v) for v in (shape if isinstance(shape, (tuple, list)) else (shape,)))
+    out = np.empty(shape, dtype=np.float64)
+    if _load().synth_uniform_f64(s, int(offset), out.size, out.ctypes.data) != 0:
+        raise RuntimeError("synth_uniform_f64 failed")
     return out

@@ -109,3 +109,10 @@ int synth_normal_f32(uint64_t seed, uint64_t offset, uint64_t count, double mean
     if (ok[t]) pthread_join(th[t], NULL);
   return 0;
 }
+
+int synth_uniform_f64(uint64_t seed, uint64_t offset, uint64_t count, double* out) {
+  if (!out && count) return -1;
+  for (uint64_t i = 0; i < count; ++i)
+    out[i] = (double)(synth_splitmix64_at(seed, offset + i) >> 11) * 0x1p-53;
+  return 0;
+}

@@ -16,6 +16,8 @@ uint64_t synth_seed_from_tag(const char* tag);
  * by OMP_NUM_THREADS).  Returns 0, or -1 on a null output. */
 int synth_normal_f32(uint64_t seed, uint64_t offset, uint64_t count, double mean, double std,
                      float* out, int nthreads);
+/* out[i] = the 53-bit uniform in [0, 1) of draw offset+i of the stream. */
+int synth_uniform_f64(uint64_t seed, uint64_t offset, uint64_t count, double* out);
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import normal
+from . import normal, uniform
 
 BLOCK_LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -43,8 +43,9 @@ BLOCK = {Q8_0: (34, 32), Q4_SM: (20, 32), Q4_K: (144, 256)}
 @dataclass(frozen=True)
 class AdapterSpec:
     name: str          # stream name of this adapter ("A1", "A2", ...)
-    rank: int
+    rank: int          # 0 for a sparse (DARE) delta
     scale: float
+    density: float = 0.0   # sparse deltas: fraction of entries kept
 
 
 @dataclass(frozen=True)
@@ -84,6 +85,20 @@ class Workload:
         L, ad = self.linears[i], self.adapters[a]
         return normal(L.tag + "/" + ad.name + "/B", (L.n_out, ad.rank), 0.0, 0.01)
 
+    def sparse_csr(self, i: int, a: int):
+        """A DARE-style sparse delta for linear i: a dense N(0, 0.001) delta, each
+        entry kept with probability `density` and rescaled by 1/density, stored as
+        CSR (row_ptr uint32 [n+1], col uint32 [nnz], val fp16 bits uint16 [nnz])."""
+        L, ad = self.linears[i], self.adapters[a]
+        tag = L.tag + "/" + ad.name
+        keep = uniform(tag + "/keep", (L.n_out, L.k_in)) < ad.density
+        vals = normal(tag + "/delta", (L.n_out, L.k_in), 0.0, 0.001)
+        rows, cols = np.nonzero(keep)
+        val16 = (vals[rows, cols] / np.float32(ad.density)).astype(np.float16).view(np.uint16)
+        row_ptr = np.zeros(L.n_out + 1, np.uint32)
+        np.cumsum(np.bincount(rows, minlength=L.n_out), out=row_ptr[1:])
+        return row_ptr, cols.astype(np.uint32), val16
+
     def x(self, i: int = 0, batch: int | None = None) -> np.ndarray:
         """Activations for linear i (fresh per linear), batch x k_in."""
         L = self.linears[i]
@@ -105,6 +120,7 @@ class Workload:
         return L.n_out * (L.k_in // nweights) * nbytes
 
     def lora_bytes(self, i: int) -> int:
+        """Bytes of the low-rank adapters of linear i (sparse deltas: sparse_bytes)."""
         L = self.linears[i]
         return sum(4 * ad.rank * (L.n_out + L.k_in) for ad in self.adapters)
 
