@@ -222,9 +222,38 @@ typedef struct {
 qbl_status qbl_adapter_load(qbl_base* base, const qbl_lora_desc* descs, int32_t n,
                             qbl_adapter** out);
 
+/* One sparse delta S on one linear of the base (n_out x k_in), in CSR form
+ * ([design] "Sparse Overlay Bytes": DARE-masked task vectors stored as 4-byte
+ * indices and 2-byte f16 values; [overlay] "Runtime Strategy Comparison
+ * Matrix": a sparse overlay adds values only at its indices).  All host:
+ *   row_ptr: n_out + 1 uint32, row_ptr[0] = 0, non-decreasing, row_ptr[n_out] = nnz;
+ *   col:     nnz uint32 column indices, strictly increasing within each row, < k_in;
+ *   val:     nnz fp16 bit patterns, finite.
+ * col and val may be NULL when nnz = 0. */
+typedef struct {
+  int32_t linear;
+  int32_t reserved; /* must be 0 */
+  int64_t nnz;
+  const uint32_t* row_ptr;
+  const uint32_t* col;
+  const uint16_t* val;
+} qbl_sparse_desc;
+
+/* Validate, stage and verify a sparse adapter touching n >= 1 linears (no
+ * linear twice), like qbl_adapter_load.  The deep checks of [design] section
+ * 11 are applied to every entry: row_ptr from 0 to nnz and non-decreasing
+ * (QBL_E_SHAPE), columns inside the row (QBL_E_SHAPE) and strictly increasing
+ * within each row (QBL_E_FORMAT), values finite (QBL_E_NONFINITE).  On the
+ * decode path the adapter adds scale * (S x) to the output, in list order with
+ * the other adapters; the prefill path refuses lists holding one
+ * (QBL_E_FORMAT).  *out receives the handle, used like any other adapter. */
+qbl_status qbl_adapter_load_sparse(qbl_base* base, const qbl_sparse_desc* descs, int32_t n,
+                                   qbl_adapter** out);
+
 /* SHA-256 of the adapter content: over the concatenation, in entry order, of
- * each entry's SHA-256 over [int32 linear][int32 rank] (little-endian) followed
- * by A's and then B's float32 bytes. */
+ * each entry's SHA-256 over, little-endian, [int32 linear][int32 rank] followed
+ * by A's and then B's float32 bytes (low-rank), or [int32 linear][int32 -1]
+ * [int64 nnz] followed by row_ptr, col and val (sparse). */
 qbl_status qbl_adapter_digest(const qbl_adapter* adapter, uint8_t sha256_out[32]);
 
 /* Drop the caller's reference.  Device memory lives on while an attached list
@@ -335,7 +364,8 @@ qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index, 
  * batch-one GEMV, kernels fused so adapter rows are used as the base block is
  * consumed; section 9: weighted adapters added at the final accumulation).
  *   y[b][n] = sum_k deq(W)[n][k] x[b][k] + sum_i s_i sum_j B_i[n][j] t_i[b][j],
- *   t_i[b] = A_i x[b],
+ *   t_i[b] = A_i x[b]   (a sparse adapter i adds s_i sum_p val_i[p] x[b][col_i[p]]
+ *   over row n's entries instead),
  * base sum first, adapters in list order, float32 accumulation.
  * x: device float32 batch x k_in; y: device float32 batch x n_out (must not
  * alias x); 1 <= batch <= QBL_MAX_BATCH.  Results are deterministic: the same

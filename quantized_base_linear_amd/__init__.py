@@ -65,6 +65,11 @@ class qbl_lora_desc(ctypes.Structure):
                 ("B", ctypes.c_void_p)]
 
 
+class qbl_sparse_desc(ctypes.Structure):
+    _fields_ = [("linear", ctypes.c_int32), ("reserved", ctypes.c_int32), ("nnz", ctypes.c_int64),
+                ("row_ptr", ctypes.c_void_p), ("col", ctypes.c_void_p), ("val", ctypes.c_void_p)]
+
+
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 _PP = ctypes.POINTER(ctypes.c_void_p)
 EXPORTS = {
@@ -84,6 +89,7 @@ EXPORTS = {
     "qbl_base_set_budget": (_i32, [_vp, _i64]),
     "qbl_base_memory": (_i32, [_vp, _vp, _vp]),
     "qbl_adapter_load": (_i32, [_vp, _vp, _i32, _PP]),
+    "qbl_adapter_load_sparse": (_i32, [_vp, _vp, _i32, _PP]),
     "qbl_adapter_digest": (_i32, [_vp, _vp]),
     "qbl_adapter_free": (_i32, [_vp]),
     "qbl_comp_create": (_i32, [_vp, _PP]),
@@ -243,6 +249,22 @@ class Library:
             descs[i].A, descs[i].B = A.ctypes.data, B.ctypes.data
         h = ctypes.c_void_p()
         self._check(self._lib.qbl_adapter_load(base, ctypes.addressof(descs), len(entries), ctypes.byref(h)))
+        return h.value
+
+    def qbl_adapter_load_sparse(self, base, entries) -> int:
+        """entries: sequence of (linear, row_ptr uint32 (n_out+1), col uint32, val fp16 bits uint16)."""
+        keep = [(_host(rp, np.uint32), _host(c, np.uint32), _host(v, np.uint16)) for (_, rp, c, v) in entries]
+        descs = (qbl_sparse_desc * max(1, len(entries)))()
+        for i, ((lin, _, _, _), (rp, c, v)) in enumerate(zip(entries, keep)):
+            if c.size != v.size:
+                raise ValueError("one value per column index")
+            descs[i].linear, descs[i].reserved, descs[i].nnz = lin, 0, c.size
+            descs[i].row_ptr = rp.ctypes.data
+            descs[i].col = c.ctypes.data if c.size else None
+            descs[i].val = v.ctypes.data if v.size else None
+        h = ctypes.c_void_p()
+        self._check(self._lib.qbl_adapter_load_sparse(base, ctypes.addressof(descs), len(entries),
+                                                      ctypes.byref(h)))
         return h.value
 
     def qbl_adapter_digest(self, adapter) -> bytes:

@@ -318,6 +318,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
       float v = acc[r][b];
       for (int i = 0; i < n_ad; ++i) {
         const int rk = g.lora.rank[i];
+        if (rk == 0) {  // sparse delta: lanes strided over the row's entries
+          const float* xb = a.x + (int64_t)b * a.x_stride;
+          const uint32_t e1 = g.lora.rp[i][row + 1];
+          float p = 0.0f;
+          for (uint32_t e = g.lora.rp[i][row] + lane; e < e1; e += 64) p = fmaf(h2f(g.lora.sv[i][e]), xb[g.lora.ci[i][e]], p);
+          v = fmaf(g.lora.scale[i], p, v);
+          continue;
+        }
         const float* ti = ts + b * T + g.lora.toff[i];
         if (prefetch) {
           const float bv = i == 0 ? bpre[r][0] : bpre[r][1];
@@ -401,6 +409,7 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   __shared__ float ssred[W];
   __shared__ float tl[kB1MaxT];
   __shared__ float outl[kB1MaxSlots];
+  __shared__ float spl[kMaxAdapters][kB1MaxSlots];  // sparse deltas' S x per adapter and slot
 
   const GemvArgs& a = f.g;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -608,6 +617,31 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
       tl[j] = (uint32_t)(tw[m] >> 32) == f.tag ? __uint_as_float((uint32_t)tw[m]) : tagged_get(tcopy + j, f.tag, f.spin_limit);
   }
   for (int j = tid + kTW * NT; j < f.rows_total; j += NT) tl[j] = tagged_get(tcopy + j, f.tag, f.spin_limit);
+
+  // ---- sparse deltas: a wave per output row, its lanes strided over the row's
+  // entries, gathering the unscaled input s = v0 + v1 + v2 (the RMS factor is
+  // applied with the rest below); one wave reduction per row and adapter
+  if (f.has_sparse) {
+    for (int s = wave; s < nslots; s += W) {
+      const GemvSeg& g = a.seg[slot_seg(s)];
+      const int row = slot_row(s);
+      if (row >= g.n) continue;
+      for (int i = 0; i < g.lora.n_ad; ++i) {
+        if (g.lora.rank[i] != 0) continue;
+        const uint32_t e1 = g.lora.rp[i][row + 1];
+        float p = 0.0f;
+        for (uint32_t e = g.lora.rp[i][row] + lane; e < e1; e += 64) {
+          const uint32_t c = g.lora.ci[i][e];
+          float xv = f.v[0][c];
+          if (f.nv > 1) xv += f.v[1][c];
+          if (f.nv > 2) xv += f.v[2][c];
+          p = fmaf(h2f(g.lora.sv[i][e]), xv, p);
+        }
+        p = wave_sum(p);
+        if (lane == 0) spl[i][s] = p;
+      }
+    }
+  }
   __syncthreads();
   if (tid < nslots) {
     const int s = tid;
@@ -619,6 +653,10 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
     v *= cscale;
     for (int i = 0; i < g.lora.n_ad; ++i) {
       const int rk = g.lora.rank[i];
+      if (rk == 0) {
+        v = fmaf(g.lora.scale[i], cscale * spl[i][s], v);
+        continue;
+      }
       const float* ti = tl + g.lora.toff[i];
       const float* Br = g.lora.B[i] + (int64_t)min(row, g.n - 1) * rk;
       float p = 0.0f;
@@ -817,7 +855,7 @@ hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc) {
     LoraSeg& L = a.seg[i].lora;
     L.prefetch = L.n_ad <= kPrefetchAdapters;
     for (int j = 0; j < L.n_ad; ++j)
-      if (L.rank[j] > 64) L.prefetch = 0;
+      if (L.rank[j] > 64 || L.rank[j] == 0) L.prefetch = 0;
   }
   switch (a.qtype) {
     case QBL_FMT_Q8: return launch_batch<QBL_FMT_Q8>(a, bb, cpl, lc);

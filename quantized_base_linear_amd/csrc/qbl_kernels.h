@@ -25,7 +25,9 @@ constexpr int kMaxAdapters = 8;
 constexpr int kMaxSegs = 3;                        // linears sharing one input in one launch
 constexpr int kMaxPrepEntries = kMaxSegs * kMaxAdapters;
 
-// The adapters of one linear in list order, as the expand needs them.
+// The adapters of one linear in list order, as the expand needs them.  An
+// entry of rank 0 is a sparse delta: row r's entries are rp[r] .. rp[r+1]-1,
+// with columns ci[] and fp16 values sv[] (its toff and B are unused).
 struct LoraSeg {
   int n_ad;
   int prefetch;              // set by launch_gemv: B rows loaded up front
@@ -33,6 +35,9 @@ struct LoraSeg {
   int rank[kMaxAdapters];
   float scale[kMaxAdapters];
   const float* B[kMaxAdapters];  // n_out x rank, row-major
+  const uint32_t* rp[kMaxAdapters];
+  const uint32_t* ci[kMaxAdapters];
+  const uint16_t* sv[kMaxAdapters];
 };
 
 // One linear of a fused GEMV launch.
@@ -99,6 +104,7 @@ struct FusedArgs {
   int rows_per_wg;     // set by the launcher
   int n_ent;
   int rows_total;      // A rows = shrink results
+  int has_sparse;      // 1: some segment has a sparse delta
   int shrink_wgs;      // set by the launcher
   int spin_limit;      // bound on the sleeps of one wait for a shrink result
   uint32_t tag;        // this launch's number, never 0

@@ -86,11 +86,16 @@ struct qbl_base {
   int64_t budget = 0;       // 0 = no cap
 };
 
+// One linear of an adapter: a LoRA pair (rank >= 1) or a sparse delta (rank 0).
 struct AdEntry {
   int linear;
   int rank;
   float* A;  // device rank x k
   float* B;  // device n x rank
+  uint32_t* rp = nullptr;  // sparse: device row_ptr [n+1], col [nnz], fp16 val [nnz]
+  uint32_t* ci = nullptr;
+  uint16_t* sv = nullptr;
+  int64_t nnz = 0;
 };
 
 struct AdapterImpl {
@@ -123,8 +128,11 @@ struct qbl_adapter {
 struct LoraRef {
   const float* A;
   const float* B;
-  int rank;
+  int rank;  // 0: sparse delta (rp, ci, sv)
   float scale;
+  const uint32_t* rp;
+  const uint32_t* ci;
+  const uint16_t* sv;
 };
 
 // One attached list.  Immutable once published; freed when no composition or
@@ -615,6 +623,127 @@ extern "C" qbl_status qbl_adapter_load(qbl_base* base, const qbl_lora_desc* desc
   })
 }
 
+namespace {
+
+// The deep checks of one sparse entry ([design] section 11: strictly monotonic
+// indices, finite f16 payloads, dimensions that match).
+qbl_status check_sparse(const qbl_sparse_desc& d, int64_t n, int64_t k, int i) {
+  if (!d.row_ptr) return fail(QBL_E_ARG, "entry %d: null row_ptr", i);
+  if (d.nnz < 0 || d.nnz > n * k || d.nnz > (int64_t)UINT32_MAX)
+    return fail(QBL_E_SHAPE, "entry %d: %lld entries for a %lld x %lld linear", i, (long long)d.nnz,
+                (long long)n, (long long)k);
+  if (d.nnz > 0 && (!d.col || !d.val)) return fail(QBL_E_ARG, "entry %d: null col or val", i);
+  if (d.reserved != 0) return fail(QBL_E_ARG, "entry %d: reserved field must be 0", i);
+  if (d.row_ptr[0] != 0 || (int64_t)d.row_ptr[n] != d.nnz)
+    return fail(QBL_E_SHAPE, "entry %d: row_ptr must run from 0 to nnz", i);
+  // row_ptr first, so that the column pass below never reads past nnz
+  for (int64_t r = 0; r < n; ++r)
+    if (d.row_ptr[r + 1] < d.row_ptr[r])
+      return fail(QBL_E_SHAPE, "entry %d: row_ptr decreases at row %lld", i, (long long)r);
+  for (int64_t r = 0; r < n; ++r) {
+    const uint32_t p0 = d.row_ptr[r], p1 = d.row_ptr[r + 1];
+    for (uint32_t p = p0; p < p1; ++p) {
+      if ((int64_t)d.col[p] >= k)
+        return fail(QBL_E_SHAPE, "entry %d: column %u of row %lld outside 0..%lld", i, d.col[p],
+                    (long long)r, (long long)k - 1);
+      if (p > p0 && d.col[p] <= d.col[p - 1])
+        return fail(QBL_E_FORMAT, "entry %d: columns of row %lld not strictly increasing", i, (long long)r);
+    }
+  }
+  for (int64_t p = 0; p < d.nnz; ++p)
+    if ((d.val[p] & 0x7C00u) == 0x7C00u) return fail(QBL_E_NONFINITE, "entry %d: value %lld is not finite", i, (long long)p);
+  return QBL_OK;
+}
+
+}  // namespace
+
+extern "C" qbl_status qbl_adapter_load_sparse(qbl_base* base, const qbl_sparse_desc* descs, int32_t n,
+                                              qbl_adapter** out) {
+  QBL_TRY({
+    if (!base || !descs || !out) return fail(QBL_E_ARG, "null pointer");
+    if (n <= 0) return fail(QBL_E_ARG, "an adapter must target at least one linear");
+    if (qbl_status s = check_device(base)) return s;
+    // -- validation
+    const int nl = (int)base->lin.size();
+    std::vector<char> seen((size_t)nl, 0);
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+      const qbl_sparse_desc& d = descs[i];
+      if (d.linear < 0 || d.linear >= nl)
+        return fail(QBL_E_SHAPE, "entry %d targets linear %d; the base has %d", i, d.linear, nl);
+      if (seen[(size_t)d.linear]) return fail(QBL_E_DUPLICATE, "linear %d appears twice", d.linear);
+      seen[(size_t)d.linear] = 1;
+      const DevLinear& L = base->lin[(size_t)d.linear];
+      if (qbl_status s = check_sparse(d, L.n, L.k, i)) return s;
+      total += align_up(4 * (L.n + 1)) + align_up(4 * d.nnz) + align_up(2 * d.nnz);
+    }
+    // -- allocation within the budget
+    auto impl = std::make_shared<AdapterImpl>();
+    impl->base = base;
+    base->refs.fetch_add(1);
+    {
+      std::lock_guard<std::mutex> g(base->mem_mu);
+      if (base->budget > 0 && base->held + total > base->budget)
+        return fail(QBL_E_BUDGET, "adapter needs %lld bytes; %lld of the budget of %lld are held",
+                    (long long)total, (long long)base->held, (long long)base->budget);
+      base->held += total;
+      impl->reserved = total;
+    }
+    hipError_t e = dev_alloc(&impl->mem, total);
+    if (e != hipSuccess)
+      return fail(QBL_E_NOMEM, "device allocation of %lld bytes: %s", (long long)total, hipGetErrorString(e));
+    impl->slot.assign((size_t)nl, -1);
+    uint8_t* p = static_cast<uint8_t*>(impl->mem);
+    for (int i = 0; i < n; ++i) {
+      const qbl_sparse_desc& d = descs[i];
+      const DevLinear& L = base->lin[(size_t)d.linear];
+      AdEntry en{d.linear, 0, nullptr, nullptr};
+      en.nnz = d.nnz;
+      en.rp = reinterpret_cast<uint32_t*>(p);
+      p += align_up(4 * (L.n + 1));
+      en.ci = reinterpret_cast<uint32_t*>(p);
+      p += align_up(4 * d.nnz);
+      en.sv = reinterpret_cast<uint16_t*>(p);
+      p += align_up(2 * d.nnz);
+      impl->slot[(size_t)d.linear] = (int)impl->ent.size();
+      impl->ent.push_back(en);
+    }
+    // -- staging, verification and digests
+    std::vector<uint8_t> digests((size_t)n * 32);
+    std::vector<qbl_status> st((size_t)n, QBL_OK);
+    std::vector<std::string> msg((size_t)n);
+    qbl::parallel_for(n, loader_threads(), [&](int64_t i) {
+      hipSetDevice(base->device);
+      const qbl_sparse_desc& d = descs[i];
+      const DevLinear& L = base->lin[(size_t)d.linear];
+      const AdEntry& en = impl->ent[(size_t)i];
+      uint8_t hdr[16];
+      put_le32(hdr, (uint32_t)d.linear);
+      put_le32(hdr + 4, 0xFFFFFFFFu);
+      put_le64(hdr + 8, (uint64_t)d.nnz);
+      qbl::Sha256 h;
+      h.update(hdr, sizeof hdr);
+      h.update(d.row_ptr, (size_t)(4 * (L.n + 1)));
+      if (d.nnz) {
+        h.update(d.col, (size_t)(4 * d.nnz));
+        h.update(d.val, (size_t)(2 * d.nnz));
+      }
+      h.final(&digests[(size_t)i * 32]);
+      const Part parts[3] = {{en.rp, d.row_ptr, 4 * (L.n + 1)}, {en.ci, d.col, 4 * d.nnz}, {en.sv, d.val, 2 * d.nnz}};
+      st[(size_t)i] = upload_verified(parts, d.nnz ? 3 : 1, &msg[(size_t)i]);
+    });
+    for (int i = 0; i < n; ++i)
+      if (st[(size_t)i] != QBL_OK) return fail(st[(size_t)i], "entry %d: %s", i, msg[(size_t)i].c_str());
+    qbl::Sha256 h;
+    h.update(digests.data(), digests.size());
+    h.final(impl->digest);
+    auto* a = new qbl_adapter;
+    a->impl = std::move(impl);
+    *out = a;
+    return QBL_OK;
+  })
+}
+
 extern "C" qbl_status qbl_adapter_digest(const qbl_adapter* adapter, uint8_t sha256_out[32]) {
   if (!adapter || !sha256_out) return fail(QBL_E_ARG, "null pointer");
   std::memcpy(sha256_out, adapter->impl->digest, 32);
@@ -699,7 +828,7 @@ extern "C" qbl_status qbl_comp_attach(qbl_comp* comp, const qbl_adapter* const* 
       L->scales.push_back(scales[i]);
       eff_digests.push_back(list[i]->impl->digest);
       for (const AdEntry& e : list[i]->impl->ent) {
-        L->plan[(size_t)e.linear].push_back(LoraRef{e.A, e.B, e.rank, scales[i]});
+        L->plan[(size_t)e.linear].push_back(LoraRef{e.A, e.B, e.rank, scales[i], e.rp, e.ci, e.sv});
         L->total_rank[(size_t)e.linear] += e.rank;
       }
     }
@@ -984,6 +1113,7 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
   int n_ent = 0;
   for (int i = 0; i < nlin; ++i) {
     for (const LoraRef& r : L->plan[(size_t)lin[i]]) {
+      if (r.rank == 0) continue;  // a sparse delta has no shrink
       ent[n_ent++] = qbl::PrepEntry{r.A, r.rank, T};
       T += r.rank;
     }
@@ -991,6 +1121,7 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
   bool same_type = true;
   for (int i = 1; i < nlin; ++i) same_type &= base->lin[(size_t)lin[i]].qtype == base->lin[(size_t)lin[0]].qtype;
 
+  int has_sparse = 0;
   auto fill_segments = [&](qbl::GemvArgs& a, int qt) {
     int toff = 0;
     for (int i = 0; i < nlin; ++i) {
@@ -1013,6 +1144,10 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
         s.lora.rank[j] = r.rank;
         s.lora.scale[j] = r.scale;
         s.lora.B[j] = r.B;
+        s.lora.rp[j] = r.rp;
+        s.lora.ci[j] = r.ci;
+        s.lora.sv[j] = r.sv;
+        has_sparse |= r.rank == 0;
         o += r.rank;
       }
       toff += this_rank;
@@ -1034,6 +1169,7 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     f.n_ent = n_ent;
     for (int i = 0; i < n_ent; ++i) f.ent[i] = ent[i];
     f.rows_total = T;
+    f.has_sparse = has_sparse;
     f.spin_limit = kSpinLimit;
     f.tag = next_tag();
     f.t = reinterpret_cast<uint64_t*>(t_buf);
@@ -1219,7 +1355,7 @@ extern "C" qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x,
     float* outs[1] = {y};
     const float* v[1] = {x};
     const DevLinear& D = b->lin[(size_t)linear];
-    const ListUse use{L.get(), st, T > 0};
+    const ListUse use{L.get(), st, !L->plan[(size_t)linear].empty()};
     return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), st);
   })
 }
@@ -1237,6 +1373,8 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
     auto L = std::atomic_load(&comp->list);
     const DevLinear& D = b->lin[(size_t)linear];
     if (D.qtype == QBL_Q4_K) return fail(QBL_E_FORMAT, "the prefill path takes q8_0 and q4_sm bases");
+    for (const LoraRef& r : L->plan[(size_t)linear])
+      if (r.rank == 0) return fail(QBL_E_FORMAT, "the prefill path takes low-rank adapters only");
     const int T = L->total_rank[(size_t)linear];
     if (qbl_status s = check_ws(ws, ws_bytes, align_up(qbl::jit_workspace_bytes((int)D.n, (int)D.k, T))))
       return s;

@@ -124,6 +124,11 @@ class Workload:
         L = self.linears[i]
         return sum(4 * ad.rank * (L.n_out + L.k_in) for ad in self.adapters)
 
+    def sparse_bytes(self, i: int, nnz: int) -> int:
+        """Bytes of a sparse delta of linear i with nnz entries: row_ptr, 4-byte
+        indices and 2-byte values."""
+        return 4 * (self.linears[i].n_out + 1) + 6 * nnz
+
 
 def _block_linears(prefix: str, d: int, h: int, qtype: int = Q8_0) -> list:
     shapes = {"q": (d, d), "k": (d, d), "v": (d, d), "o": (d, d),
@@ -139,6 +144,14 @@ def single(n: int = 256, k: int = 256) -> Workload:
 def block(d: int = 4096, h: int = 11008, name: str = "block", rank: int = 16) -> Workload:
     return Workload(name, _block_linears(name + "/b0", d, h), [AdapterSpec("A1", rank, 1.0)],
                     blocks=1, tokens=1)
+
+
+def block_sparse(d: int = 4096, h: int = 11008, name: str = "block_sparse", rank: int = 16,
+                 density: float = 0.1) -> Workload:
+    """The 7B block with a rank-16 LoRA and, after it in the list, a DARE-style
+    sparse delta keeping `density` of each linear's entries, both at scale 1.0."""
+    return Workload(name, _block_linears(name + "/b0", d, h),
+                    [AdapterSpec("A1", rank, 1.0), AdapterSpec("S1", 0, 1.0, density)], blocks=1, tokens=1)
 
 
 def stack(d: int = 4096, h: int = 11008, n_blocks: int = 32, tokens: int = 256,
@@ -167,6 +180,10 @@ def prefill(m: int = 512, k: int = 4096, n: int = 14336, name: str = "prefill",
 # several kernel tiles and a ragged tail.
 def small_block() -> Workload:
     return block(d=544, h=1440, name="small_block")
+
+
+def small_block_sparse() -> Workload:
+    return block_sparse(d=544, h=1440, name="small_block_sparse")
 
 
 def small_stack() -> Workload:

@@ -41,13 +41,17 @@ class Built:
             del w
         self.base = q.qbl_base_load(descs)
         del descs
-        self.factors = []   # [adapter][linear] -> (A, B)
+        self.factors = []   # [adapter][linear] -> (A, B), or (row_ptr, col, val) for a sparse delta
         self.adapters = []
-        for a in range(len(wl.adapters)):
-            fac = [(wl.lora_a(i, a), wl.lora_b(i, a)) for i in range(len(wl.linears))]
+        for a, spec in enumerate(wl.adapters):
+            if spec.rank == 0:
+                fac = [wl.sparse_csr(i, a) for i in range(len(wl.linears))]
+                handle = q.qbl_adapter_load_sparse(self.base, [(i, *f) for i, f in enumerate(fac)])
+            else:
+                fac = [(wl.lora_a(i, a), wl.lora_b(i, a)) for i in range(len(wl.linears))]
+                handle = q.qbl_adapter_load(self.base, [(i, A, B) for i, (A, B) in enumerate(fac)])
             self.factors.append(fac if keep_oracle else None)
-            self.adapters.append(q.qbl_adapter_load(
-                self.base, [(i, A, B) for i, (A, B) in enumerate(fac)]))
+            self.adapters.append(handle)
         self.comp = q.qbl_comp_create(self.base)
 
     def attach(self, idx, scales=None):
@@ -56,7 +60,8 @@ class Built:
 
     def oracle_ads(self, i, idx, scales=None):
         scales = [self.wl.adapters[a].scale for a in idx] if scales is None else scales
-        return [oracle.Lora(*self.factors[a][i], s) for a, s in zip(idx, scales)]
+        return [(oracle.Sparse if self.wl.adapters[a].rank == 0 else oracle.Lora)(*self.factors[a][i], s)
+                for a, s in zip(idx, scales)]
 
     def oracle_layers(self, idx, scales=None):
         return [oracle.Layer(L.qtype, self.or_blocks[i], L.n_out, L.k_in,
