@@ -16,6 +16,7 @@ Also reported on the same JSON line:
   stack         32 such blocks, two adapters (r16@1.0 then r64@0.5), 256 tokens
   q4_mlp        70B-style q4_sm MLP linears at batch 1 and 8
   q4k_mlp       the same MLP with a q4_K (256-weight super-block) base
+  sparse_block  the 7B block with its LoRA and a 10%-dense sparse (CSR) delta
   prefill       the JIT-materialisation prefill GEMM (when available)
   stack.lifecycle  load (staging + verification + digest), attach, rollback and
                 base-hash costs on the stack
@@ -276,6 +277,44 @@ def bench_lifecycle(q, base, ads, comp, timing, hash_s):
     return out
 
 
+def bench_sparse(torch, q, workloads, args):
+    """The 7B block with its rank-16 LoRA and a 10%-dense sparse (DARE/CSR) delta
+    after it on every linear; weights, factors and deltas rotated over copies."""
+    wl = workloads.block_sparse()
+    copies = args.copies
+    log(f"[sparse] building {copies} copies of one 7B block (q8_0, r16 + 10% sparse delta)")
+    t0 = time.time()
+    blocks = [q.qbl_quantize(L.qtype, wl.weight(i)) for i, L in enumerate(wl.linears)]
+    n = len(wl.linears)
+    base = q.qbl_base_load([(L.qtype, L.n_out, L.k_in, blocks[i]) for c in range(copies)
+                            for i, L in enumerate(wl.linears)])
+    fac = [(wl.lora_a(i, 0), wl.lora_b(i, 0)) for i in range(n)]
+    lora = q.qbl_adapter_load(base, [(c * n + i, A, B) for c in range(copies) for i, (A, B) in enumerate(fac)])
+    csr = [wl.sparse_csr(i, 1) for i in range(n)]
+    sparse = q.qbl_adapter_load_sparse(base, [(c * n + i, *csr[i]) for c in range(copies) for i in range(n)])
+    comp = q.qbl_comp_create(base)
+    q.qbl_comp_attach(comp, [lora, sparse], [1.0, 1.0])
+    log(f"[sparse] built in {time.time() - t0:.1f}s")
+    x = torch.from_numpy(wl.x0()[0]).cuda()
+    ys = [torch.empty(4096, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    ws = q.workspace(comp, q.OP_BLOCK)
+
+    def step(i):
+        q.qbl_block(comp, i % copies, x, ys[i % copies], ws)
+
+    ms = time_loop(torch, step, args.steps, args.warmup)
+    nnz = sum(int(c[1].size) for c in csr)
+    step_bytes = sum(linear_bytes(wl, i) + wl.sparse_bytes(i, int(csr[i][1].size)) for i in range(n))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    q.qbl_comp_free(comp)
+    q.qbl_adapter_free(lora)
+    q.qbl_adapter_free(sparse)
+    q.qbl_base_free(base)
+    log(f"[sparse] {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({nnz} sparse entries per block)")
+    return {"us_per_step": round(ms * 1e3, 1), "GB_per_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_step": step_bytes, "sparse_entries": nnz, "density": wl.adapters[1].density}
+
+
 def bench_q4(torch, q, wl, args, label):
     out = {}
     log(f"[{label}] building 70B MLP linears ({label}, r32)")
@@ -378,6 +417,7 @@ def main():
         result["stack"] = bench_stack(torch, q, workloads, args)
         result["q4_mlp"] = bench_q4(torch, q, workloads.mlp70b(), args, "q4_sm")
         result["q4k_mlp"] = bench_q4(torch, q, workloads.mlp70b_q4k(), args, "q4_K")
+        result["sparse_block"] = bench_sparse(torch, q, workloads, args)
         result["prefill"] = bench_prefill(torch, q, workloads, args)
     import oracle
     log("[cpu] timing the oracle")

@@ -191,6 +191,35 @@ __device__ __forceinline__ float chunk_dot(float p, const uint4 q, const float4*
   }
 }
 
+// Sum over entries [e0, e1) of one CSR row of fp16 val[e] * x(col[e]), this
+// lane's share: entries e0 + lane, e0 + lane + 64, ...  Loads go out in rounds
+// of 8 per lane (the column and value loads of a round first, then its 8
+// gathers), so a row of up to 512 entries waits for two memory round trips.
+// Entries past e1 read entry e0 with value 0.  xat(c) returns the input at
+// column c.
+template <class XAt>
+__device__ __forceinline__ float csr_row_dot(const uint32_t* col, const uint16_t* val, uint32_t e0,
+                                             uint32_t e1, int lane, XAt xat) {
+  float p = 0.0f;
+  for (uint32_t r0 = e0; r0 < e1; r0 += 8 * 64) {
+    uint32_t c[8];
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t e = r0 + 64 * u + lane;
+      const bool ok = e < e1;
+      c[u] = *gp(col + (ok ? e : e0));
+      v[u] = ok ? (uint32_t)*gp(val + e) : 0u;
+    }
+    float xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xv[u] = xat(c[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p = fmaf(h2f(v[u]), xv[u], p);
+  }
+  return p;
+}
+
 // A value handed from one workgroup to others in the same launch: one 64-bit
 // word, the launch's (or phase's) tag in the high half and the float in the low
 // half, read with device-coherent relaxed loads until the tag matches (bounded).

@@ -320,9 +320,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
         const int rk = g.lora.rank[i];
         if (rk == 0) {  // sparse delta: lanes strided over the row's entries
           const float* xb = a.x + (int64_t)b * a.x_stride;
-          const uint32_t e1 = g.lora.rp[i][row + 1];
-          float p = 0.0f;
-          for (uint32_t e = g.lora.rp[i][row] + lane; e < e1; e += 64) p = fmaf(h2f(g.lora.sv[i][e]), xb[g.lora.ci[i][e]], p);
+          const float p = csr_row_dot(g.lora.ci[i], g.lora.sv[i], g.lora.rp[i][row], g.lora.rp[i][row + 1], lane,
+                                      [&](uint32_t c) { return *gp(xb + c); });
           v = fmaf(g.lora.scale[i], p, v);
           continue;
         }
@@ -628,15 +627,13 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
       if (row >= g.n) continue;
       for (int i = 0; i < g.lora.n_ad; ++i) {
         if (g.lora.rank[i] != 0) continue;
-        const uint32_t e1 = g.lora.rp[i][row + 1];
-        float p = 0.0f;
-        for (uint32_t e = g.lora.rp[i][row] + lane; e < e1; e += 64) {
-          const uint32_t c = g.lora.ci[i][e];
-          float xv = f.v[0][c];
-          if (f.nv > 1) xv += f.v[1][c];
-          if (f.nv > 2) xv += f.v[2][c];
-          p = fmaf(h2f(g.lora.sv[i][e]), xv, p);
-        }
+        float p = csr_row_dot(g.lora.ci[i], g.lora.sv[i], g.lora.rp[i][row], g.lora.rp[i][row + 1], lane,
+                              [&](uint32_t c) {
+                                float xv = *gp(f.v[0] + c);
+                                if (f.nv > 1) xv += *gp(f.v[1] + c);
+                                if (f.nv > 2) xv += *gp(f.v[2] + c);
+                                return xv;
+                              });
         p = wave_sum(p);
         if (lane == 0) spl[i][s] = p;
       }
