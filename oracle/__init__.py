@@ -69,6 +69,7 @@ def _load():
             "or_linear_dual": (i32, [i32, vp, i64, i64, vp, i32, vp, i32, vp, i64, vp, i32]),
             "or_linear_materialised": (i32, [i32, vp, i64, i64, vp, i32, vp, i32, vp, i64, vp, i32]),
             "or_jit_weff": (i32, [i32, vp, i64, i64, vp, i32, vp, i64, vp, i32]),
+            "or_requantize": (i32, [i32, vp, i64, i64, vp, i32, vp, i32]),
             "or_gemm_bf16": (i32, [vp, i64, vp, i64, i64, vp, i32]),
             "or_rms": (None, [vp, i64, ctypes.c_double, vp]),
             "or_block": (i32, [vp, vp, vp, i32]),
@@ -248,6 +249,18 @@ def jit_weff(qtype, blocks, n, k, ads=(), rows=None, nthreads=0) -> np.ndarray:
                              None if r is None else r.ctypes.data, nr, out.ctypes.data, nthreads)
     if rc != 0:
         raise ValueError("or_jit_weff rejected its arguments")
+    return out
+
+
+def requantize(qtype, blocks, n, k, ads=(), nthreads=0) -> np.ndarray:
+    """Canonical blocks of Q(deq(W) + sum of the adapters' deltas), the merged
+    weight formed by the float32 recipe of or_requantize."""
+    blocks = _c(blocks, np.uint8)
+    out = np.empty((n, k // block_weights(qtype) * block_bytes(qtype)), np.uint8)
+    la = _lora_array(ads)
+    if _load().or_requantize(qtype, blocks.ctypes.data, n, k, ctypes.addressof(la), len(ads),
+                             out.ctypes.data, nthreads):
+        raise ValueError("or_requantize rejected its arguments")
     return out
 
 

@@ -558,6 +558,70 @@ int32_t or_jit_weff(int32_t qtype, const uint8_t* blocks, int64_t n, int64_t k,
   return for_rows(n_rows, nthreads, k, jit_row, &c);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Dequantize-add-requantize, the destructive merge the overlay avoids       */
+/* (overlay page, "Quantized-Base Numerical Analysis"; Deep Technical Design, */
+/* "The Pathology of Dequantize-Add-Requantize (DAR) Error"): the merged      */
+/* float32 weight of each element, then the base format's quantiser.  The    */
+/* merged weight follows one fixed float32 recipe, so that a GPU kernel can  */
+/* reach the same codes:                                                     */
+/*   w = f32(deq(W)[r][k]);                                                  */
+/*   for each adapter in list order:                                        */
+/*     LoRA:   u = 0; for j = 0..rank-1: u = fma(B[r][j], A[j][k], u);        */
+/*             w = fma(scale, u, w)                                          */
+/*     sparse: if (r, k) is an entry with value v: w = fma(scale, f32(v), w)  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t qtype;
+  const uint8_t* blocks;
+  int64_t k;
+  const or_lora* ads;
+  int32_t n_ads;
+  uint8_t* out;
+} dar_ctx;
+
+static void dar_row(void* vc, int64_t r, double* tmp) {
+  const dar_ctx* c = (const dar_ctx*)vc;
+  const int64_t k = c->k;
+  float* w = (float*)malloc((size_t)k * sizeof(float));
+  if (!w) return;
+  dequant_row(c->qtype, c->blocks, r, k, tmp);
+  for (int64_t kk = 0; kk < k; ++kk) w[kk] = (float)tmp[kk];
+  for (int32_t a = 0; a < c->n_ads; ++a) {
+    const or_lora* ad = &c->ads[a];
+    if (ad->rank == 0) {
+      for (uint32_t p = ad->row_ptr[r]; p < ad->row_ptr[r + 1]; ++p)
+        w[ad->col[p]] = fmaf(ad->scale, or_f32_from_f16(ad->val[p]), w[ad->col[p]]);
+      continue;
+    }
+    for (int64_t kk = 0; kk < k; ++kk) {
+      float u = 0.0f;
+      for (int32_t j = 0; j < ad->rank; ++j) u = fmaf(ad->B[r * ad->rank + j], ad->A[(int64_t)j * k + kk], u);
+      w[kk] = fmaf(ad->scale, u, w[kk]);
+    }
+  }
+  const int32_t bw = or_block_weights(c->qtype), bb = or_block_bytes(c->qtype);
+  const int64_t nb = k / bw;
+  for (int64_t b = 0; b < nb; ++b) {
+    uint8_t* dst = c->out + (r * nb + b) * bb;
+    if (c->qtype == OR_Q8_0)
+      quantize_q8_0_block(w + b * bw, dst);
+    else if (c->qtype == OR_Q4_SM)
+      quantize_q4_sm_block(w + b * bw, dst);
+    else
+      quantize_q4_k_block(w + b * bw, dst);
+  }
+  free(w);
+}
+
+int32_t or_requantize(int32_t qtype, const uint8_t* blocks, int64_t n, int64_t k, const or_lora* ads,
+                      int32_t n_ads, uint8_t* blocks_out, int32_t nthreads) {
+  if (check_lin(qtype, blocks, n, k, ads, n_ads, NULL, n) || !blocks_out) return -1;
+  dar_ctx c = {qtype, blocks, k, ads, n_ads, blocks_out};
+  return for_rows(n, nthreads, k, dar_row, &c);
+}
+
 typedef struct {
   const uint16_t* X;
   int64_t m;

@@ -96,6 +96,15 @@ int32_t or_jit_weff(int32_t qtype, const uint8_t* blocks, int64_t n, int64_t k,
 int32_t or_gemm_bf16(const uint16_t* X, int64_t m, const uint16_t* weff, int64_t n_rows,
                      int64_t k, double* y, int32_t nthreads);
 
+/* Dequantize-add-requantize (the destructive merge the overlay avoids): the
+ * base format's quantiser applied to the float32 merged weight
+ *   w = f32(deq(W)[r][k]), then per adapter in list order
+ *   LoRA   w = fma(scale, u, w), u = fma chain over j = 0..rank-1 of B[r][j]*A[j][k]
+ *   sparse w = fma(scale, f32(val), w) at the delta's entries.
+ * blocks_out: n x k/block_weights canonical blocks.  Returns 0 or -1. */
+int32_t or_requantize(int32_t qtype, const uint8_t* blocks, int64_t n, int64_t k, const or_lora* ads,
+                      int32_t n_ads, uint8_t* blocks_out, int32_t nthreads);
+
 /* RMS scaling: out = v / sqrt(mean(v^2) + eps). */
 void or_rms(const double* v, int64_t n, double eps, double* out);
 
