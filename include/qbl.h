@@ -399,6 +399,24 @@ qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_blocks, con
                       float* y_tokens, int32_t n_tokens, void* ws, int64_t ws_bytes,
                       void* stream);
 
+/* ---------------------------------------------------------- measurement --- */
+
+/* Dequantize-add-requantize of one linear under the composition's current list:
+ * the destructive merge that the overlay never performs, offered only to
+ * measure its drift ([overlay] "Quantized-Base Numerical Analysis"; [design]
+ * "The Pathology of Dequantize-Add-Requantize (DAR) Error").  Writes the
+ * canonical blocks of Q(W') to blocks_out (device, at least
+ * n_out*k_in/qbl_block_weights*qbl_block_bytes bytes, 2-byte aligned; else
+ * QBL_E_BUDGET / QBL_E_ARG), where Q is the base format's quantiser
+ * (qbl_quantize) and W' the float32 merged weight
+ *   w = f32(deq(W)[n][k]); then for each entry in list order
+ *   low-rank: w = fma(s, u, w), u = fma chain over j = 0..rank-1 of B[n][j]*A[j][k]
+ *   sparse:   w = fma(s, f32(val), w) at the delta's entries.
+ * The base itself is never written.  Asynchronous on stream.  A block whose
+ * scale overflows fp16 is written with an infinite scale. */
+qbl_status qbl_requantize(qbl_comp* comp, int32_t linear, void* blocks_out, int64_t out_bytes,
+                          void* stream);
+
 /* ------------------------------------------------------------- timing --- */
 
 /* Kernel timing for measurement tools.  While enabled (on != 0), every launch
@@ -407,7 +425,7 @@ qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_blocks, con
  * the recorded events and returns, per kernel kind (0 = batch-1 / batched
  * dequant-GEMV, 1 = glue/shrink prep, 2 = JIT prefill GEMM), the number of
  * launches and their
- * summed duration in milliseconds.  Timing adds host work per launch: leave it
+ * summed duration in milliseconds (3 = qbl_requantize).  Timing adds host work per launch: leave it
  * off in production. */
 qbl_status qbl_profile_enable(int32_t on);
 qbl_status qbl_profile_read(int32_t kind, int64_t* launches, double* total_ms);

@@ -107,6 +107,7 @@ EXPORTS = {
     "qbl_linear_jit": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
     "qbl_block": (_i32, [_vp, _i32, _vp, _vp, _vp, _i64, _vp]),
     "qbl_decode": (_i32, [_vp, _i32, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
+    "qbl_requantize": (_i32, [_vp, _i32, _vp, _i64, _vp]),
     "qbl_profile_enable": (_i32, [_i32]),
     "qbl_profile_read": (_i32, [_i32, _vp, _vp]),
 }
@@ -364,6 +365,11 @@ class Library:
         self._check(self._lib.qbl_decode(comp, first_block, n_blocks, _dev_ptr(x0, torch.float32),
                                          _dev_ptr(y_tokens, torch.float32), n_tokens, wp, wb, _stream(stream)))
 
+    def qbl_requantize(self, comp, linear: int, out, stream=None) -> None:
+        """Canonical blocks of the dequantize-add-requantize merge into `out` (a CUDA byte tensor)."""
+        self._check(self._lib.qbl_requantize(comp, linear, _dev_ptr(out), out.numel() * out.element_size(),
+                                             _stream(stream)))
+
     # -- timing ------------------------------------------------------------------
     def qbl_profile_enable(self, on: bool) -> None:
         self._check(self._lib.qbl_profile_enable(1 if on else 0))
@@ -375,7 +381,7 @@ class Library:
         return n.value, ms.value
 
 
-KIND_GEMV, KIND_PREP, KIND_JIT = 0, 1, 2
+KIND_GEMV, KIND_PREP, KIND_JIT, KIND_DAR = 0, 1, 2, 3
 
 _default = Library(_SO)
 _lib = _default._lib

@@ -130,6 +130,26 @@ struct JitArgs {
   uint16_t* ws;        // scratch for the staged bf16 factors (see launch_jit)
 };
 
+// Dequantize-add-requantize of one linear under an adapter list (a merge the
+// overlay never performs; used to measure its drift): canonical blocks of
+// Q(deq(W) + sum of the adapters' deltas) into out.  Adapter entries as in
+// LoraSeg (rank 0: sparse delta rp/ci/sv; otherwise A rank x k and B n x rank).
+struct DarArgs {
+  int qtype;
+  const uint8_t* qs;
+  const void* sc;
+  int n, k;
+  int n_ad;
+  int rank[kMaxAdapters];
+  float scale[kMaxAdapters];
+  const float* A[kMaxAdapters];
+  const float* B[kMaxAdapters];
+  const uint32_t* rp[kMaxAdapters];
+  const uint32_t* ci[kMaxAdapters];
+  const uint16_t* sv[kMaxAdapters];
+  uint8_t* out;
+};
+
 // Where a kernel goes: the stream, and optionally a pair of events that the
 // runtime attaches to the dispatch itself (hipExtLaunchKernelGGL) so that they
 // time the kernel's execution.
@@ -153,5 +173,6 @@ inline int64_t t_copy_stride(int64_t rows) { return (rows + 31) / 32 * 32 + 32; 
 hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc);
 
 int64_t jit_workspace_bytes(int n, int k, int total_rank);
+hipError_t launch_dar(const DarArgs& a, const LaunchCtx& lc);
 
 }  // namespace qbl

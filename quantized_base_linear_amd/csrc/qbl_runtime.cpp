@@ -1406,6 +1406,47 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
   })
 }
 
+extern "C" qbl_status qbl_requantize(qbl_comp* comp, int32_t linear, void* blocks_out, int64_t out_bytes,
+                                     void* stream) {
+  QBL_TRY({
+    if (!comp || !blocks_out) return fail(QBL_E_ARG, "null pointer");
+    const qbl_base* b = comp->base;
+    if (linear < 0 || linear >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", linear);
+    if (qbl_status s = check_device(b)) return s;
+    const DevLinear& D = b->lin[(size_t)linear];
+    const int64_t need = D.n * (D.k / qbl_block_weights(D.qtype)) * qbl_block_bytes(D.qtype);
+    if (out_bytes < need)
+      return fail(QBL_E_BUDGET, "output holds %lld bytes; the linear needs %lld", (long long)out_bytes, (long long)need);
+    if (reinterpret_cast<uintptr_t>(blocks_out) % 2) return fail(QBL_E_ARG, "output must be 2-byte aligned");
+    std::lock_guard<std::mutex> g(comp->mu);
+    auto L = std::atomic_load(&comp->list);
+    qbl::DarArgs a{};
+    a.qtype = D.qtype;
+    a.qs = D.qs;
+    a.sc = D.sc;
+    a.n = (int)D.n;
+    a.k = (int)D.k;
+    for (const LoraRef& r : L->plan[(size_t)linear]) {
+      const int j = a.n_ad++;
+      a.rank[j] = r.rank;
+      a.scale[j] = r.scale;
+      a.A[j] = r.A;
+      a.B[j] = r.B;
+      a.rp[j] = r.rp;
+      a.ci[j] = r.ci;
+      a.sv[j] = r.sv;
+    }
+    a.out = static_cast<uint8_t*>(blocks_out);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const ListUse use{L.get(), st, a.n_ad > 0};
+    KernelTimer tm(3, st);
+    hipError_t e = qbl::launch_dar(a, tm.ctx());
+    if (e != hipSuccess) return hip_fail(e, "requantize launch");
+    tm.stop();
+    return QBL_OK;
+  })
+}
+
 extern "C" qbl_status qbl_block(qbl_comp* comp, int32_t block, const float* x, float* y, void* ws,
                                 int64_t ws_bytes, void* stream) {
   QBL_TRY({

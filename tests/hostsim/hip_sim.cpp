@@ -146,6 +146,7 @@ bool fused_supported(int, int) { return true; }
 hipError_t launch_fused(FusedArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
 hipError_t launch_jit(const JitArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
 int64_t jit_workspace_bytes(int, int, int) { return 0; }
+hipError_t launch_dar(const DarArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
 }  // namespace qbl
 
 // Inspection of the double, for the tests.
