@@ -17,6 +17,8 @@ Also reported on the same JSON line:
   q4_mlp        70B-style q4_sm MLP linears at batch 1 and 8
   q4k_mlp       the same MLP with a q4_K (256-weight super-block) base
   sparse_block  the 7B block with its LoRA and a 10%-dense sparse (CSR) delta
+  dar           drift of dequantize-add-requantize merges (the merge the overlay
+                avoids) and the requantise kernel's time
   prefill       the JIT-materialisation prefill GEMM (when available)
   stack.lifecycle  load (staging + verification + digest), attach, rollback and
                 base-hash costs on the stack
@@ -315,6 +317,110 @@ def bench_sparse(torch, q, workloads, args):
             "bytes_per_step": step_bytes, "sparse_entries": nnz, "density": wl.adapters[1].density}
 
 
+def bench_dar(torch, q, workloads, args):
+    """Drift of the dequantize-add-requantize merge that the overlay avoids, on
+    two linears of a 7B block (o 4096x4096, gate 11008x4096, q8_0) with the
+    stack's adapters A (r16 @ 1.0) and B (r64 @ 0.5): one merge Q(W + A + B),
+    the chains Q(Q(W + A) + B) and Q(Q(W + B) + A), and 8 switch cycles
+    W <- Q(Q(W + A) - A).  Errors are relative to the exact merged weight (or,
+    for the cycles, to the base) and to the adapters' own delta; the overlay's
+    figure is 0 by construction (the base bytes never change).  Also the
+    requantise kernel's time."""
+    import numpy as np
+    wl = workloads.stack(n_blocks=1, tokens=1, name="dar_bench")
+    lins = [3, 4]
+    out = {"linears": {}}
+    x_rng = np.random.default_rng(7)
+
+    def load(blocks_list):
+        return q.qbl_base_load([(wl.linears[i].qtype, wl.linears[i].n_out, wl.linears[i].k_in, blk)
+                                for i, blk in zip(lins, blocks_list)])
+
+    def merge(blocks_list, terms):
+        """terms: list of (adapter index, scale) applied in order; one requantisation."""
+        base = load(blocks_list)
+        ads = [q.qbl_adapter_load(base, [(j, wl.lora_a(i, a), wl.lora_b(i, a)) for j, i in enumerate(lins)])
+               for a, _ in terms]
+        comp = q.qbl_comp_create(base)
+        q.qbl_comp_attach(comp, ads, [s for _, s in terms])
+        res = []
+        for j, i in enumerate(lins):
+            L = wl.linears[i]
+            o = torch.empty(L.n_out * L.k_in // 32 * 34, dtype=torch.uint8, device="cuda")
+            q.qbl_requantize(comp, j, o)
+            torch.cuda.synchronize()
+            res.append(o.cpu().numpy().reshape(L.n_out, -1))
+        free_all(q, base, ads, comp)
+        return res
+
+    base_blocks = [q.qbl_quantize(wl.linears[i].qtype, wl.weight(i)) for i in lins]
+    sA, sB = wl.adapters[0].scale, wl.adapters[1].scale
+    once = merge(base_blocks, [(0, sA), (1, sB)])
+    chain_ab = merge(merge(base_blocks, [(0, sA)]), [(1, sB)])
+    chain_ba = merge(merge(base_blocks, [(1, sB)]), [(0, sA)])
+    cyc = base_blocks
+    for _ in range(8):
+        cyc = merge(merge(cyc, [(0, sA)]), [(0, -sA)])
+
+    # kernel time of one requantisation of both linears under A and B
+    base = load(base_blocks)
+    ads = [q.qbl_adapter_load(base, [(j, wl.lora_a(i, a), wl.lora_b(i, a)) for j, i in enumerate(lins)])
+           for a in (0, 1)]
+    comp = q.qbl_comp_create(base)
+    q.qbl_comp_attach(comp, ads, [sA, sB])
+    outs = [torch.empty(wl.linears[i].n_out * wl.linears[i].k_in // 32 * 34, dtype=torch.uint8, device="cuda")
+            for i in lins]
+    q.qbl_profile_enable(True)
+    for _ in range(5):
+        for j in range(len(lins)):
+            q.qbl_requantize(comp, j, outs[j])
+    torch.cuda.synchronize()
+    n_dar, ms_dar = q.qbl_profile_read(q.KIND_DAR)
+    q.qbl_profile_enable(False)
+    free_all(q, base, ads, comp)
+    r = sum(a.rank for a in wl.adapters)
+    dar_bytes = sum(2 * wl.base_bytes(i) + 4 * r * (wl.linears[i].n_out + wl.linears[i].k_in) for i in lins)
+    dar_us = ms_dar / max(n_dar, 1) * len(lins) * 1e3
+    out["requantize_us_both_linears"] = round(dar_us, 1)
+    out["requantize_GB_per_s"] = round(dar_bytes / (dar_us * 1e-6) / 1e9, 1)
+
+    for j, i in enumerate(lins):
+        L = wl.linears[i]
+        deq = lambda blk: q.qbl_dequantize(L.qtype, blk, L.n_out, L.k_in).astype(np.float64)
+        W0 = deq(base_blocks[j])
+        delta = sA * (wl.lora_b(i, 0).astype(np.float64) @ wl.lora_a(i, 0)) + \
+            sB * (wl.lora_b(i, 1).astype(np.float64) @ wl.lora_a(i, 1))
+        exact = W0 + delta
+        nd, ne, n0 = np.linalg.norm(delta), np.linalg.norm(exact), np.linalg.norm(W0)
+        rel = lambda blk: float(np.linalg.norm(deq(blk) - exact))
+        x = x_rng.standard_normal(L.k_in)
+        y_exact = exact @ x
+        y_once = deq(once[j]) @ x
+        d_old = base_blocks[j].reshape(L.n_out, -1, 34)[:, :, :2].copy().view(np.float16).astype(np.float64)
+        d_new = once[j].reshape(L.n_out, -1, 34)[:, :, :2].copy().view(np.float16).astype(np.float64)
+        ratio = d_new[d_old > 0] / d_old[d_old > 0]
+        codes_old = base_blocks[j].reshape(L.n_out, -1, 34)[:, :, 2:]
+        codes_new = once[j].reshape(L.n_out, -1, 34)[:, :, 2:]
+        out["linears"][f"{L.n_out}x{L.k_in}"] = {
+            "delta_rel_to_weight": round(nd / n0, 5),
+            "once_err_rel_weight": round(rel(once[j]) / ne, 6),
+            "once_err_rel_delta": round(rel(once[j]) / nd, 4),
+            "chain_ab_err_rel_delta": round(rel(chain_ab[j]) / nd, 4),
+            "chain_ba_err_rel_delta": round(rel(chain_ba[j]) / nd, 4),
+            "chain_orders_bytes_differ": bool(not np.array_equal(chain_ab[j], chain_ba[j])),
+            "cycles8_base_drift_rel_weight": round(float(np.linalg.norm(deq(cyc[j]) - W0)) / n0, 6),
+            "cycles8_bytes_changed_frac": round(float((cyc[j] != base_blocks[j]).mean()), 4),
+            "once_scale_changed_frac": round(float((ratio != 1.0).mean()), 4),
+            "once_scale_ratio_max": round(float(ratio.max()), 4),
+            "once_codes_changed_frac": round(float((codes_new != codes_old).mean()), 4),
+            "once_output_rel_l2": round(float(np.linalg.norm(y_once - y_exact) / np.linalg.norm(y_exact)), 6),
+            "overlay_err": 0.0,
+        }
+        log(f"[dar] {L.n_out}x{L.k_in}: {out['linears'][f'{L.n_out}x{L.k_in}']}")
+    log(f"[dar] requantise {dar_us:.1f} us for both linears ({out['requantize_GB_per_s']} GB/s)")
+    return out
+
+
 def bench_q4(torch, q, wl, args, label):
     out = {}
     log(f"[{label}] building 70B MLP linears ({label}, r32)")
@@ -418,6 +524,7 @@ def main():
         result["q4_mlp"] = bench_q4(torch, q, workloads.mlp70b(), args, "q4_sm")
         result["q4k_mlp"] = bench_q4(torch, q, workloads.mlp70b_q4k(), args, "q4_K")
         result["sparse_block"] = bench_sparse(torch, q, workloads, args)
+        result["dar"] = bench_dar(torch, q, workloads, args)
         result["prefill"] = bench_prefill(torch, q, workloads, args)
     import oracle
     log("[cpu] timing the oracle")

@@ -3,8 +3,10 @@
 // overlay system", "Quantized-Base Numerical Analysis"; "Deep Technical
 // Design", "The Pathology of Dequantize-Add-Requantize (DAR) Error").
 //
-// One thread per 32-weight chunk (a q8_0 or q4_sm block, a q4_K sub-block;
-// the 8 sub-blocks of a q4_K super-block are 8 consecutive lanes).  A thread
+// One thread per 32-weight chunk (a q8_0 or q4_sm block, a q4_K sub-block).
+// A wave covers 64 rows at one chunk (q4_K: 8 rows at the 8 chunks of one
+// super-block, whose sub-blocks are then 8 consecutive lanes), so the A values
+// of a chunk are one broadcast load for the wave instead of one per lane.  A thread
 // forms the merged float32 weights of its chunk with one fixed recipe
 //   w = f32(deq(W));  per adapter in list order:
 //     low-rank  w = fma(s, u, w),  u = fma chain over j of B[r][j] * A[j][k]
@@ -32,10 +34,16 @@ __device__ __forceinline__ float mx(float a, float b) { return a < b ? b : a; }
 template <int QT>
 __global__ __launch_bounds__(kDarThreads) void dar_kernel(DarArgs a) {
 #pragma clang fp contract(off)  // the codes depend on each rounding: only the fmas written out fuse
-  const int64_t t = (int64_t)blockIdx.x * kDarThreads + threadIdx.x;
-  const int cpr = a.k / 32;                       // chunks per row
-  if (t >= (int64_t)a.n * cpr) return;            // q4_K: whole 8-lane groups leave together
-  const int row = (int)(t / cpr), c = (int)(t % cpr);
+  constexpr int RW = QT == QBL_FMT_Q4K ? 8 : 64;  // rows per wave
+  constexpr int CW = 64 / RW;                      // chunks per wave
+  const int cpr = a.k / 32;                        // chunks per row
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = ((int64_t)blockIdx.x * kDarThreads + threadIdx.x) >> 6;
+  const int64_t n_rw = (a.n + RW - 1) / RW;        // row groups
+  const int rgrp = (int)(wv % n_rw), cgrp = (int)(wv / n_rw);
+  const int row = rgrp * RW + lane / CW, c = cgrp * CW + lane % CW;
+  if (row >= a.n || c >= cpr) return;              // q4_K: whole 8-lane groups leave together
+  const int64_t t = (int64_t)row * cpr + c;        // the chunk's index in canonical order
   const int k0 = 32 * c;
 
   // ---- exact float32 dequantisation of the chunk
@@ -215,8 +223,9 @@ __global__ __launch_bounds__(kDarThreads) void dar_kernel(DarArgs a) {
 hipError_t launch_dar(const DarArgs& a, const LaunchCtx& lc) {
   (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   if (a.k % (a.qtype == QBL_FMT_Q4K ? 256 : 32) || a.n < 1) return hipErrorInvalidValue;
-  const int64_t threads = (int64_t)a.n * (a.k / 32);
-  const dim3 grid((unsigned)((threads + kDarThreads - 1) / kDarThreads));
+  const int rw = a.qtype == QBL_FMT_Q4K ? 8 : 64;
+  const int64_t waves = (int64_t)(a.n + rw - 1) / rw * ((a.k / 32) / (64 / rw));
+  const dim3 grid((unsigned)((waves * 64 + kDarThreads - 1) / kDarThreads));
   switch (a.qtype) {
     case QBL_FMT_Q8: QBL_LAUNCH((dar_kernel<QBL_FMT_Q8>), grid, dim3(kDarThreads), 0, lc, a); break;
     case QBL_FMT_Q4: QBL_LAUNCH((dar_kernel<QBL_FMT_Q4>), grid, dim3(kDarThreads), 0, lc, a); break;
