@@ -657,8 +657,19 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
       const float* ti = tl + g.lora.toff[i];
       const float* Br = g.lora.B[i] + (int64_t)min(row, g.n - 1) * rk;
       float p = 0.0f;
+      int j = 0;
+      if (rk % 4 == 0) {  // 16-byte B loads, four in flight (the row is 16-byte aligned)
+#pragma unroll 4
+        for (; j < rk; j += 4) {
+          const float4 b4 = gload4(Br + j);
+          p = fmaf(b4.x, ti[j], p);
+          p = fmaf(b4.y, ti[j + 1], p);
+          p = fmaf(b4.z, ti[j + 2], p);
+          p = fmaf(b4.w, ti[j + 3], p);
+        }
+      }
 #pragma unroll 8
-      for (int j = 0; j < rk; ++j) p = fmaf(Br[j], ti[j], p);
+      for (; j < rk; ++j) p = fmaf(Br[j], ti[j], p);
       v = fmaf(g.lora.scale[i], p, v);
     }
     if (f.sum) outl[s] = v;
@@ -794,6 +805,44 @@ hipError_t launch_batch(GemvArgs& a, int bb, int cpl, const LaunchCtx& lc) {
   }
 }
 
+// y = v / sqrt(mean(v^2) + 1e-6) for one vector (n a multiple of 4): a single
+// workgroup of 1024 threads; up to 16384 values stay in registers between the
+// sum of squares and the scaled write (larger vectors are read twice).  The sum
+// is formed per thread, then per wave (DPP), then over the 16 waves in order.
+constexpr int kRmsThreads = 1024;
+constexpr int kRmsHeld = 4;  // float4 per thread kept in registers
+
+__global__ __launch_bounds__(kRmsThreads) void rms_kernel(const float* v, int n, float* y) {
+  __shared__ float red[kRmsThreads / 64];
+  const int tid = threadIdx.x, n4 = n / 4;
+  float4 r[kRmsHeld];
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRmsHeld; ++i) {
+    const int f = tid + kRmsThreads * i;
+    r[i] = f < n4 ? gload4(v + 4 * (int64_t)f) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss = fmaf(r[i].x, r[i].x, fmaf(r[i].y, r[i].y, fmaf(r[i].z, r[i].z, fmaf(r[i].w, r[i].w, ss))));
+  }
+  for (int f = tid + kRmsThreads * kRmsHeld; f < n4; f += kRmsThreads) {
+    const float4 t = gload4(v + 4 * (int64_t)f);
+    ss = fmaf(t.x, t.x, fmaf(t.y, t.y, fmaf(t.z, t.z, fmaf(t.w, t.w, ss))));
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRmsThreads / 64; ++i) tot += red[i];
+  const float c = 1.0f / sqrtf(tot / (float)n + 1e-6f);
+#pragma unroll
+  for (int i = 0; i < kRmsHeld; ++i) {
+    const int f = tid + kRmsThreads * i;
+    if (f < n4) *reinterpret_cast<float4*>(y + 4 * (int64_t)f) = mul4(c, r[i]);
+  }
+  for (int f = tid + kRmsThreads * kRmsHeld; f < n4; f += kRmsThreads)
+    *reinterpret_cast<float4*>(y + 4 * (int64_t)f) = mul4(c, gload4(v + 4 * (int64_t)f));
+}
+
 template <bool LDS>
 hipError_t launch_prep_t(const PrepArgs& a, int grid, size_t lds, const LaunchCtx& lc) {
   if (LDS) {
@@ -815,6 +864,13 @@ hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc) {
   const int64_t floats = (int64_t)a.batch * a.k;
   if (floats <= kPrepLdsFloats) return launch_prep_t<true>(a, grid, sizeof(float) * floats, lc);
   return launch_prep_t<false>(a, grid, 0, lc);
+}
+
+hipError_t launch_rms(const float* v, int n, float* y, const LaunchCtx& lc) {
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
+  if (n < 4 || n % 4) return hipErrorInvalidValue;
+  QBL_LAUNCH(rms_kernel, dim3(1), dim3(kRmsThreads), 0, lc, v, n, y);
+  return hipGetLastError();
 }
 
 bool fused_supported(int qtype, int k) {

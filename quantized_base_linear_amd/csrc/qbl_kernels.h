@@ -159,6 +159,8 @@ struct LaunchCtx {
 };
 
 hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc);
+// y = v / sqrt(mean(v^2) + 1e-6), one vector of n floats (n a multiple of 4)
+hipError_t launch_rms(const float* v, int n, float* y, const LaunchCtx& lc);
 hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc);
 // false when the fused path cannot serve this shape (the caller then uses prep + gemv)
 bool fused_supported(int qtype, int k);

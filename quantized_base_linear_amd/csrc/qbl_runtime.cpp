@@ -1228,16 +1228,8 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
 
 // rms of one vector into y (a prep launch with no adapter rows)
 qbl_status run_rms(const float* v, int64_t n, float* y, hipStream_t st) {
-  qbl::PrepArgs p{};
-  p.v[0] = v;
-  p.nv = 1;
-  p.rms = 1;
-  p.batch = 1;
-  p.k = (int)n;
-  p.v_stride = n;
-  p.xin = y;
   KernelTimer tm(1, st);
-  hipError_t e = qbl::launch_prep(p, tm.ctx());
+  hipError_t e = qbl::launch_rms(v, (int)n, y, tm.ctx());
   if (e != hipSuccess) return hip_fail(e, "rms launch");
   tm.stop();
   return QBL_OK;

@@ -141,6 +141,7 @@ const char* hipGetErrorString(hipError_t error) {
 // The kernel launchers: no GPU here.
 namespace qbl {
 hipError_t launch_prep(const PrepArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
+hipError_t launch_rms(const float*, int, float*, const LaunchCtx&) { return hipErrorNoDevice; }
 hipError_t launch_gemv(GemvArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
 bool fused_supported(int, int) { return true; }
 hipError_t launch_fused(FusedArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
