@@ -348,7 +348,10 @@ qbl_status qbl_fault_inject(int32_t point, int32_t after);
  *   op 0: qbl_linear on `index` = linear at batch m;
  *   op 1: qbl_linear_jit on linear `index` with m rows;
  *   op 2: qbl_block / qbl_decode (index ignored; m ignored).
- * The size depends on the current list; query after attach.
+ * The size depends on the current list; query after attach.  Op 0 above batch
+ * 1 always needs a workspace (the inputs are staged there as f16 operands of
+ * the matrix-core GEMV, with the partial sums of workgroups that split K),
+ * with or without adapters.
  * At batch 1 (ops 0 and 2) one launch both computes the adapter shrink and
  * consumes it: each shrink value is stored with the launch's number beside it,
  * and readers wait until they see that number.  Zero the buffer once before its
@@ -366,7 +369,10 @@ qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index, 
  *   y[b][n] = sum_k deq(W)[n][k] x[b][k] + sum_i s_i sum_j B_i[n][j] t_i[b][j],
  *   t_i[b] = A_i x[b]   (a sparse adapter i adds s_i sum_p val_i[p] x[b][col_i[p]]
  *   over row n's entries instead),
- * base sum first, adapters in list order, float32 accumulation.
+ * base sum first, adapters in list order, float32 accumulation.  Above batch 1
+ * the base sum runs on the matrix cores: each input, scaled by a power of two
+ * per batch row, enters as two f16 parts whose sum is within 2^-22 of it
+ * (relative), multiplied by the exact integer codes, float32 sums per block.
  * x: device float32 batch x k_in; y: device float32 batch x n_out (must not
  * alias x); 1 <= batch <= QBL_MAX_BATCH.  Results are deterministic: the same
  * inputs and list give the same bits. */

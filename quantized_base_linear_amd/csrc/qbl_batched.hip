@@ -1,0 +1,611 @@
+// Decode at batch 2..8 on the matrix cores (gfx950).
+//
+// The base product of the dual path for a few inputs ("Deep Technical Design",
+// section 8: the decode GEMV), y[b][n] = sum_k deq(W)[n][k] x[b][k], is a skinny
+// matrix product: every 32-weight block is one v_mfma_f32_16x16x32_f16 with the
+// block's integer codes (exact in f16) as the B operand (16 weight rows) and the
+// inputs as the A operand (16 rows).  The block's scale and minimum multiply the
+// float32 result, so no weight is ever rounded:
+//   y[b][n] = 2^e_b sum_blk ( d[n][blk] S[b][n][blk] + m[n][blk] X[b][blk] ),
+//   S = sum over the block of code * x', X = sum over the block of x',
+// with x' = x 2^-e_b, e_b chosen per batch row so that its largest |x'| lies in
+// [2^14, 2^15).  Each x' is split into two f16 values, x' = hi + lo + r with
+// hi = f16(x'), lo = f16(x' - hi), |r| <= 2^-22 |x'| (plus an absolute 2^-25
+// where lo is subnormal), so the products carry float32-level precision: the A
+// operand's 16 rows are hi of batch rows 0..7 and lo of batch rows 0..7, and
+// the two halves of the result are added at the end.  X is the float32 sum of
+// x' itself.  Low-rank and sparse terms follow in float32, in list order.
+//
+// v_mfma_f32_16x16x32_f16 lanes (checked on the device): A lane l holds row
+// l % 16, inputs 8 (l / 16) .. +7; B lane l holds column l % 16, the same
+// inputs; D lane l holds rows 4 (l / 16) + j, j = 0..3, of column l % 16.  The
+// order of the 32 inputs inside one instruction is free as long as A and B
+// agree, which the q4 formats use to unpack nibbles with two masks (below).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "qbl_device.h"
+#include "qbl_kernels.h"
+
+namespace qbl {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kStageThreads = 256;
+constexpr int kWaves = 4;  // waves of a GEMV workgroup, splitting the blocks of K
+constexpr int kMfmaThreads = 64 * kWaves;
+
+// Codes of one lane's 8 weights as exact f16 values, in the lane's input order.
+// Bits 0x64XX are the f16 value 1024 + XX.
+//   q8_0: 8 offset-binary bytes u (= q + 128), in order: u - 128.  v_perm_b32
+//   picks bytes from {w (bytes 4..7), 0x64646464 (bytes 0..3)}: selector
+//   0x00050004 gives (w.b0, 0x64, w.b1, 0x64), 0x00070006 the upper two.
+__device__ __forceinline__ half8 codes_q8(uint32_t w0, uint32_t w1) {
+  const uint32_t d0 = __builtin_amdgcn_perm(w0, 0x64646464u, 0x00050004u);
+  const uint32_t d1 = __builtin_amdgcn_perm(w0, 0x64646464u, 0x00070006u);
+  const uint32_t d2 = __builtin_amdgcn_perm(w1, 0x64646464u, 0x00050004u);
+  const uint32_t d3 = __builtin_amdgcn_perm(w1, 0x64646464u, 0x00070006u);
+  const half8 h = __builtin_bit_cast(half8, make_uint4(d0, d1, d2, d3));
+  return h - (half8)(_Float16)1152.0f;
+}
+// (a & m) | o in one instruction; a VOP3 encoding takes no literal operand, so
+// the masks come in registers.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+//   q4_sm / q4_K: one 32-bit word of nibbles, weights 0..7 of the lane's share
+//   (byte i: weight 2i in the low nibble, 2i+1 in the high one).  The high
+//   nibbles stay in place, so they read as 16 q; the matching inputs carry a
+//   factor 1/16 instead (exact).  Input order: w0, w4, w1, w5, w2, w6, w3, w7.
+//   lo, hi, magic: 0x000F000F, 0x00F000F0, 0x64006400 (kept in registers).
+__device__ __forceinline__ half8 codes_q4(uint32_t w, uint32_t lo, uint32_t hi, uint32_t magic) {
+  const uint32_t s = w >> 8;
+  const uint32_t d0 = and_or(w, lo, magic);
+  const uint32_t d1 = and_or(w, hi, magic);
+  const uint32_t d2 = and_or(s, lo, magic);
+  const uint32_t d3 = and_or(s, hi, magic);
+  const half8 h = __builtin_bit_cast(half8, make_uint4(d0, d1, d2, d3));
+  return h - (half8)(_Float16)1024.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Scan: workgroup (p, q) covers inputs [256 p, 256 p + 256) of every batch row
+// and adapter rows [16 q, 16 q + 16):
+//   mxpart[p][b] = largest |x[b][k]| over the range (q = 0 only; 0 for rows
+//   b >= batch),
+//   tpart[p][j][b] = sum over the range of A[j][k] x[b][k] (the low-rank shrink
+//   split by range: lane l takes inputs 4 l .. 4 l + 3, then a fixed-order wave
+//   sum).  Wave w takes rows 16 q + 4 w .. + 3, their loads issued together.
+// ---------------------------------------------------------------------------
+constexpr int kScanK = 256;
+constexpr int kScanJ = 16;
+
+struct ScanArgs {
+  const float* x;
+  int64_t x_stride;
+  int batch, k, T, n_ent;
+  PrepEntry ent[kMaxPrepEntries];
+  float* mxpart;   // [P][8]
+  float* tpart;    // [P][T][8]
+};
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  __shared__ __attribute__((aligned(16))) float xs[8][kScanK];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int p = blockIdx.x, k0 = p * kScanK, kn = min(kScanK, a.k - k0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // thread: rows wave and wave + 4, inputs 4 lane ..
+    const int b = wave + 4 * i;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (b < a.batch && 4 * lane < kn) v = *gp(reinterpret_cast<const f32x4*>(a.x + (int64_t)b * a.x_stride + k0) + lane);
+    *reinterpret_cast<f32x4*>(&xs[b][4 * lane]) = v;
+    if (blockIdx.y == 0) {
+      float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if (lane == 0) a.mxpart[p * 8 + b] = mx;
+    }
+  }
+  const int j0 = blockIdx.y * kScanJ + 4 * wave;
+  f32x4 w[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    w[u] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    if (j0 + u < a.T && 4 * lane < kn) {
+      const int j = j0 + u;
+      int e = 0, base = 0;
+      while (base + a.ent[e].rank <= j) base += a.ent[e++].rank;
+      w[u] = *gp(reinterpret_cast<const f32x4*>(a.ent[e].A + (int64_t)(j - base) * a.k + k0) + lane);
+    }
+  }
+  __syncthreads();
+  if (j0 >= a.T) return;
+  f32x4 xv[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) xv[b] = *reinterpret_cast<const f32x4*>(&xs[b][4 * lane]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (j0 + u >= a.T) break;
+    float acc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      acc[b] = wave_sum(fmaf(w[u].x, xv[b].x, fmaf(w[u].y, xv[b].y, fmaf(w[u].z, xv[b].z, w[u].w * xv[b].w))));
+    if (lane < 8) {
+      float v = acc[0];
+#pragma unroll
+      for (int b = 1; b < 8; ++b) v = lane == b ? acc[b] : v;
+      a.tpart[((int64_t)p * a.T + j0 + u) * 8 + lane] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage: workgroups [0, nblk / 32): thread (b = tid / 32, block 32 wg + tid % 32)
+// writes the A-operand values of the block in instruction order:
+//   frag[blk][l] for lane l = 16 g + r: row r < 8: hi of batch row r, r >= 8:
+//   lo of batch row r - 8, inputs 8 g .. 8 g + 7 of the block (permuted and
+//   scaled for the q4 formats as codes_q4 expects);
+//   xsum[blk][r] = X of batch row r for r < 8 (float32, input order), 0 for r >= 8;
+//   ex[b] = e_b, from the scan's partial maxima.
+// Rows b >= batch are zero.  The workgroups after those add the scan's partial
+// shrink sums in range order: t[b][j] = sum_p tpart[p][j][b].
+// ---------------------------------------------------------------------------
+template <int QT>
+__global__ __launch_bounds__(256) void stage_kernel(const float* x, int64_t x_stride, int batch, int K, int P, int T,
+                                                    const float* mxpart, const float* tpart, float* t, u32x4* frag,
+                                                    float* xsum, int* ex) {
+  const int tid = threadIdx.x, nblk = K / 32, conv = (nblk + 31) / 32;
+  if ((int)blockIdx.x >= conv) {  // 16 lanes per output (j, b): ranges l16, l16 + 16, ..., then a fixed-order sum
+    const int idx = ((int)blockIdx.x - conv) * 16 + (tid >> 4), l16 = tid & 15;
+    const int j = idx >> 3, b = idx & 7;
+    const bool ok = j < T && b < batch;
+    float s = 0.0f;
+    if (ok)
+      for (int q = l16; q < P; q += 16) s += tpart[((int64_t)q * T + j) * 8 + b];
+    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (ok && l16 == 0) t[(int64_t)b * T + j] = s;
+    return;
+  }
+  const int b = tid >> 5, l32 = tid & 31;
+  float mx = 0.0f;
+  for (int q = l32; q < P; q += 32) mx = fmaxf(mx, mxpart[q * 8 + b]);
+  for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  int e = 0;
+  if (mx > 0.0f) {
+    int me;
+    frexpf(mx, &me);  // mx in [2^(me-1), 2^me)
+    e = me - 15;
+  }
+  if (blockIdx.x == 0 && l32 == 0) ex[b] = e;
+  const int blk = blockIdx.x * 32 + l32;
+  if (blk >= nblk) return;
+  const bool live = b < batch;
+  const float* xr = x + (int64_t)b * x_stride;
+  u32x4* dst = frag + (int64_t)blk * 64 + b;
+  float s = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      const float4 p = gload4(xr + 32 * blk + 8 * g), q = gload4(xr + 32 * blk + 8 * g + 4);
+      v[0] = p.x, v[1] = p.y, v[2] = p.z, v[3] = p.w, v[4] = q.x, v[5] = q.y, v[6] = q.z, v[7] = q.w;
+    }
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[i] = ldexpf(v[i], -e);
+      s += o[i];
+    }
+    if constexpr (QT != QBL_FMT_Q8) {  // input order of codes_q4, high-nibble inputs / 16
+      const float tt[8] = {o[0], o[4], o[1] * 0.0625f, o[5] * 0.0625f, o[2], o[6], o[3] * 0.0625f, o[7] * 0.0625f};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = tt[i];
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __half h0 = __float2half_rn(o[2 * i]), h1 = __float2half_rn(o[2 * i + 1]);
+      const __half l0 = __float2half_rn(o[2 * i] - __half2float(h0));
+      const __half l1 = __float2half_rn(o[2 * i + 1] - __half2float(h1));
+      hw[i] = (uint32_t)__half_as_ushort(h0) | ((uint32_t)__half_as_ushort(h1) << 16);
+      lw[i] = (uint32_t)__half_as_ushort(l0) | ((uint32_t)__half_as_ushort(l1) << 16);
+    }
+    const u32x4 hv = {hw[0], hw[1], hw[2], hw[3]}, lv = {lw[0], lw[1], lw[2], lw[3]};
+    dst[16 * g] = hv;
+    dst[16 * g + 8] = lv;
+  }
+  float* xs = xsum + (int64_t)blk * 16;
+  xs[b] = s;
+  xs[b + 8] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV.  A workgroup owns 64 consecutive rows of one segment (4 tiles of 16)
+// and a range of the blocks of K (split-K over KS workgroups when the rows
+// alone give too few workgroups).  Its 4 waves take the range's slabs in turn
+// (wave w: slabs w, w + 4, ...); a slab is the next 64 bytes of all 64 rows
+// (2 q8_0 blocks or 4 q4 blocks).  A wave loads a slab with 16-byte loads that
+// run along the rows (a quarter-wave covers 64 contiguous bytes of each of four
+// rows), together with the slab's scales and the A operands of its blocks, one
+// slab ahead of the arithmetic; it puts the slab in its own LDS region (rows 80
+// bytes apart, so that the 64 lanes of an operand read hit 64 different banks)
+// and feeds the instructions from there.
+// The waves' partial sums meet in LDS and are added in wave order, hi part then
+// lo part.  With split-K each workgroup stores its partial sums and a second
+// launch adds the KS partial sums of each output in split order and finishes
+// the rows (the kernel boundary orders the two; no fence inside a launch).
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kRowStride = 80;  // LDS bytes per slab row
+
+template <int QT>
+struct SlabFmt {
+  static constexpr int S = QT == QBL_FMT_Q8 ? 2 : 4;           // blocks per slab
+  static constexpr int kBpb = QT == QBL_FMT_Q8 ? 32 : 16;      // weight bytes per block
+  static constexpr int kScE = QT == QBL_FMT_Q8 ? 2 : 4;        // q8_0 d, q4_sm (d | m << 16)
+  static constexpr int kScStride = QT == QBL_FMT_Q8 ? 4 : QT == QBL_FMT_Q4 ? 20 : 16;
+  static constexpr int kScLoads = QT == QBL_FMT_Q4K ? 0 : S;    // 64 S scale values / 64 lanes
+  static constexpr int kXBytes = QT == QBL_FMT_Q8 ? 0 : S * 64; // block sums X, [j][16] floats
+  static constexpr int kScOff = 64 * kRowStride;
+  static constexpr int kXOff = kScOff + 64 * kScStride;
+  static constexpr int kWave = kXOff + kXBytes;                 // LDS bytes per wave
+};
+
+// What a wave loads for one slab.
+template <int QT>
+struct SlabRegs {
+  using F = SlabFmt<QT>;
+  u32x4 w[4];
+  uint32_t sc[F::kScLoads > 0 ? F::kScLoads : 1];
+  u32x4 hd;                // q4_K: the row's super-block header (lane = row)
+  u32x4 xf[F::S];
+  f32x4 X;                 // q4: lanes 0..31, X of block lane / 4, batch rows 4 (lane % 4) ..
+};
+
+struct MfmaSplit {
+  int ks;                  // workgroups per 64 rows, splitting the blocks
+  int per;                 // blocks per split (a multiple of the slab)
+  float* partial;          // ks > 1: [seg][ks][8][n] partial sums
+  int64_t poff[kMaxSegs];  // segment offsets into partial (floats)
+};
+
+// Output (b, n) of segment g from its base sum s (before the 2^e_b scale):
+// scale, then the adapters in list order, then the store.
+__device__ __forceinline__ void finish_output(const GemvArgs& a, const GemvSeg& g, const int* ex, int b, int n,
+                                              float s) {
+  float v = ldexpf(s, ex[b]);
+  for (int i = 0; i < g.lora.n_ad; ++i) {
+    const int rk = g.lora.rank[i];
+    float p = 0.0f;
+    if (rk == 0) {  // sparse delta: row n's entries against x[b]
+      const float* xb = a.x + (int64_t)b * a.x_stride;
+      const uint32_t e1 = g.lora.rp[i][n + 1];
+      for (uint32_t e = g.lora.rp[i][n]; e < e1; ++e) p = fmaf(h2f(g.lora.sv[i][e]), xb[g.lora.ci[i][e]], p);
+    } else {
+      const float* Br = g.lora.B[i] + (int64_t)n * rk;
+      const float* tb = a.t + (int64_t)b * a.t_stride + g.lora.toff[i];
+#pragma unroll 8
+      for (int q = 0; q < rk; ++q) p = fmaf(Br[q], tb[q], p);
+    }
+    v = fmaf(g.lora.scale[i], p, v);
+  }
+  g.y[(int64_t)b * g.y_stride + n] = v;
+}
+
+template <int QT>
+__global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_mfma_kernel(GemvArgs a, MfmaSplit sp, const u32x4* frag,
+                                                                 const float* xsum, const int* ex) {
+  using F = SlabFmt<QT>;
+  constexpr int S = F::S;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * F::kWave];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int wg = blockIdx.x;
+  const int si = (a.nseg > 2 && wg >= a.seg[2].wg_begin) ? 2 : (a.nseg > 1 && wg >= a.seg[1].wg_begin) ? 1 : 0;
+  const GemvSeg& g = a.seg[si];
+  const int local = wg - g.wg_begin;
+  const int rg = local / sp.ks, ks = local % sp.ks;
+  const int row0 = rg * 64;
+  const int K = a.k, nblk = K / 32;
+  const int kb0 = min(nblk, ks * sp.per), kb1 = min(nblk, kb0 + sp.per);
+  const int nsl = (kb1 - kb0 + S - 1) / S;
+  const int64_t rbytes = Fmt<QT>::row_bytes(K);
+
+  unsigned char* W = lds + wave * F::kWave;
+  unsigned char* SC = W + F::kScOff;
+  unsigned char* XL = W + F::kXOff;
+
+  // load slab sl of this workgroup's range (rows and blocks clamped to valid ones)
+  auto issue = [&](SlabRegs<QT>& r, int sl) {
+    const int b0 = kb0 + S * sl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = 16 * i + (lane >> 2), c = lane & 3;
+      const int grow = min(row0 + rl, g.n - 1);
+      int64_t off;
+      if constexpr (QT == QBL_FMT_Q8)
+        off = (int64_t)min(b0 + (c >> 1), nblk - 1) * 32 + 16 * (c & 1);
+      else
+        off = (int64_t)min(b0 + c, nblk - 1) * 16;
+      r.w[i] = *gp(reinterpret_cast<const u32x4*>(g.qs + (int64_t)grow * rbytes + off));
+    }
+    if constexpr (QT == QBL_FMT_Q4K) {
+      const int grow = min(row0 + lane, g.n - 1);
+      r.hd = *gp(reinterpret_cast<const u32x4*>(g.sc) + (int64_t)grow * (K / 256) + b0 / 8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < F::kScLoads; ++i) {
+        const int e = 64 * i + lane, rl = e / S, j = e % S;
+        const int64_t idx = (int64_t)min(row0 + rl, g.n - 1) * nblk + min(b0 + j, nblk - 1);
+        if constexpr (QT == QBL_FMT_Q8)
+          r.sc[i] = *gp(reinterpret_cast<const uint16_t*>(g.sc) + idx);
+        else
+          r.sc[i] = *gp(reinterpret_cast<const uint32_t*>(g.sc) + idx);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < S; ++j) r.xf[j] = *gp(frag + (int64_t)min(b0 + j, nblk - 1) * 64 + lane);
+    if constexpr (QT != QBL_FMT_Q8)
+      r.X = *gp(reinterpret_cast<const f32x4*>(xsum + (int64_t)min(b0 + ((lane >> 2) & (S - 1)), nblk - 1) * 16) +
+                (lane & 3));
+  };
+  // the loaded slab into this wave's LDS region
+  auto stash = [&](const SlabRegs<QT>& r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(W + (16 * i + (lane >> 2)) * kRowStride + 16 * (lane & 3)) = r.w[i];
+    if constexpr (QT == QBL_FMT_Q4K) {
+      *reinterpret_cast<u32x4*>(SC + lane * 16) = r.hd;
+    } else {
+#pragma unroll
+      for (int i = 0; i < F::kScLoads; ++i) {
+        const int e = 64 * i + lane, rl = e / S, j = e % S;
+        if constexpr (QT == QBL_FMT_Q8)
+          *reinterpret_cast<uint16_t*>(SC + rl * F::kScStride + 2 * j) = (uint16_t)r.sc[i];
+        else
+          *reinterpret_cast<uint32_t*>(SC + rl * F::kScStride + 4 * j) = r.sc[i];
+      }
+    }
+    if constexpr (QT != QBL_FMT_Q8)
+      if (lane < 4 * S) *reinterpret_cast<f32x4*>(XL + 16 * lane) = r.X;
+  };
+
+  f32x4v acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = (f32x4v){0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  // nibble masks for codes_q4, in registers (opaque to the optimiser so that
+  // they stay there instead of being folded back into literal operands)
+  uint32_t k_lo = 0x000F000Fu, k_hi = 0x00F000F0u, k_magic = 0x64006400u;
+  asm("" : "+v"(k_lo), "+v"(k_hi), "+v"(k_magic));
+
+  SlabRegs<QT> r;
+  if (wave < nsl) issue(r, wave);
+  for (int sl = wave; sl < nsl; sl += kWaves) {
+    stash(r);
+    u32x4 xf[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) xf[j] = r.xf[j];
+    if (sl + kWaves < nsl) issue(r, sl + kWaves);
+    const int nb = min(S, kb1 - (kb0 + S * sl));
+    u32x4 hd[4];
+    if constexpr (QT == QBL_FMT_Q4K) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) hd[t] = *reinterpret_cast<const u32x4*>(SC + (16 * t + col) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      if (j >= nb) break;
+      const half8 xv = __builtin_bit_cast(half8, xf[j]);
+      f32x4 xs = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (QT != QBL_FMT_Q8) xs = *reinterpret_cast<const f32x4*>(XL + 64 * j + 16 * grp);
+      f32x4v o[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const unsigned char* wr = W + (16 * t + col) * kRowStride;
+        half8 wv;
+        if constexpr (QT == QBL_FMT_Q8) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(wr + 32 * j + 8 * grp);
+          wv = codes_q8(w.x, w.y);
+        } else {
+          wv = codes_q4(*reinterpret_cast<const uint32_t*>(wr + 16 * j + 4 * grp), k_lo, k_hi, k_magic);
+        }
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, zero, 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if constexpr (QT == QBL_FMT_Q8) {
+          const float d = h2f(*reinterpret_cast<const uint16_t*>(SC + (16 * t + col) * F::kScStride + 2 * j));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(d, o[t][q], acc[t][q]);
+        } else {
+          float d, m;
+          if constexpr (QT == QBL_FMT_Q4) {
+            const uint32_t dm = *reinterpret_cast<const uint32_t*>(SC + (16 * t + col) * F::kScStride + 4 * j);
+            d = h2f(dm);
+            m = h2f(dm >> 16);
+          } else {
+            float M;
+            q4k_step_offset(make_uint4(hd[t].x, hd[t].y, hd[t].z, hd[t].w), (kb0 + S * sl + j) & 7, d, M);
+            m = -M;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(m, xs[q], fmaf(d, o[t][q], acc[t][q]));
+        }
+      }
+    }
+  }
+
+  // the four waves' sums (the slab regions are reused: wait until every wave is done with them)
+  __syncthreads();
+  f32x4v* part = reinterpret_cast<f32x4v*>(lds);  // [wave][tile][lane]
+#pragma unroll
+  for (int t = 0; t < 4; ++t) part[(wave * 4 + t) * 64 + lane] = acc[t];
+  __syncthreads();
+
+  // Rows of the workgroup: thread -> (batch row b, row rr), consecutive threads
+  // on consecutive rows.  Hi of row b sits in lane 16 (b / 4) + col, element
+  // b % 4; lo in lane 16 (2 + b / 4) + col.
+  auto wg_sum = [&](int b, int rr) {
+    const int t = rr >> 4, c = rr & 15, j = b & 3;
+    const int lh = 16 * (b >> 2) + c, ll = lh + 32;
+    float hi = part[t * 64 + lh][j], lo = part[t * 64 + ll][j];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      hi += part[(w * 4 + t) * 64 + lh][j];
+      lo += part[(w * 4 + t) * 64 + ll][j];
+    }
+    return hi + lo;
+  };
+  if (sp.ks == 1) {  // thread -> (row rr, batch row b), b fastest: 8 lanes share a row of each B_i
+    for (int idx = tid; idx < 64 * 8; idx += kMfmaThreads) {
+      const int b = idx & 7, rr = idx >> 3, n = row0 + rr;
+      if (b < a.batch && n < g.n) finish_output(a, g, ex, b, n, wg_sum(b, rr));
+    }
+    return;
+  }
+  float* pbase = sp.partial + sp.poff[si];
+  for (int idx = tid; idx < 64 * 8; idx += kMfmaThreads) {
+    const int b = idx >> 6, rr = idx & 63, n = row0 + rr;
+    if (b < a.batch && n < g.n) pbase[((int64_t)ks * 8 + b) * g.n + n] = wg_sum(b, rr);
+  }
+}
+
+// Split-K: output (b, n) = the ks partial sums in split order, finished.  One
+// thread per output, batch row fastest (8 lanes share a row of each B_i);
+// 32 rows per workgroup over the rows of all segments.
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemvArgs a, MfmaSplit sp, const int* ex) {
+  const int b = threadIdx.x & 7;
+  int n = blockIdx.x * 32 + (threadIdx.x >> 3);
+  int si = 0;
+  while (si + 1 < a.nseg && n >= a.seg[si].n) n -= a.seg[si++].n;
+  const GemvSeg& g = a.seg[si];
+  if (n >= g.n || b >= a.batch) return;
+  const float* p = sp.partial + sp.poff[si] + (int64_t)b * g.n + n;
+  float s = 0.0f;
+  for (int q = 0; q < sp.ks; ++q) s += p[(int64_t)q * 8 * g.n];
+  finish_output(a, g, ex, b, n, s);
+}
+
+// Workgroups per 64 rows: about as many workgroups as the chip holds at once
+// (256 compute units, 4 workgroups each), each keeping at least 8 slabs.
+int split_ks(int64_t row_groups, int nblk, int slab) {
+  const int64_t want = 1024 / row_groups;
+  const int64_t most = std::max<int64_t>(1, (nblk + slab - 1) / slab / 8);
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, 16}));
+}
+
+template <int QT>
+hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, float* t, void* stage, int ks_force,
+                     const LaunchCtx& prep_lc, const LaunchCtx& lc) {
+  const int nblk = a.k / 32, P = (a.k + kScanK - 1) / kScanK;
+  char* st = static_cast<char*>(stage);
+  u32x4* frag = reinterpret_cast<u32x4*>(st);
+  float* xsum = reinterpret_cast<float*>(st + (int64_t)nblk * 1024);
+  int* ex = reinterpret_cast<int*>(xsum + (int64_t)nblk * 16);
+  float* mxpart = reinterpret_cast<float*>(st + mfma_stage_only_bytes(a.k));
+  float* tpart = mxpart + (int64_t)P * 8;
+  ScanArgs sa{};
+  sa.x = a.x;
+  sa.x_stride = a.x_stride;
+  sa.batch = a.batch;
+  sa.k = a.k;
+  sa.T = T;
+  sa.n_ent = n_ent;
+  for (int i = 0; i < n_ent; ++i) sa.ent[i] = ent[i];
+  sa.mxpart = mxpart;
+  sa.tpart = tpart;
+  // the timing events of prep_lc go around the scan and the stage launches
+  LaunchCtx p1 = prep_lc, p2 = prep_lc;
+  p1.stop = nullptr;
+  p2.start = nullptr;
+  QBL_LAUNCH(scan_kernel, dim3(P, std::max(1, (T + kScanJ - 1) / kScanJ)), dim3(256), 0, p1, sa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int conv = (nblk + 31) / 32, tred = (T * 8 + 15) / 16;
+  QBL_LAUNCH(stage_kernel<QT>, dim3(conv + tred), dim3(256), 0, p2, a.x, a.x_stride, a.batch, a.k, P, T, mxpart,
+             tpart, t, frag, xsum, ex);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int S = SlabFmt<QT>::S;
+  int64_t row_groups = 0;
+  for (int i = 0; i < a.nseg; ++i) row_groups += (a.seg[i].n + 63) / 64;
+  MfmaSplit sp{};
+  sp.ks = ks_force > 0 ? ks_force : split_ks(row_groups, nblk, S);
+  const int nslab = (nblk + S - 1) / S;
+  sp.per = (nslab + sp.ks - 1) / sp.ks * S;
+  sp.partial = reinterpret_cast<float*>(st + mfma_stage_only_bytes(a.k) + mfma_scan_bytes(a.k, T));
+  int wg = 0;
+  int64_t po = 0, rows = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg[i].wg_begin = wg;
+    wg += (a.seg[i].n + 63) / 64 * sp.ks;
+    sp.poff[i] = po;
+    po += (int64_t)sp.ks * 8 * a.seg[i].n;
+    rows += a.seg[i].n;
+  }
+  if (sp.ks > 1 && po * 4 > mfma_partial_bytes(row_groups * 64)) return hipErrorInvalidValue;
+  a.grid = wg;
+  if (sp.ks == 1) {
+    QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(kMfmaThreads), 0, lc, a, sp, frag, xsum, ex);
+    return hipGetLastError();
+  }
+  // the timing events of lc go around both launches
+  LaunchCtx first = lc, second = lc;
+  first.stop = nullptr;
+  second.start = nullptr;
+  QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(kMfmaThreads), 0, first, a, sp, frag, xsum, ex);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  QBL_LAUNCH(split_reduce_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, second, a, sp, ex);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Staging layout: A operands [nblk][64] x 16 bytes, block sums [nblk][16]
+// floats, 8 exponents; the scan's partial maxima [P][8] and partial shrink sums
+// [P][T][8]; then the split-K partial sums.
+int64_t mfma_stage_only_bytes(int k) {
+  const int64_t nblk = k / 32;
+  return (nblk * (1024 + 64) + 32 + 255) / 256 * 256;
+}
+int64_t mfma_scan_bytes(int k, int T) {
+  const int64_t P = (k + kScanK - 1) / kScanK;
+  return (P * 8 * 4 * (1 + (int64_t)T) + 255) / 256 * 256;
+}
+int64_t mfma_partial_bytes(int64_t rows) { return rows * 8 * 16 * 4; }  // up to 16 splits
+int64_t mfma_stage_bytes(int64_t rows, int k, int T) {
+  return mfma_stage_only_bytes(k) + mfma_scan_bytes(k, T) +
+         (mfma_partial_bytes((rows + 63) / 64 * 64) + 255) / 256 * 256;
+}
+
+hipError_t launch_gemv_mfma(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, void* stage, int ks,
+                            const LaunchCtx& prep_lc, const LaunchCtx& lc) {
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
+  if (a.batch < 2 || a.batch > 8 || a.nseg < 1 || a.nseg > kMaxSegs || !stage) return hipErrorInvalidValue;
+  if (a.k < 32 || a.k % (a.qtype == QBL_FMT_Q4K ? 256 : 32) || a.x_stride % 4) return hipErrorInvalidValue;
+  if (reinterpret_cast<uintptr_t>(stage) % 256 || reinterpret_cast<uintptr_t>(a.x) % 16) return hipErrorInvalidValue;
+  if (ks < 0 || ks > 16 || n_ent < 0 || n_ent > kMaxPrepEntries || T < 0 || (T > 0 && !a.t)) return hipErrorInvalidValue;
+  int rk = 0;
+  for (int i = 0; i < n_ent; ++i) {
+    if (ent[i].toff != rk || ent[i].rank <= 0) return hipErrorInvalidValue;
+    rk += ent[i].rank;
+  }
+  if (rk != T || (T > 0 && a.t_stride != T)) return hipErrorInvalidValue;
+  float* t = const_cast<float*>(a.t);
+  switch (a.qtype) {
+    case QBL_FMT_Q8: return launch_qt<QBL_FMT_Q8>(a, ent, n_ent, T, t, stage, ks, prep_lc, lc);
+    case QBL_FMT_Q4: return launch_qt<QBL_FMT_Q4>(a, ent, n_ent, T, t, stage, ks, prep_lc, lc);
+    case QBL_FMT_Q4K: return launch_qt<QBL_FMT_Q4K>(a, ent, n_ent, T, t, stage, ks, prep_lc, lc);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qbl

@@ -11,7 +11,7 @@ namespace qbl {
 // Launch `kernel` on lc.stream, with lc's timing events when they are set.
 #define QBL_LAUNCH(kernel, grid, block, lds, lc, ...)                                              \
   do {                                                                                             \
-    if ((lc).start)                                                                                \
+    if ((lc).start || (lc).stop)                                                                   \
       hipExtLaunchKernelGGL(kernel, grid, block, lds, (lc).stream, (lc).start, (lc).stop, 0,       \
                             __VA_ARGS__);                                                          \
     else                                                                                           \
@@ -162,6 +162,20 @@ hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc);
 // y = v / sqrt(mean(v^2) + 1e-6), one vector of n floats (n a multiple of 4)
 hipError_t launch_rms(const float* v, int n, float* y, const LaunchCtx& lc);
 hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc);
+// Batch 2..8 on the matrix cores (no input glue): a scan launch (maxima of the
+// inputs and the low-rank shrink by input range), a stage launch (the inputs as
+// f16 instruction operands, the shrink results t into a.t, [batch][T]) -- both
+// timed by prep_lc -- then the GEMV launch and, when K is split, a reduce launch
+// (both timed by lc).  `stage`: mfma_stage_bytes(rows, k, T) bytes, rows = all
+// output rows of the launch, 256-byte aligned.  ent: the shrink entries with
+// toff = running sum of the ranks.  ks: workgroups per 64 rows splitting K
+// (1..16; 0 picks it from the shape).
+int64_t mfma_stage_only_bytes(int k);
+int64_t mfma_scan_bytes(int k, int T);
+int64_t mfma_partial_bytes(int64_t rows);
+int64_t mfma_stage_bytes(int64_t rows, int k, int T);
+hipError_t launch_gemv_mfma(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, void* stage, int ks,
+                            const LaunchCtx& prep_lc, const LaunchCtx& lc);
 // false when the fused path cannot serve this shape (the caller then uses prep + gemv)
 bool fused_supported(int qtype, int k);
 hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc);

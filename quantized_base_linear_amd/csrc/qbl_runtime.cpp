@@ -1089,7 +1089,8 @@ int blocks_tmax(const ListImpl* L, int first_block, int n_blocks) {
 // c the RMS scale when rms != 0.  At batch 1 the glue, the shrink and the GEMV
 // share one launch (the shrink results pass through t_buf as tagged words);
 // otherwise the prep kernel (glue and/or shrink) runs first, then one GEMV per
-// quantisation type present.
+// quantisation type present: at batch 2..8 the matrix-core GEMV, which stages
+// its inputs in `stage` first.
 constexpr int kSpinLimit = 1 << 22;  // ~0.1 s of s_sleep(1) before a wait gives up
 
 // Numbers that tag the shrink results one workgroup hands to others within a
@@ -1105,7 +1106,7 @@ uint32_t next_tag() {
 qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, float* const* outs,
                      int nlin, const float* const* vin, int nv, int rms, int batch, int64_t v_stride,
                      float* xin_buf, float* t_buf, hipStream_t st, bool sum_ok = false,
-                     bool* summed = nullptr) {
+                     bool* summed = nullptr, void* stage = nullptr) {
   if (summed) *summed = false;
   const int64_t K = base->lin[(size_t)lin[0]].k;
   int T = 0;
@@ -1187,7 +1188,8 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
   p.n_ent = n_ent;
   const bool glue = rms || nv > 1;
   const float* x = vin[0];
-  if (glue || T > 0) {
+  if (batch > 1 && glue) return fail(QBL_E_ARG, "input glue runs at batch 1 only");
+  if (batch == 1 && (glue || T > 0)) {
     for (int i = 0; i < nv; ++i) p.v[i] = vin[i];
     p.nv = nv;
     p.rms = rms;
@@ -1217,6 +1219,16 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     a.x_stride = glue ? K : v_stride;
     a.t = T > 0 ? t_buf : nullptr;
     a.t_stride = T;
+    if (batch > 1) {
+      if (!stage) return fail(QBL_E_ARG, "the batched GEMV needs a staging buffer");
+      KernelTimer ts(1, st);
+      KernelTimer tm(0, st);
+      hipError_t e = qbl::launch_gemv_mfma(a, ent, n_ent, T, stage, 0, ts.ctx(), tm.ctx());
+      if (e != hipSuccess) return hip_fail(e, "batched gemv launch");
+      ts.stop();
+      tm.stop();
+      continue;
+    }
     KernelTimer tm(0, st);
     hipError_t e = qbl::launch_gemv(a, tm.ctx());
     if (e != hipSuccess) return hip_fail(e, "gemv launch");
@@ -1285,10 +1297,14 @@ qbl_status check_ws(void* ws, int64_t ws_bytes, int64_t need) {
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 // qbl_linear: the shrink results t, float per batch row, or at batch 1 (the
-// fused launch) kTCopies copies of one tagged 8-byte word each.
-int64_t linear_ws_bytes(int64_t batch, int64_t T) {
+// fused launch) kTCopies copies of one tagged 8-byte word each; above batch 1
+// the matrix-core GEMV's staged inputs follow t.
+int64_t linear_t_bytes(int64_t batch, int64_t T) {
   if (T == 0) return 0;
   return align_up(batch == 1 ? qbl::kTCopies * qbl::t_copy_stride(T) * 8 : batch * T * 4);
+}
+int64_t linear_ws_bytes(int64_t batch, int64_t T, int64_t n, int64_t k) {
+  return linear_t_bytes(batch, T) + (batch > 1 ? align_up(qbl::mfma_stage_bytes(n, (int)k, (int)T)) : 0);
 }
 
 }  // namespace
@@ -1302,7 +1318,7 @@ extern "C" qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int3
     if (op == 0) {
       if (index < 0 || index >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", index);
       if (m < 1 || m > QBL_MAX_BATCH) return fail(QBL_E_LIMIT, "batch %d outside 1..%d", m, QBL_MAX_BATCH);
-      *bytes_out = linear_ws_bytes(m, L->total_rank[(size_t)index]);
+      *bytes_out = linear_ws_bytes(m, L->total_rank[(size_t)index], b->lin[(size_t)index].n, b->lin[(size_t)index].k);
       return QBL_OK;
     }
     if (op == 1) {
@@ -1341,14 +1357,16 @@ extern "C" qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x,
     std::lock_guard<std::mutex> g(comp->mu);
     auto L = std::atomic_load(&comp->list);
     const int T = L->total_rank[(size_t)linear];
-    if (qbl_status s = check_ws(ws, ws_bytes, linear_ws_bytes(batch, T))) return s;
+    const DevLinear& D = b->lin[(size_t)linear];
+    if (qbl_status s = check_ws(ws, ws_bytes, linear_ws_bytes(batch, T, D.n, D.k))) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int lin[1] = {linear};
     float* outs[1] = {y};
     const float* v[1] = {x};
-    const DevLinear& D = b->lin[(size_t)linear];
     const ListUse use{L.get(), st, !L->plan[(size_t)linear].empty()};
-    return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), st);
+    void* stage = batch > 1 ? static_cast<char*>(ws) + linear_t_bytes(batch, T) : nullptr;
+    return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), st, false,
+                     nullptr, stage);
   })
 }
 

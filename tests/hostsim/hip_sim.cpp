@@ -143,6 +143,10 @@ namespace qbl {
 hipError_t launch_prep(const PrepArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
 hipError_t launch_rms(const float*, int, float*, const LaunchCtx&) { return hipErrorNoDevice; }
 hipError_t launch_gemv(GemvArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
+int64_t mfma_stage_bytes(int64_t, int, int) { return 0; }
+hipError_t launch_gemv_mfma(GemvArgs&, const PrepEntry*, int, int, void*, int, const LaunchCtx&, const LaunchCtx&) {
+  return hipErrorNoDevice;
+}
 bool fused_supported(int, int) { return true; }
 hipError_t launch_fused(FusedArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
 hipError_t launch_jit(const JitArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
