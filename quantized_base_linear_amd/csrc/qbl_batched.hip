@@ -243,6 +243,7 @@ __global__ __launch_bounds__(256) void stage_kernel(const float* x, int64_t x_st
 // ---------------------------------------------------------------------------
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRowStride = 80;  // LDS bytes per slab row
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource flags: raw 32-bit data
 
 template <int QT>
 struct SlabFmt {
@@ -321,39 +322,53 @@ __global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_
   unsigned char* SC = W + F::kScOff;
   unsigned char* XL = W + F::kXOff;
 
-  // load slab sl of this workgroup's range (rows and blocks clamped to valid ones)
-  auto issue = [&](SlabRegs<QT>& r, int sl) {
-    const int b0 = kb0 + S * sl;
+  // Slab loads are buffer loads: a per-lane byte offset fixed for the whole
+  // loop plus the slab's offset (wave-uniform).  Reads past the end of a
+  // buffer return zero; rows past n and blocks past the range land there or in
+  // the next row, and neither is used.
+  const uint32_t n32 = (uint32_t)g.n, nb32 = (uint32_t)nblk;
+  const __amdgpu_buffer_rsrc_t qs_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.qs), 0,
+                                                                         (int)(n32 * (uint32_t)rbytes), kRsrcWord3);
+  uint32_t sc_bytes;
+  if constexpr (QT == QBL_FMT_Q4K) sc_bytes = n32 * (uint32_t)(K / 256) * 16u;
+  else sc_bytes = n32 * nb32 * (uint32_t)F::kScE;
+  const __amdgpu_buffer_rsrc_t sc_r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.sc), 0, (int)sc_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t fr_r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(frag), 0, (int)(nb32 * 1024u), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xs_r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(xsum), 0, (int)(nb32 * 64u), kRsrcWord3);
+  uint32_t w_off[4], s_off[F::kScLoads > 0 ? F::kScLoads : 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rl = 16 * i + (lane >> 2), c = lane & 3;
-      const int grow = min(row0 + rl, g.n - 1);
-      int64_t off;
-      if constexpr (QT == QBL_FMT_Q8)
-        off = (int64_t)min(b0 + (c >> 1), nblk - 1) * 32 + 16 * (c & 1);
-      else
-        off = (int64_t)min(b0 + c, nblk - 1) * 16;
-      r.w[i] = *gp(reinterpret_cast<const u32x4*>(g.qs + (int64_t)grow * rbytes + off));
-    }
+  for (int i = 0; i < 4; ++i) w_off[i] = (uint32_t)(row0 + 16 * i + (lane >> 2)) * (uint32_t)rbytes + 16u * (lane & 3);
+#pragma unroll
+  for (int i = 0; i < F::kScLoads; ++i) {
+    const int e = 64 * i + lane, rl = e / S, j = e % S;
+    s_off[i] = ((uint32_t)(row0 + rl) * nb32 + (uint32_t)j) * (uint32_t)F::kScE;
+  }
+  const uint32_t h_off = (uint32_t)(row0 + lane) * (uint32_t)(K / 256) * 16u;
+  const uint32_t x_off = (uint32_t)((lane >> 2) & (S - 1)) * 64u + 16u * (lane & 3);
+
+  auto issue = [&](SlabRegs<QT>& r, int sl) {
+    const int b0 = kb0 + S * sl;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(qs_r, w_off[i], b0 * F::kBpb, 0);
     if constexpr (QT == QBL_FMT_Q4K) {
-      const int grow = min(row0 + lane, g.n - 1);
-      r.hd = *gp(reinterpret_cast<const u32x4*>(g.sc) + (int64_t)grow * (K / 256) + b0 / 8);
+      r.hd = __builtin_amdgcn_raw_buffer_load_b128(sc_r, h_off, (b0 / 8) * 16, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < F::kScLoads; ++i) {
-        const int e = 64 * i + lane, rl = e / S, j = e % S;
-        const int64_t idx = (int64_t)min(row0 + rl, g.n - 1) * nblk + min(b0 + j, nblk - 1);
         if constexpr (QT == QBL_FMT_Q8)
-          r.sc[i] = *gp(reinterpret_cast<const uint16_t*>(g.sc) + idx);
+          r.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(sc_r, s_off[i], b0 * 2, 0);
         else
-          r.sc[i] = *gp(reinterpret_cast<const uint32_t*>(g.sc) + idx);
+          r.sc[i] = __builtin_amdgcn_raw_buffer_load_b32(sc_r, s_off[i], b0 * 4, 0);
       }
     }
 #pragma unroll
-    for (int j = 0; j < S; ++j) r.xf[j] = *gp(frag + (int64_t)min(b0 + j, nblk - 1) * 64 + lane);
+    for (int j = 0; j < S; ++j) r.xf[j] = __builtin_amdgcn_raw_buffer_load_b128(fr_r, 16u * lane, (b0 + j) * 1024, 0);
     if constexpr (QT != QBL_FMT_Q8)
-      r.X = *gp(reinterpret_cast<const f32x4*>(xsum + (int64_t)min(b0 + ((lane >> 2) & (S - 1)), nblk - 1) * 16) +
-                (lane & 3));
+      r.X = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xs_r, x_off, b0 * 64, 0));
   };
   // the loaded slab into this wave's LDS region
   auto stash = [&](const SlabRegs<QT>& r) {
@@ -493,9 +508,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemvArgs a, MfmaSplit
   finish_output(a, g, ex, b, n, s);
 }
 
-// Workgroups per 64 rows: about as many workgroups as the chip holds at once
-// (256 compute units, 4 workgroups each), each keeping at least 8 slabs.
+// Workgroups per 64 rows: none split when the rows alone give 1.5 workgroups
+// per compute unit (256 of them), else about as many workgroups as the chip
+// holds at once (4 per compute unit), each keeping at least 8 slabs.
 int split_ks(int64_t row_groups, int nblk, int slab) {
+  if (row_groups >= 384) return 1;
   const int64_t want = 1024 / row_groups;
   const int64_t most = std::max<int64_t>(1, (nblk + slab - 1) / slab / 8);
   return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, 16}));
