@@ -220,6 +220,44 @@ __device__ __forceinline__ float csr_row_dot(const uint32_t* col, const uint16_t
   return p;
 }
 
+// csr_row_dot for R rows at once, U loads per row and lane per round: the
+// rounds' loads of all R rows go out together.  Each lane still visits its
+// entries of a row in the same order (e0 + lane, e0 + lane + 64, ...), so every
+// p[r] has the bits csr_row_dot gives; entries past a row's end are not loaded
+// and add 0 * x(0).
+template <int R, int U, class XAt>
+__device__ __forceinline__ void csr_rows_dot(const uint32_t* const (&col)[R], const uint16_t* const (&val)[R],
+                                             const uint32_t (&e0)[R], const uint32_t (&e1)[R], int lane, XAt xat,
+                                             float (&p)[R]) {
+  uint32_t len = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    p[r] = 0.0f;
+    len = max(len, e1[r] - e0[r]);
+  }
+  for (uint32_t off = 0; off < len; off += 64 * U) {
+    uint32_t c[R][U], v[R][U];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t e = e0[r] + off + 64 * u + lane;
+        const bool ok = e < e1[r];
+        c[r][u] = ok ? *gp(col[r] + e) : 0u;
+        v[r][u] = ok ? (uint32_t)*gp(val[r] + e) : 0u;
+      }
+    float xv[R][U];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) xv[r][u] = xat(c[r][u]);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) p[r] = fmaf(h2f(v[r][u]), xv[r][u], p[r]);
+  }
+}
+
 // A value handed from one workgroup to others in the same launch: one 64-bit
 // word, the launch's (or phase's) tag in the high half and the float in the low
 // half, read with device-coherent relaxed loads until the tag matches (bounded).

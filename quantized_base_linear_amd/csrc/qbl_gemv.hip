@@ -17,6 +17,7 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "qbl_device.h"
@@ -408,14 +409,62 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   __shared__ float ssred[W];
   __shared__ float tl[kB1MaxT];
   __shared__ float outl[kB1MaxSlots];
-  __shared__ float spl[kMaxAdapters][kB1MaxSlots];  // sparse deltas' S x per adapter and slot
 
   const GemvArgs& a = f.g;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = a.k, CT = K / WPC;
   const int64_t row_bytes = F::row_bytes(K);
   const bool shrinker = (int)blockIdx.x < f.shrink_wgs;
-  const int wg = (int)blockIdx.x - f.shrink_wgs;
+  const int wg = (int)blockIdx.x - f.shrink_wgs - f.sparse_wgs;
+
+  // ---- sparse workgroups [shrink_wgs, shrink_wgs + sparse_wgs): a wave per
+  // (segment, sparse adapter, row) item, its lanes strided over the row's
+  // entries, gathering the unscaled input s = v0 + v1 + v2 (the RMS factor is
+  // applied by the row's GEMV workgroup); one wave reduction per item, stored
+  // as a tagged word like the shrink values.  They precede every GEMV
+  // workgroup in dispatch order and never wait.
+  if (!shrinker && wg < 0) {
+    constexpr int kSpR = 2;  // items (rows) per wave at once (1, 3 and 4 measured slower)
+    const int per = (f.sp_items + f.sparse_wgs - 1) / f.sparse_wgs;
+    const int i0 = ((int)blockIdx.x - f.shrink_wgs) * per, i1 = min(f.sp_items, i0 + per);
+    for (int g0 = i0 + kSpR * wave; g0 < i1; g0 += kSpR * W) {
+      const uint32_t* col[kSpR];
+      const uint16_t* val[kSpR];
+      uint32_t e0[kSpR], e1[kSpR];
+#pragma unroll
+      for (int r = 0; r < kSpR; ++r) {
+        const int item = g0 + r;
+        int sg = 0, ad = 0;
+        for (int q = 0; q < a.nseg; ++q)
+          for (int i = 0; i < a.seg[q].lora.n_ad; ++i)
+            if (f.sp_base[q][i] >= 0 && item >= f.sp_base[q][i] && item < f.sp_base[q][i] + a.seg[q].n) sg = q, ad = i;
+        const LoraSeg& L = a.seg[sg].lora;
+        col[r] = L.ci[ad];
+        val[r] = L.sv[ad];
+        e0[r] = e1[r] = 0;
+        if (item < i1) {
+          const int row = item - f.sp_base[sg][ad];
+          e0[r] = L.rp[ad][row];
+          e1[r] = L.rp[ad][row + 1];
+        }
+      }
+      float p[kSpR];
+      csr_rows_dot<kSpR, 4>(col, val, e0, e1, lane, [&](uint32_t c) {
+        float xv = *gp(f.v[0] + c);
+        if (f.nv > 1) xv += *gp(f.v[1] + c);
+        if (f.nv > 2) xv += *gp(f.v[2] + c);
+        return xv;
+      }, p);
+#pragma unroll
+      for (int r = 0; r < kSpR; ++r) {
+        const float w = wave_sum(p[r]);
+        if (lane == 0 && g0 + r < i1)
+          __hip_atomic_store(f.sp + g0 + r, ((uint64_t)f.tag << 32) | __float_as_uint(w), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  }
 
   // this lane's chunks
   int cidx[CPW];
@@ -617,27 +666,16 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   }
   for (int j = tid + kTW * NT; j < f.rows_total; j += NT) tl[j] = tagged_get(tcopy + j, f.tag, f.spin_limit);
 
-  // ---- sparse deltas: a wave per output row, its lanes strided over the row's
-  // entries, gathering the unscaled input s = v0 + v1 + v2 (the RMS factor is
-  // applied with the rest below); one wave reduction per row and adapter
-  if (f.has_sparse) {
-    for (int s = wave; s < nslots; s += W) {
-      const GemvSeg& g = a.seg[slot_seg(s)];
-      const int row = slot_row(s);
-      if (row >= g.n) continue;
-      for (int i = 0; i < g.lora.n_ad; ++i) {
-        if (g.lora.rank[i] != 0) continue;
-        float p = csr_row_dot(g.lora.ci[i], g.lora.sv[i], g.lora.rp[i][row], g.lora.rp[i][row + 1], lane,
-                              [&](uint32_t c) {
-                                float xv = *gp(f.v[0] + c);
-                                if (f.nv > 1) xv += *gp(f.v[1] + c);
-                                if (f.nv > 2) xv += *gp(f.v[2] + c);
-                                return xv;
-                              });
-        p = wave_sum(p);
-        if (lane == 0) spl[i][s] = p;
-      }
-    }
+  // the first sparse value of each row, requested before the barrier so that
+  // its round trip overlaps the wait there
+  uint64_t spw = 0;
+  int sp_first = -1;
+  if (f.sp_items > 0 && tid < nslots) {
+    const int sg = slot_seg(tid), row = slot_row(tid);
+    for (int i = 0; i < a.seg[sg].lora.n_ad && sp_first < 0; ++i)
+      if (f.sp_base[sg][i] >= 0) sp_first = i;
+    if (sp_first >= 0 && row < a.seg[sg].n)
+      spw = __hip_atomic_load(f.sp + f.sp_base[sg][sp_first] + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (tid < nslots) {
@@ -651,7 +689,13 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
     for (int i = 0; i < g.lora.n_ad; ++i) {
       const int rk = g.lora.rank[i];
       if (rk == 0) {
-        v = fmaf(g.lora.scale[i], cscale * spl[i][s], v);
+        float p = 0.0f;
+        if (row < g.n) {
+          const uint64_t* w = f.sp + f.sp_base[slot_seg(s)][i] + row;
+          p = i == sp_first && (uint32_t)(spw >> 32) == f.tag ? __uint_as_float((uint32_t)spw)
+                                                             : tagged_get(w, f.tag, f.spin_limit);
+        }
+        v = fmaf(g.lora.scale[i], cscale * p, v);
         continue;
       }
       const float* ti = tl + g.lora.toff[i];
@@ -719,10 +763,25 @@ hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
   using S = B1Shape<QT, CPW>;
   GemvArgs& a = f.g;
   f.shrink_wgs = (f.rows_total + S::kRS - 1) / S::kRS;
+  const int resident = b1_resident_per_cu<QT, W, CPW, G>() * device_cus();
+  // sparse workgroups: their share of the round is twice their share of the
+  // launch's bytes (a gathering workgroup moves about half the bytes per unit
+  // time of a streaming one; measured on the 10 %-dense 7B block), at least one,
+  // at most one per W items
+  f.sparse_wgs = 0;
+  if (f.sp_items > 0) {
+    double dense = 0.0;
+    for (int i = 0; i < a.nseg; ++i)
+      dense += (double)a.seg[i].n * (double)(Fmt<QT>::row_bytes(a.k) + (QT == QBL_FMT_Q8 ? a.k / 16 : QT == QBL_FMT_Q4 ? a.k / 8 : a.k / 16));
+    const double share = std::min(0.9, 2.0 * (double)f.sp_bytes / ((double)f.sp_bytes + dense));
+    int sw = (int)(share * (double)(resident - f.shrink_wgs) + 0.5);
+    sw = std::min(std::max(sw, 1), (f.sp_items + W - 1) / W);
+    f.sparse_wgs = sw;
+  }
   if (f.rows_per_wg <= 0) {
-    // one round: as many GEMV workgroups as the chip holds next to the shrink ones
+    // one round: as many GEMV workgroups as the chip holds next to the shrink and sparse ones
     const int units = f.sum ? a.seg[0].n : [&] { int u = 0; for (int i = 0; i < a.nseg; ++i) u += a.seg[i].n; return u; }();
-    const int slots = b1_resident_per_cu<QT, W, CPW, G>() * device_cus() - f.shrink_wgs;
+    const int slots = resident - f.shrink_wgs - f.sparse_wgs;
     const int rmax = kB1MaxSlots / (f.sum ? a.nseg : 1);
     int r = slots > 0 ? (units + slots - 1) / slots : rmax;
     f.rows_per_wg = r < 1 ? 1 : (r > rmax ? rmax : r);
@@ -736,7 +795,7 @@ hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
       wg += (a.seg[i].n + f.rows_per_wg - 1) / f.rows_per_wg;
     }
   }
-  a.grid = f.shrink_wgs + wg;
+  a.grid = f.shrink_wgs + f.sparse_wgs + wg;
   QBL_LAUNCH((gemv_b1_kernel<QT, W, CPW, G>), dim3(a.grid), dim3(W * 64), 0, lc, f);
   return hipGetLastError();
 }
@@ -885,6 +944,13 @@ hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc) {
   if (a.batch != 1 || !fused_supported(a.qtype, a.k) || f.rows_total > kB1MaxT) return hipErrorInvalidValue;
   for (int i = 0; i < a.nseg; ++i)
     if (f.sum && a.seg[i].n != a.seg[0].n) return hipErrorInvalidValue;
+  // sparse items: every (segment, sparse adapter) has its n rows at sp_base, all below sp_items
+  for (int i = 0; i < a.nseg; ++i)
+    for (int j = 0; j < a.seg[i].lora.n_ad; ++j) {
+      const bool sparse = a.seg[i].lora.rank[j] == 0;
+      const int b = f.sp_base[i][j];
+      if (sparse != (b >= 0) || (sparse && (b + a.seg[i].n > f.sp_items || !f.sp))) return hipErrorInvalidValue;
+    }
   f.rows_per_wg = 0;  // chosen by the launcher from the kernel's occupancy
   switch (a.qtype) {
     case QBL_FMT_Q8: return launch_b1_q<QBL_FMT_Q8>(f, lc);

@@ -106,6 +106,11 @@ struct FusedArgs {
   int rows_total;      // A rows = shrink results
   int has_sparse;      // 1: some segment has a sparse delta
   int shrink_wgs;      // set by the launcher
+  int sparse_wgs;      // set by the launcher (0 when sp_items == 0)
+  int sp_items;        // sparse (segment, adapter, row) items: S x values handed to the GEMV workgroups
+  int64_t sp_bytes;    // CSR bytes of the launch (for the launcher's split of the round)
+  int sp_base[kMaxSegs][kMaxAdapters];  // first item of (segment, adapter), -1 unless the adapter is sparse
+  uint64_t* sp;        // sp_items tagged words (launch number << 32 | float bits)
   int spin_limit;      // bound on the sleeps of one wait for a shrink result
   uint32_t tag;        // this launch's number, never 0
   uint64_t* t;         // kTCopies copies of the rows_total shrink results, (tag << 32) | float bits

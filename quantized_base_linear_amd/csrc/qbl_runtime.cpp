@@ -133,6 +133,7 @@ struct LoraRef {
   const uint32_t* rp;
   const uint32_t* ci;
   const uint16_t* sv;
+  int64_t nnz;
 };
 
 // One attached list.  Immutable once published; freed when no composition or
@@ -828,7 +829,7 @@ extern "C" qbl_status qbl_comp_attach(qbl_comp* comp, const qbl_adapter* const* 
       L->scales.push_back(scales[i]);
       eff_digests.push_back(list[i]->impl->digest);
       for (const AdEntry& e : list[i]->impl->ent) {
-        L->plan[(size_t)e.linear].push_back(LoraRef{e.A, e.B, e.rank, scales[i], e.rp, e.ci, e.sv});
+        L->plan[(size_t)e.linear].push_back(LoraRef{e.A, e.B, e.rank, scales[i], e.rp, e.ci, e.sv, e.nnz});
         L->total_rank[(size_t)e.linear] += e.rank;
       }
     }
@@ -1042,10 +1043,11 @@ qbl_status block_shape(const qbl_base* b, int blk, Block* out) {
 // Layout of the block/decode workspace (floats, 256-byte aligned pieces).
 struct BlockWs {
   float *xin, *t, *q, *k, *v, *a, *g, *u, *dd;
+  uint64_t* sp;
   int64_t bytes;
 };
 
-BlockWs block_ws(void* ws, int64_t d, int64_t h, int64_t tmax) {
+BlockWs block_ws(void* ws, int64_t d, int64_t h, int64_t tmax, int64_t spmax) {
   BlockWs w{};
   int64_t off = 0;
   auto take = [&](int64_t floats) {
@@ -1056,6 +1058,7 @@ BlockWs block_ws(void* ws, int64_t d, int64_t h, int64_t tmax) {
   const int64_t m = std::max(d, h);
   w.xin = take(m);
   w.t = take(std::max<int64_t>(2 * qbl::kTCopies * qbl::t_copy_stride(tmax), tmax));  // tagged 8-byte words
+  w.sp = reinterpret_cast<uint64_t*>(take(2 * spmax));  // tagged 8-byte words
   w.q = take(d);
   w.k = take(d);
   w.v = take(d);
@@ -1065,6 +1068,28 @@ BlockWs block_ws(void* ws, int64_t d, int64_t h, int64_t tmax) {
   w.dd = take(d);
   w.bytes = off;
   return w;
+}
+
+// Sparse (linear, adapter, row) items of a launch group: the rows of every
+// sparse delta on its linears.
+int64_t group_sp_items(const qbl_base* base, const ListImpl* L, const int* lin, int nlin) {
+  int64_t n = 0;
+  for (int i = 0; i < nlin; ++i)
+    for (const LoraRef& r : L->plan[(size_t)lin[i]])
+      if (r.rank == 0) n += base->lin[(size_t)lin[i]].n;
+  return n;
+}
+
+// Max sparse items over the four launch groups of every block in range.
+int64_t blocks_spmax(const qbl_base* base, const ListImpl* L, int first_block, int n_blocks) {
+  int64_t m = 0;
+  for (int b = first_block; b < first_block + n_blocks; ++b) {
+    const int f = 7 * b;
+    const int g0[3] = {f, f + 1, f + 2}, g1[1] = {f + 3}, g2[2] = {f + 4, f + 5}, g3[1] = {f + 6};
+    m = std::max({m, group_sp_items(base, L, g0, 3), group_sp_items(base, L, g1, 1),
+                  group_sp_items(base, L, g2, 2), group_sp_items(base, L, g3, 1)});
+  }
+  return m;
 }
 
 int group_rank(const ListImpl* L, const int* lin, int nlin) {
@@ -1105,7 +1130,7 @@ uint32_t next_tag() {
 
 qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, float* const* outs,
                      int nlin, const float* const* vin, int nv, int rms, int batch, int64_t v_stride,
-                     float* xin_buf, float* t_buf, hipStream_t st, bool sum_ok = false,
+                     float* xin_buf, float* t_buf, uint64_t* sp_buf, hipStream_t st, bool sum_ok = false,
                      bool* summed = nullptr, void* stage = nullptr) {
   if (summed) *summed = false;
   const int64_t K = base->lin[(size_t)lin[0]].k;
@@ -1171,6 +1196,21 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     for (int i = 0; i < n_ent; ++i) f.ent[i] = ent[i];
     f.rows_total = T;
     f.has_sparse = has_sparse;
+    // sparse items: the rows of each (linear, sparse adapter), in segment and list order
+    for (int i = 0; i < f.g.nseg; ++i) {
+      int j = 0;
+      for (const LoraRef& r : L->plan[(size_t)lin[i]]) {
+        f.sp_base[i][j] = -1;
+        if (r.rank == 0) {
+          f.sp_base[i][j] = f.sp_items;
+          f.sp_items += f.g.seg[i].n;
+          f.sp_bytes += r.nnz * 6 + ((int64_t)f.g.seg[i].n + 1) * 4;
+        }
+        ++j;
+      }
+    }
+    if (f.sp_items > 0 && !sp_buf) return fail(QBL_E_ARG, "the workspace has no room for the sparse values");
+    f.sp = sp_buf;
     f.spin_limit = kSpinLimit;
     f.tag = next_tag();
     f.t = reinterpret_cast<uint64_t*>(t_buf);
@@ -1259,27 +1299,27 @@ qbl_status run_block(const qbl_base* base, const ListImpl* L, const Block& B, co
     const int lin[3] = {f, f + 1, f + 2};
     float* outs[3] = {w.q, w.k, w.v};
     const float* v[1] = {in};
-    if (qbl_status s = run_group(base, L, lin, outs, 3, v, 1, rms_in, 1, B.d, w.xin, w.t, st, true, &summed))
+    if (qbl_status s = run_group(base, L, lin, outs, 3, v, 1, rms_in, 1, B.d, w.xin, w.t, w.sp, st, true, &summed))
       return s;
   }
   {
     const int lin[1] = {f + 3};
     float* outs[1] = {w.a};
     const float* v[3] = {w.q, w.k, w.v};
-    if (qbl_status s = run_group(base, L, lin, outs, 1, v, summed ? 1 : 3, 1, 1, B.d, w.xin, w.t, st)) return s;
+    if (qbl_status s = run_group(base, L, lin, outs, 1, v, summed ? 1 : 3, 1, 1, B.d, w.xin, w.t, w.sp, st)) return s;
   }
   {
     const int lin[2] = {f + 4, f + 5};
     float* outs[2] = {w.g, w.u};
     const float* v[1] = {w.a};
-    if (qbl_status s = run_group(base, L, lin, outs, 2, v, 1, 1, 1, B.d, w.xin, w.t, st, true, &summed))
+    if (qbl_status s = run_group(base, L, lin, outs, 2, v, 1, 1, 1, B.d, w.xin, w.t, w.sp, st, true, &summed))
       return s;
   }
   {
     const int lin[1] = {f + 6};
     float* outs[1] = {w.dd};
     const float* v[2] = {w.g, w.u};
-    if (qbl_status s = run_group(base, L, lin, outs, 1, v, summed ? 1 : 2, 1, 1, B.h, w.xin, w.t, st)) return s;
+    if (qbl_status s = run_group(base, L, lin, outs, 1, v, summed ? 1 : 2, 1, 1, B.h, w.xin, w.t, w.sp, st)) return s;
   }
   return QBL_OK;
 }
@@ -1303,8 +1343,9 @@ int64_t linear_t_bytes(int64_t batch, int64_t T) {
   if (T == 0) return 0;
   return align_up(batch == 1 ? qbl::kTCopies * qbl::t_copy_stride(T) * 8 : batch * T * 4);
 }
-int64_t linear_ws_bytes(int64_t batch, int64_t T, int64_t n, int64_t k) {
-  return linear_t_bytes(batch, T) + (batch > 1 ? align_up(qbl::mfma_stage_bytes(n, (int)k, (int)T)) : 0);
+int64_t linear_ws_bytes(int64_t batch, int64_t T, int64_t n, int64_t k, int64_t sp_items) {
+  return linear_t_bytes(batch, T) +
+         (batch > 1 ? align_up(qbl::mfma_stage_bytes(n, (int)k, (int)T)) : align_up(sp_items * 8));
 }
 
 }  // namespace
@@ -1318,7 +1359,8 @@ extern "C" qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int3
     if (op == 0) {
       if (index < 0 || index >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", index);
       if (m < 1 || m > QBL_MAX_BATCH) return fail(QBL_E_LIMIT, "batch %d outside 1..%d", m, QBL_MAX_BATCH);
-      *bytes_out = linear_ws_bytes(m, L->total_rank[(size_t)index], b->lin[(size_t)index].n, b->lin[(size_t)index].k);
+      *bytes_out = linear_ws_bytes(m, L->total_rank[(size_t)index], b->lin[(size_t)index].n, b->lin[(size_t)index].k,
+                                   group_sp_items(b, L.get(), &index, 1));
       return QBL_OK;
     }
     if (op == 1) {
@@ -1337,7 +1379,7 @@ extern "C" qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int3
         d = std::max(d, B.d);
         h = std::max(h, B.h);
       }
-      *bytes_out = block_ws(nullptr, d, h, blocks_tmax(L.get(), 0, nb)).bytes;
+      *bytes_out = block_ws(nullptr, d, h, blocks_tmax(L.get(), 0, nb), blocks_spmax(b, L.get(), 0, nb)).bytes;
       return QBL_OK;
     }
     return fail(QBL_E_ARG, "unknown op %d", op);
@@ -1358,14 +1400,18 @@ extern "C" qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x,
     auto L = std::atomic_load(&comp->list);
     const int T = L->total_rank[(size_t)linear];
     const DevLinear& D = b->lin[(size_t)linear];
-    if (qbl_status s = check_ws(ws, ws_bytes, linear_ws_bytes(batch, T, D.n, D.k))) return s;
+    const int64_t sp_items = group_sp_items(b, L.get(), &linear, 1);
+    if (qbl_status s = check_ws(ws, ws_bytes, linear_ws_bytes(batch, T, D.n, D.k, sp_items))) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int lin[1] = {linear};
     float* outs[1] = {y};
     const float* v[1] = {x};
     const ListUse use{L.get(), st, !L->plan[(size_t)linear].empty()};
     void* stage = batch > 1 ? static_cast<char*>(ws) + linear_t_bytes(batch, T) : nullptr;
-    return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), st, false,
+    uint64_t* sp = batch == 1 && sp_items > 0
+                       ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + linear_t_bytes(batch, T))
+                       : nullptr;
+    return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), sp, st, false,
                      nullptr, stage);
   })
 }
@@ -1468,9 +1514,9 @@ extern "C" qbl_status qbl_block(qbl_comp* comp, int32_t block, const float* x, f
     if (qbl_status s = check_device(b)) return s;
     std::lock_guard<std::mutex> g(comp->mu);
     auto L = std::atomic_load(&comp->list);
-    const BlockWs need = block_ws(nullptr, B.d, B.h, blocks_tmax(L.get(), block, 1));
+    const BlockWs need = block_ws(nullptr, B.d, B.h, blocks_tmax(L.get(), block, 1), blocks_spmax(b, L.get(), block, 1));
     if (qbl_status s = check_ws(ws, ws_bytes, need.bytes)) return s;
-    const BlockWs w = block_ws(ws, B.d, B.h, blocks_tmax(L.get(), block, 1));
+    const BlockWs w = block_ws(ws, B.d, B.h, blocks_tmax(L.get(), block, 1), blocks_spmax(b, L.get(), block, 1));
     hipStream_t st = static_cast<hipStream_t>(stream);
     const ListUse use{L.get(), st, true};
     if (qbl_status s = run_block(b, L.get(), B, x, 0, w, st)) return s;
@@ -1499,8 +1545,9 @@ extern "C" qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_
     std::lock_guard<std::mutex> g(comp->mu);
     auto L = std::atomic_load(&comp->list);  // one list for the whole call
     const int tmax = blocks_tmax(L.get(), first_block, n_blocks);
-    if (qbl_status s = check_ws(ws, ws_bytes, block_ws(nullptr, d, h, tmax).bytes)) return s;
-    const BlockWs w = block_ws(ws, d, h, tmax);
+    const int64_t spmax = blocks_spmax(b, L.get(), first_block, n_blocks);
+    if (qbl_status s = check_ws(ws, ws_bytes, block_ws(nullptr, d, h, tmax, spmax).bytes)) return s;
+    const BlockWs w = block_ws(ws, d, h, tmax, spmax);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const ListUse use{L.get(), st, true};
     for (int t = 0; t < n_tokens; ++t) {
