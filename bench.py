@@ -424,15 +424,17 @@ def bench_dar(torch, q, workloads, args):
 def bench_q4(torch, q, wl, args, label):
     out = {}
     log(f"[{label}] building 70B MLP linears ({label}, r32)")
-    base, ads, comp, _ = build_copies(q, wl, 1, [0])
+    copies = 2  # 2 x 455 MB rotated: well past the 256 MB Infinity Cache
+    base, ads, comp, _ = build_copies(q, wl, copies, [0])
     for batch in (1, 8):
         xs = [torch.from_numpy(wl.x(i, batch)).cuda() for i in range(3)]
         ys = [torch.empty((batch, L.n_out), dtype=torch.float32, device="cuda") for L in wl.linears]
-        wss = [q.workspace(comp, q.OP_LINEAR, i, batch) for i in range(3)]
+        wss = [q.workspace(comp, q.OP_LINEAR, c * 3 + i, batch) for c in range(copies) for i in range(3)]
 
-        def step(_):
+        def step(s):
+            c = s % copies
             for i in range(3):
-                q.qbl_linear(comp, i, xs[i], ys[i], batch, wss[i])
+                q.qbl_linear(comp, c * 3 + i, xs[i], ys[i], batch, wss[c * 3 + i])
 
         ms = time_loop(torch, step, max(5, args.steps // 2), 2)
         byts = sum(wl.base_bytes(i) + wl.lora_bytes(i) + 4 * batch * (L.n_out + L.k_in)
@@ -447,7 +449,7 @@ def bench_q4(torch, q, wl, args, label):
 
 def bench_prefill(torch, q, workloads, args):
     wl = workloads.prefill()
-    copies = 4
+    copies = 10  # 10 x 62 MB base + factors rotated: past the 256 MB Infinity Cache
     log(f"[prefill] building {copies} copies of the 14336x4096 q8_0 layer (r64)")
     base, ads, comp, _ = build_copies(q, wl, copies, [0])
     x = torch.from_numpy(wl.x_prefill_f32()).to(torch.bfloat16).view(torch.int16).cuda()
@@ -476,6 +478,9 @@ def bench_prefill(torch, q, workloads, args):
             "tokens_per_s": round(wl.m_tokens / (ms * 1e-3), 1)}
 
 
+EXTRAS = ("stack", "q4_mlp", "q4k_mlp", "sparse_block", "dar", "prefill")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -485,6 +490,8 @@ def main():
     ap.add_argument("--stack-tokens", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extras", action="store_true", help="skip the stack / q4 / prefill lines")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma-separated extra lines to run (default: all of " + ",".join(EXTRAS) + ")")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of this many MiB (a known-size kernel "
                          "for scaling hardware byte counters)")
@@ -519,13 +526,20 @@ def main():
                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
         "roofline": roof,
     }
-    if not args.no_extras:
-        result["stack"] = bench_stack(torch, q, workloads, args)
-        result["q4_mlp"] = bench_q4(torch, q, workloads.mlp70b(), args, "q4_sm")
-        result["q4k_mlp"] = bench_q4(torch, q, workloads.mlp70b_q4k(), args, "q4_K")
-        result["sparse_block"] = bench_sparse(torch, q, workloads, args)
-        result["dar"] = bench_dar(torch, q, workloads, args)
-        result["prefill"] = bench_prefill(torch, q, workloads, args)
+    extras = [] if args.no_extras else [e for e in args.extras.split(",") if e]
+    for e in extras:
+        if e not in EXTRAS:
+            print(f"unknown extra line {e!r}; choose from {','.join(EXTRAS)}", file=sys.stderr)
+            sys.exit(2)
+    runs = {"stack": lambda: bench_stack(torch, q, workloads, args),
+            "q4_mlp": lambda: bench_q4(torch, q, workloads.mlp70b(), args, "q4_sm"),
+            "q4k_mlp": lambda: bench_q4(torch, q, workloads.mlp70b_q4k(), args, "q4_K"),
+            "sparse_block": lambda: bench_sparse(torch, q, workloads, args),
+            "dar": lambda: bench_dar(torch, q, workloads, args),
+            "prefill": lambda: bench_prefill(torch, q, workloads, args)}
+    for e in EXTRAS:
+        if e in extras:
+            result[e] = runs[e]()
     import oracle
     log("[cpu] timing the oracle")
     result["cpu_baseline"] = cpu_baseline(oracle, wl, blocks, args.cpu_seconds)
