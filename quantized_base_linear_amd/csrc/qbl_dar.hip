@@ -6,7 +6,10 @@
 // One thread per 32-weight chunk (a q8_0 or q4_sm block, a q4_K sub-block).
 // A wave covers 64 rows at one chunk (q4_K: 8 rows at the 8 chunks of one
 // super-block, whose sub-blocks are then 8 consecutive lanes), so the A values
-// of a chunk are one broadcast load for the wave instead of one per lane.  A thread
+// of its chunks are shared by the whole wave: they are staged in the wave's LDS
+// region kRB rank rows at a time, together with the kRB B values of the wave's
+// rows (loaded four lanes to a row, then read back per lane), so that one
+// memory round trip serves kRB steps of every lane's fma chain.  A thread
 // forms the merged float32 weights of its chunk with one fixed recipe
 //   w = f32(deq(W));  per adapter in list order:
 //     low-rank  w = fma(s, u, w),  u = fma chain over j of B[r][j] * A[j][k]
@@ -24,6 +27,7 @@ namespace qbl {
 namespace {
 
 constexpr int kDarThreads = 256;
+constexpr int kRB = 8;  // rank rows of A staged per round
 
 __device__ __forceinline__ uint16_t f2h_bits(float f) { return __half_as_ushort(__float2half_rn(f)); }
 __device__ __forceinline__ float h_bits2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
@@ -32,17 +36,22 @@ __device__ __forceinline__ float mn(float a, float b) { return b < a ? b : a; }
 __device__ __forceinline__ float mx(float a, float b) { return a < b ? b : a; }
 
 template <int QT>
-__global__ __launch_bounds__(kDarThreads) void dar_kernel(DarArgs a) {
+__global__ __launch_bounds__(kDarThreads, 4) void dar_kernel(DarArgs a) {
 #pragma clang fp contract(off)  // the codes depend on each rounding: only the fmas written out fuse
   constexpr int RW = QT == QBL_FMT_Q4K ? 8 : 64;  // rows per wave
   constexpr int CW = 64 / RW;                      // chunks per wave
+  __shared__ f32x4 a_st[kDarThreads / 64][kRB][CW * 8];  // per wave: kRB rank rows of A at its chunks
+  __shared__ f32x4 b_st[kDarThreads / 64][RW][kRB / 4 + 1];  // per wave: its rows' kRB B values (+ pad)
   const int cpr = a.k / 32;                        // chunks per row
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t wv = ((int64_t)blockIdx.x * kDarThreads + threadIdx.x) >> 6;
   const int64_t n_rw = (a.n + RW - 1) / RW;        // row groups
   const int rgrp = (int)(wv % n_rw), cgrp = (int)(wv / n_rw);
-  const int row = rgrp * RW + lane / CW, c = cgrp * CW + lane % CW;
-  if (row >= a.n || c >= cpr) return;              // q4_K: whole 8-lane groups leave together
+  if (cgrp * CW >= cpr) return;                    // whole waves past the end
+  // lanes on rows past n work on the last row and store nothing (q4_K: whole
+  // 8-lane groups, so the group exchanges below stay within valid data)
+  const bool valid = rgrp * RW + lane / CW < a.n;
+  const int row = min(rgrp * RW + lane / CW, a.n - 1), c = cgrp * CW + lane % CW;
   const int64_t t = (int64_t)row * cpr + c;        // the chunk's index in canonical order
   const int k0 = 32 * c;
 
@@ -93,21 +102,61 @@ __global__ __launch_bounds__(kDarThreads) void dar_kernel(DarArgs a) {
     }
     const int rk = a.rank[i];
     const float* Br = a.B[i] + (int64_t)row * rk;
-    const float* Ac = a.A[i] + k0;
+    const f32x4* Ab = reinterpret_cast<const f32x4*>(a.A[i] + 32 * cgrp * CW);  // the wave's first column
     float u[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) u[j] = 0.0f;
-    for (int r = 0; r < rk; ++r) {
-      const float b = Br[r];
-      const float* Ar = Ac + (int64_t)r * a.k;
+    for (int r0 = 0; r0 < rk; r0 += kRB) {
+      const int nr = min(kRB, rk - r0);
+      // rank rows r0 .. r0 + nr of A at the wave's CW chunks (CW * 8 float4 each)
 #pragma unroll
-      for (int j = 0; j < 32; j += 4) {
-        const float4 a4 = gload4(Ar + j);
-        u[j] = fmaf(b, a4.x, u[j]);
-        u[j + 1] = fmaf(b, a4.y, u[j + 1]);
-        u[j + 2] = fmaf(b, a4.z, u[j + 2]);
-        u[j + 3] = fmaf(b, a4.w, u[j + 3]);
+      for (int q0 = 0; q0 < kRB * CW * 8; q0 += 64) {
+        const int q = q0 + lane, rr = q / (CW * 8), f = q % (CW * 8);
+        if (rr < nr) a_st[wave][rr][f] = *gp(Ab + (int64_t)(r0 + rr) * (a.k / 4) + f);
       }
+      // the wave's RW rows x nr B values: 4 lanes per row with 16-byte loads when
+      // the rows allow it (each lane then reads its row back), else per lane
+      float b[kRB];
+      const bool coalesced = rk % 4 == 0;
+      if (coalesced) {
+#pragma unroll
+        for (int q0 = 0; q0 < RW * kRB / 4; q0 += 64) {
+          const int q = q0 + lane, ro = q / (kRB / 4), part = q % (kRB / 4);
+          const int grow = min(rgrp * RW + ro, a.n - 1);
+          if (q < RW * kRB / 4 && 4 * part < nr)
+            b_st[wave][ro][part] = *gp(reinterpret_cast<const f32x4*>(a.B[i] + (int64_t)grow * rk + r0) + part);
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < kRB; ++rr) b[rr] = rr < nr ? *gp(Br + r0 + rr) : 0.0f;
+      }
+      // a wave's LDS writes and reads run in issue order; this keeps the
+      // compiler from moving the reads above the writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (coalesced) {
+#pragma unroll
+        for (int p4 = 0; p4 < kRB / 4; ++p4) {
+          const f32x4 v = b_st[wave][lane / CW][p4];
+          b[4 * p4] = v.x, b[4 * p4 + 1] = v.y, b[4 * p4 + 2] = v.z, b[4 * p4 + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < kRB; ++rr) {
+        if (rr >= nr) break;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f32x4 a4 = a_st[wave][rr][(lane % CW) * 8 + j];
+          u[4 * j] = fmaf(b[rr], a4.x, u[4 * j]);
+          u[4 * j + 1] = fmaf(b[rr], a4.y, u[4 * j + 1]);
+          u[4 * j + 2] = fmaf(b[rr], a4.z, u[4 * j + 2]);
+          u[4 * j + 3] = fmaf(b[rr], a4.w, u[4 * j + 3]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 #pragma unroll
     for (int j = 0; j < 32; ++j) w[j] = fmaf(s, u[j], w[j]);
@@ -121,6 +170,7 @@ __global__ __launch_bounds__(kDarThreads) void dar_kernel(DarArgs a) {
     const uint16_t dh = f2h_bits(__fdiv_rn(amax, 127.0f));
     const float d = h_bits2f(dh);
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out + t * 34);
+    if (!valid) return;
     out[0] = dh;
 #pragma unroll
     for (int j = 0; j < 32; j += 2) {
@@ -145,6 +195,7 @@ __global__ __launch_bounds__(kDarThreads) void dar_kernel(DarArgs a) {
     const uint16_t dh = f2h_bits(__fdiv_rn(hi - m, 15.0f));
     const float d = h_bits2f(dh);
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out + t * 20);
+    if (!valid) return;
     out[0] = dh;
     out[1] = mh;
 #pragma unroll
@@ -192,7 +243,7 @@ __global__ __launch_bounds__(kDarThreads) void dar_kernel(DarArgs a) {
         q = fminf(15.0f, fmaxf(0.0f, q));
         nib |= (uint32_t)(int)q << (4 * h);
       }
-      nb[j / 4] = (uint16_t)nib;
+      if (valid) nb[j / 4] = (uint16_t)nib;
     }
     // the 16 six-bit codes into lane 0 of the group: code i at field bit 6i
     const uint32_t codes = (uint32_t)sc | ((uint32_t)mc << 8);
@@ -206,7 +257,7 @@ __global__ __launch_bounds__(kDarThreads) void dar_kernel(DarArgs a) {
       if (bm < 64) f_lo |= m6 << bm;
       if (bm + 6 > 64) f_hi |= bm >= 64 ? m6 << (bm - 64) : m6 >> (64 - bm);
     }
-    if (j8 == 0) {
+    if (valid && j8 == 0) {
       uint16_t* hdr = reinterpret_cast<uint16_t*>(blk);
       hdr[0] = dh;
       hdr[1] = mh;
