@@ -384,7 +384,8 @@ qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x, float* y, 
  *   W_eff = bf16( float32(deq(W)) + sum_i bf16(s_i B_i) bf16(A_i) )    (tile by tile, on chip)
  *   Y = X W_eff^T with float32 accumulation.
  * X: device bfloat16 bit patterns, m x k_in; Y: device float32 m x n_out;
- * q8_0 and q4_sm bases (QBL_E_FORMAT for q4_K); m >= 1. */
+ * q8_0, q4_sm and q4_K bases, low-rank adapters (QBL_E_FORMAT for a list with a
+ * sparse delta); m >= 1. */
 qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint16_t* x_bf16, float* y,
                           int32_t m, void* ws, int64_t ws_bytes, void* stream);
 

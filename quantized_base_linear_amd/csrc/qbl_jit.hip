@@ -20,6 +20,7 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include "qbl_device.h"
 #include "qbl_kernels.h"
 
 namespace qbl {
@@ -40,10 +41,6 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-  return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xFFFFu)));
 }
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
@@ -139,8 +136,9 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
   // quantised weights); At is loaded one step before it is staged in LDS.
   struct Ops {
     uint4 xr[4];
-    uint4 qv;  // 16 consecutive weights of this lane's row: 16 bytes (q8_0) or 8 (q4_sm)
+    uint4 qv;  // 16 consecutive weights of this lane's row: 16 bytes (q8_0) or 8 (q4_sm, q4_K)
     uint32_t scv;
+    uint4 hd;  // q4_K: the super-block header of the lane's block
   };
   Ops opa, opb;
   uint4 atr = make_uint4(0u, 0u, 0u, 0u);
@@ -181,7 +179,11 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
     } else {
       const uint2 q2 = *reinterpret_cast<const uint2*>(a.qs + (int64_t)nrow * (K / 2) + (kbase + 16 * h) / 2);
       o.qv = make_uint4(q2.x, q2.y, 0u, 0u);
-      o.scv = reinterpret_cast<const uint32_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+      if constexpr (QT == QBL_FMT_Q4K)
+        o.hd = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sc) +
+                                               ((int64_t)nrow * (K / 256) + kbase / 256) * 16);
+      else
+        o.scv = reinterpret_cast<const uint32_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
     }
   };
 
@@ -210,8 +212,16 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
     }
     // a K block past the matrix contributes zeros (d = m = 0 and no adapter term)
     const bool kin = k0 + 32 * kb < K;
-    const float d = kin ? h2f(scv) : 0.0f;
-    const float mn = QT == QBL_FMT_Q8 ? -128.0f * d : (kin ? h2f(scv >> 16) : 0.0f);
+    float d, mn;
+    if constexpr (QT == QBL_FMT_Q4K) {  // the block is sub-block (k / 32) % 8 of its super-block
+      float D, M;
+      q4k_step_offset(o.hd, (min(k0 + 32 * kb, K - 32) / 32) & 7, D, M);
+      d = kin ? D : 0.0f;
+      mn = kin ? -M : 0.0f;
+    } else {
+      d = kin ? h2f(scv) : 0.0f;
+      mn = QT == QBL_FMT_Q8 ? -128.0f * d : (kin ? h2f(scv >> 16) : 0.0f);
+    }
     // lane (col, h): weights k = 16 h + v, v = 0..15, of row col
     uint32_t packed[8];
 #pragma unroll
@@ -219,9 +229,9 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
       float wv[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        // q8_0: d (u - 128) = fma(d, u, -128 d), u the offset-binary byte; q4_sm: fma(d, q, m).
-        // Both are exact in float32 (a product of at most 19 significant bits, then
-        // one rounding for q4_sm), as in the recipe.
+        // q8_0: d (u - 128) = fma(d, u, -128 d), u the offset-binary byte; q4_sm: fma(d, q, m);
+        // q4_K: fma(D, q, -M).  Each is float32(dequant) (products of at most 21
+        // significant bits, then one rounding for the q4 formats), as in the recipe.
         const int e = v + j;
         float deq;
         if (QT == QBL_FMT_Q8)
@@ -358,7 +368,12 @@ hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return a.qtype == QBL_FMT_Q8 ? launch_q<QBL_FMT_Q8>(a, tp, lc) : launch_q<QBL_FMT_Q4>(a, tp, lc);
+  switch (a.qtype) {
+    case QBL_FMT_Q8: return launch_q<QBL_FMT_Q8>(a, tp, lc);
+    case QBL_FMT_Q4: return launch_q<QBL_FMT_Q4>(a, tp, lc);
+    case QBL_FMT_Q4K: return a.k % 256 ? hipErrorInvalidValue : launch_q<QBL_FMT_Q4K>(a, tp, lc);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace qbl

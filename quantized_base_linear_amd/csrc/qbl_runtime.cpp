@@ -1428,7 +1428,6 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
     std::lock_guard<std::mutex> g(comp->mu);
     auto L = std::atomic_load(&comp->list);
     const DevLinear& D = b->lin[(size_t)linear];
-    if (D.qtype == QBL_Q4_K) return fail(QBL_E_FORMAT, "the prefill path takes q8_0 and q4_sm bases");
     for (const LoraRef& r : L->plan[(size_t)linear])
       if (r.rank == 0) return fail(QBL_E_FORMAT, "the prefill path takes low-rank adapters only");
     const int T = L->total_rank[(size_t)linear];

@@ -37,7 +37,9 @@ def _jit(b, torch, linear, xbits):
 
 
 @pytest.mark.parametrize("shape", [(96, 608, 1184, 1, (64,)), (300, 96, 200, 1, (16, 64)),
-                                   (257, 1056, 130, 2, (32,)), (40, 640, 384, 1, (8, 8, 8))])
+                                   (257, 1056, 130, 2, (32,)), (40, 640, 384, 1, (8, 8, 8)),
+                                   (96, 512, 1184, 3, (64,)), (257, 1280, 130, 3, (16, 32)),
+                                   (33, 256, 200, 3, (8,))])
 def test_jit_parity(torch_cuda, shape):
     torch = torch_cuda
     m, k, n, qtype, ranks = shape
@@ -70,9 +72,11 @@ def test_jit_parity(torch_cuda, shape):
         b.close()
 
 
-def test_jit_one_hot_rows_give_bf16_dequant_columns(torch_cuda):
+@pytest.mark.parametrize("qtype", [1, 2, 3])
+def test_jit_one_hot_rows_give_bf16_dequant_columns(torch_cuda, qtype):
     torch = torch_cuda
-    wl = workloads.Workload("jit_onehot", [workloads.LinearSpec("jit/onehot", 160, 256)], [], m_tokens=4)
+    wl = workloads.Workload(f"jit_onehot_{qtype}", [workloads.LinearSpec(f"jit/onehot/{qtype}", 160, 256, qtype)], [],
+                            m_tokens=4)
     b = Built(wl)
     try:
         L = wl.linears[0]
