@@ -615,6 +615,14 @@ hipError_t launch_gemv_mfma(GemvArgs& a, const PrepEntry* ent, int n_ent, int T,
     if (ent[i].toff != rk || ent[i].rank <= 0) return hipErrorInvalidValue;
     rk += ent[i].rank;
   }
+  // the GEMV's buffer loads address a segment's weights and scales with 32-bit
+  // byte offsets: each must stay below 2^31 bytes
+  const int64_t rbytes = a.qtype == QBL_FMT_Q8 ? a.k : a.k / 2;
+  const int64_t sbytes = a.qtype == QBL_FMT_Q8 ? a.k / 16 : a.qtype == QBL_FMT_Q4 ? a.k / 8 : a.k / 16;
+  for (int i = 0; i < a.nseg; ++i)
+    if ((int64_t)(a.seg[i].n + 63) / 64 * 64 * rbytes >= (int64_t)1 << 31 ||
+        (int64_t)(a.seg[i].n + 63) / 64 * 64 * sbytes >= (int64_t)1 << 31)
+      return hipErrorInvalidValue;
   if (rk != T || (T > 0 && a.t_stride != T)) return hipErrorInvalidValue;
   float* t = const_cast<float*>(a.t);
   switch (a.qtype) {

@@ -141,6 +141,33 @@ def test_ragged_shapes_and_batches(torch_cuda, qtype, n, k, batch):
         b.close()
 
 
+@pytest.mark.parametrize("qtype,n,k", [(1, 300, 1056), (2, 257, 1088), (3, 130, 2304)])
+def test_batched_rows_at_extreme_scales(torch_cuda, qtype, n, k):
+    """Above batch 1 each input row is scaled by its own power of two before its
+    f16 split: rows of 1e-30 and 1e30 magnitude, an all-zero row, a row mixing
+    1e20 and 1e-20, and an ordinary row, in one batch, each within the bound of
+    the oracle; the zero row gives exact zeros."""
+    torch = torch_cuda
+    wl = workloads.Workload(f"extreme_{qtype}_{n}_{k}", [workloads.LinearSpec(f"extreme/{qtype}/{n}/{k}", n, k, qtype)],
+                            [workloads.AdapterSpec("A1", 16, 0.75), workloads.AdapterSpec("S1", 0, 1.5, 0.05)], batch=5)
+    log(f"extreme row scales: qtype={qtype} n={n} k={k}")
+    b = Built(wl)
+    try:
+        rng = np.random.default_rng(1234 + qtype)
+        g = rng.standard_normal((5, k))
+        x = np.stack([g[0] * 1e-30, g[1] * 1e30, np.zeros(k), g[3],
+                      np.where(np.arange(k) % 2 == 0, 1e20, 1e-20) * g[4]]).astype(np.float32)
+        b.attach([0, 1])
+        y = _run(b, torch, 0, x)
+        ref = oracle.linear_dual(qtype, b.or_blocks[0], n, k, x.astype(np.float64), b.oracle_ads(0, [0, 1]))
+        for r in (0, 1, 3, 4):
+            assert np.all(np.isfinite(y[r])), r
+            assert rel_l2(y[r:r + 1], ref[r:r + 1]) <= TOL, r
+        assert np.array_equal(y[2], np.zeros(n, np.float32))
+    finally:
+        b.close()
+
+
 def test_q4k_one_hot_inputs_give_dequantised_columns(torch_cuda):
     """x = e_c: every product but one is an exact zero, so each output is the
     float32 rounding of D*q - M, the dequantised weight, at batch 1 and 4."""
