@@ -133,3 +133,44 @@ def test_block_with_sparse_delta(torch_cuda, full):
         assert rel_l2(ref, ref_l) > 10 * TOL          # the sparse delta matters
     finally:
         b.close()
+
+
+def test_block_with_two_sparse_deltas_around_a_lora():
+    """Two sparse deltas and a low-rank adapter in one list (S1, A1, S2): every
+    launch group of the block hands over two sparse values per row, added at
+    their list positions; parity with the oracle, and the list order matters."""
+    import torch
+    assert torch.cuda.is_available()
+    d, h = 544, 1440
+    wl = workloads.Workload("block_two_sparse", workloads._block_linears("block_two_sparse/b0", d, h),
+                            [workloads.AdapterSpec("A1", 16, 0.5), workloads.AdapterSpec("S1", 0, 1.0, 0.1),
+                             workloads.AdapterSpec("S2", 0, -0.75, 0.3)], blocks=1, tokens=1)
+    log("small block with S1, A1, S2")
+    b = Built(wl)
+    try:
+        x = wl.x0()[0]
+        b.attach([1, 0, 2])
+        y = _block(b, torch, x)
+        ref = oracle.block(b.oracle_layers([1, 0, 2]), x.astype(np.float64))
+        assert rel_l2(y, ref) <= TOL
+        b.attach([0])
+        ref_l = oracle.block(b.oracle_layers([0]), x.astype(np.float64))
+        assert rel_l2(ref, ref_l) > 10 * TOL                    # the sparse deltas matter
+        b.attach([2, 0, 1])
+        y2 = _block(b, torch, x)
+        assert rel_l2(y2, oracle.block(b.oracle_layers([2, 0, 1]), x.astype(np.float64))) <= TOL
+        # one linear at batch 1 (the fused launch) and at batch 3 (the matrix-core path)
+        b.attach([1, 0, 2])
+        L = wl.linears[4]
+        for batch in (1, 3):
+            xs = wl.x(4, batch)
+            q = b.q
+            xd = torch.from_numpy(np.ascontiguousarray(xs, np.float32)).cuda()
+            yd = torch.empty((batch, L.n_out), dtype=torch.float32, device="cuda")
+            q.qbl_linear(b.comp, 4, xd, yd, batch, q.workspace(b.comp, q.OP_LINEAR, 4, batch))
+            torch.cuda.synchronize()
+            refl = oracle.linear_dual(L.qtype, b.or_blocks[4], L.n_out, L.k_in, xs, b.oracle_ads(4, [1, 0, 2]))
+            assert rel_l2(yd.cpu().numpy(), refl) <= TOL, batch
+    finally:
+        b.close()
+
