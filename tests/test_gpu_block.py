@@ -72,6 +72,30 @@ def test_small_block_parity_and_invariants(torch_cuda):
         b.close()
 
 
+def test_block_with_mixed_ranks(torch_cuda):
+    """The block's summed launches (q+k+v, gate+up) with adapters of rank 16,
+    64, 6 and 36, side by side across the segments of one launch, in two list
+    orders, against the oracle."""
+    torch = torch_cuda
+    wl = workloads.Workload("mixed_block", workloads.small_block().linears,
+                            [workloads.AdapterSpec("A1", 16, 1.0), workloads.AdapterSpec("A2", 64, 0.5),
+                             workloads.AdapterSpec("A3", 6, -0.75), workloads.AdapterSpec("A4", 36, 0.25)],
+                            blocks=1, tokens=1)
+    log("small block d=544 h=1440, ranks 16, 64, 6, 36")
+    b = Built(wl)
+    try:
+        x = wl.x0()[0]
+        y0 = _block(b, torch, 0, x)
+        for idx in ([0, 1, 2, 3], [2, 3, 0, 1]):
+            b.attach(idx)
+            y = _block(b, torch, 0, x)
+            ref = oracle.block(b.oracle_layers(idx), x.astype(np.float64))
+            assert rel_l2(y, ref) <= TOL, idx
+            assert rel_l2(y, y0) > 1e-3
+    finally:
+        b.close()
+
+
 def test_small_stack_free_running_chain(torch_cuda):
     torch = torch_cuda
     wl = workloads.small_stack()

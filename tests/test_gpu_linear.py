@@ -141,6 +141,33 @@ def test_ragged_shapes_and_batches(torch_cuda, qtype, n, k, batch):
         b.close()
 
 
+def test_batch1_mixed_ranks_tall_linear(torch_cuda):
+    """Batch 1 with four adapters of ranks 16, 64, 6 and 36 on a tall linear
+    (16384 rows: 13 or more rows per workgroup): ranks that are and are not
+    multiples of 4 (16-byte and 4-byte B loads), small and large, in both list
+    orders and alone, against the oracle."""
+    torch = torch_cuda
+    n, k = 16384, 1024
+    wl = workloads.Workload("mixed_ranks", [workloads.LinearSpec("mixed_ranks/q8", n, k, 1)],
+                            [workloads.AdapterSpec("A1", 16, 0.5), workloads.AdapterSpec("A2", 64, 1.0),
+                             workloads.AdapterSpec("A3", 6, -0.75), workloads.AdapterSpec("A4", 36, 0.25)])
+    log(f"mixed ranks: q8_0 {n}x{k}, ranks 16, 64, 6, 36 at batch 1")
+    b = Built(wl)
+    try:
+        x = wl.x(0)
+        y0 = _run(b, torch, 0, x)
+        ref0 = oracle.linear_dual(1, b.or_blocks[0], n, k, x)
+        assert rel_l2(y0, ref0) <= TOL
+        for idx in ([0, 1, 2, 3], [3, 2, 1, 0], [1], [3]):
+            b.attach(idx)
+            y = _run(b, torch, 0, x)
+            ref = oracle.linear_dual(1, b.or_blocks[0], n, k, x, b.oracle_ads(0, idx))
+            assert rel_l2(y, ref) <= TOL, idx
+            assert rel_l2(y - y0, ref - ref0) <= TOL, idx
+    finally:
+        b.close()
+
+
 @pytest.mark.parametrize("qtype,n,k", [(1, 300, 1056), (2, 257, 1088), (3, 130, 2304)])
 def test_batched_rows_at_extreme_scales(torch_cuda, qtype, n, k):
     """Above batch 1 each input row is scaled by its own power of two before its
