@@ -494,8 +494,8 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   auto slot_seg = [&](int s) { return f.sum ? s / R : sg0; };
   auto slot_row = [&](int s) { return row0 + (f.sum ? s % R : s); };
 
-  // ---- loads, in the order they are needed: the input (L2-resident), the B
-  // values of the expand, then the weight stream (or the A rows when shrinking)
+  // ---- loads: the input (L2-resident), then the weight stream (or the A rows
+  // when shrinking); the expand's B values are read after the row loop
   float4 xr[CPW][NS];
 #pragma unroll
   for (int u = 0; u < CPW; ++u)
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
     if (ngroups > 1) load_group(qb, sb, 1);
   }
 
-  // ---- chunk sums and sum of squares of the input; B values into LDS
+  // ---- chunk sums and sum of squares of the input
   float xsm[CPW];
   float ss = 0.0f;
 #pragma unroll
