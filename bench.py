@@ -447,6 +447,32 @@ def bench_q4(torch, q, wl, args, label):
     return out
 
 
+def bench_probe(torch, q, nbytes=4 << 30, reps=20):
+    """Achievable HBM read bandwidth: qbl_hbm_probe streaming a 4 GiB buffer
+    (16x the 256 MB Infinity Cache) with the batch-1 kernels' 16-byte
+    non-temporal loads; median of `reps` timed passes on the current stream."""
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        wg = q.qbl_hbm_probe(buf, sink)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        q.qbl_hbm_probe(buf, sink)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[reps // 2]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[probe] read {nbytes >> 20} MiB in {ms * 1e3:.1f} us: {gbs:.0f} GB/s ({wg} workgroups)")
+    del buf, sink
+    return {"read_GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes,
+            "workgroups": wg, "us_median": round(ms * 1e3, 1), "passes": reps,
+            "access": "read-only, 16-byte non-temporal loads from every lane, grid-stride"}
+
+
 def bench_prefill(torch, q, workloads, args):
     wl = workloads.prefill()
     copies = 10  # 10 x 62 MB base + factors rotated: past the 256 MB Infinity Cache
@@ -526,6 +552,10 @@ def main():
                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
         "roofline": roof,
     }
+    probe = bench_probe(torch, q)
+    roof["achievable_read_GB_per_s"] = probe["read_GB_per_s"]
+    roof["frac_of_achievable"] = round(roof["achieved"] / probe["read_GB_per_s"], 4)
+    result["hbm_probe"] = probe
     extras = [] if args.no_extras else [e for e in args.extras.split(",") if e]
     for e in extras:
         if e not in EXTRAS:

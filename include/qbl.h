@@ -424,6 +424,19 @@ qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_blocks, con
 qbl_status qbl_requantize(qbl_comp* comp, int32_t linear, void* blocks_out, int64_t out_bytes,
                           void* stream);
 
+/* Read-only HBM streaming probe, the achievable read bandwidth as context for
+ * the fraction of the nameplate peak: reads the `bytes` bytes at buf (device,
+ * 16-byte aligned, bytes a positive multiple of 16) once, with the access of the
+ * batch-1 kernels (16-byte non-temporal loads from every lane; workgroup g,
+ * thread t reads 16-byte words g*256 + t + i*stride, stride = 256 * workgroups).
+ * Workgroup g writes the XOR of the 32-bit words it read to sink[g] (device,
+ * sink_words >= 1 words); *workgroups (host) receives the workgroup count,
+ * min(sink_words, 8 per compute unit).  The XOR of sink[0 .. *workgroups) is the
+ * XOR of the whole buffer, so every word was read exactly once.  Asynchronous
+ * on stream; QBL_E_ARG for a null or misaligned pointer or a bad size. */
+qbl_status qbl_hbm_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t sink_words,
+                         int32_t* workgroups, void* stream);
+
 /* ------------------------------------------------------------- timing --- */
 
 /* Kernel timing for measurement tools.  While enabled (on != 0), every launch
@@ -432,7 +445,7 @@ qbl_status qbl_requantize(qbl_comp* comp, int32_t linear, void* blocks_out, int6
  * the recorded events and returns, per kernel kind (0 = batch-1 / batched
  * dequant-GEMV, 1 = glue/shrink prep, 2 = JIT prefill GEMM), the number of
  * launches and their
- * summed duration in milliseconds (3 = qbl_requantize).  Timing adds host work per launch: leave it
+ * summed duration in milliseconds (3 = qbl_requantize, 4 = qbl_hbm_probe).  Timing adds host work per launch: leave it
  * off in production. */
 qbl_status qbl_profile_enable(int32_t on);
 qbl_status qbl_profile_read(int32_t kind, int64_t* launches, double* total_ms);

@@ -108,6 +108,7 @@ EXPORTS = {
     "qbl_block": (_i32, [_vp, _i32, _vp, _vp, _vp, _i64, _vp]),
     "qbl_decode": (_i32, [_vp, _i32, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
     "qbl_requantize": (_i32, [_vp, _i32, _vp, _i64, _vp]),
+    "qbl_hbm_probe": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
     "qbl_profile_enable": (_i32, [_i32]),
     "qbl_profile_read": (_i32, [_i32, _vp, _vp]),
 }
@@ -371,6 +372,17 @@ class Library:
                                              _stream(stream)))
 
     # -- timing ------------------------------------------------------------------
+    def qbl_hbm_probe(self, buf, sink, stream=None) -> int:
+        """Read all of the device tensor buf once (read-only streaming probe); the
+        XOR of each workgroup's words goes to sink (device int32/uint32 tensor).
+        Returns the number of workgroups (sink words written)."""
+        if sink.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("sink must hold 32-bit words")
+        wg = ctypes.c_int32()
+        self._check(self._lib.qbl_hbm_probe(_dev_ptr(buf), buf.numel() * buf.element_size(), _dev_ptr(sink),
+                                            sink.numel(), ctypes.addressof(wg), _stream(stream)))
+        return wg.value
+
     def qbl_profile_enable(self, on: bool) -> None:
         self._check(self._lib.qbl_profile_enable(1 if on else 0))
 
@@ -381,7 +393,7 @@ class Library:
         return n.value, ms.value
 
 
-KIND_GEMV, KIND_PREP, KIND_JIT, KIND_DAR = 0, 1, 2, 3
+KIND_GEMV, KIND_PREP, KIND_JIT, KIND_DAR, KIND_PROBE = 0, 1, 2, 3, 4
 
 _default = Library(_SO)
 _lib = _default._lib

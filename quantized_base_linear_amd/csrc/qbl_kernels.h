@@ -195,5 +195,10 @@ hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc);
 
 int64_t jit_workspace_bytes(int n, int k, int total_rank);
 hipError_t launch_dar(const DarArgs& a, const LaunchCtx& lc);
+// Read-only streaming probe: reads `bytes` (a multiple of 16) at buf once; the
+// XOR of each workgroup's words goes to sink[workgroup] for probe_workgroups()
+// workgroups.
+int probe_workgroups(int sink_words);
+hipError_t launch_hbm_probe(const void* buf, int64_t bytes, uint32_t* sink, int sink_words, const LaunchCtx& lc);
 
 }  // namespace qbl

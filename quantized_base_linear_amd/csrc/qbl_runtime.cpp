@@ -1461,6 +1461,23 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
   })
 }
 
+extern "C" qbl_status qbl_hbm_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t sink_words,
+                                    int32_t* workgroups, void* stream) {
+  QBL_TRY({
+    if (!buf || !sink || !workgroups) return fail(QBL_E_ARG, "null pointer");
+    if (bytes < 16 || bytes % 16) return fail(QBL_E_ARG, "bytes must be a positive multiple of 16");
+    if (reinterpret_cast<uintptr_t>(buf) % 16) return fail(QBL_E_ARG, "buf must be 16-byte aligned");
+    if (sink_words < 1) return fail(QBL_E_ARG, "sink_words must be >= 1");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    KernelTimer tm(4, st);
+    hipError_t e = qbl::launch_hbm_probe(buf, bytes, sink, sink_words, tm.ctx());
+    if (e != hipSuccess) return hip_fail(e, "probe launch");
+    tm.stop();
+    *workgroups = qbl::probe_workgroups(sink_words);
+    return QBL_OK;
+  })
+}
+
 extern "C" qbl_status qbl_requantize(qbl_comp* comp, int32_t linear, void* blocks_out, int64_t out_bytes,
                                      void* stream) {
   QBL_TRY({

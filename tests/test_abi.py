@@ -121,3 +121,23 @@ def test_errors_leave_a_message():
     with pytest.raises(q.QblError):
         q.qbl_quantize(q.QBL_Q8_0, np.zeros((2, 48), np.float32))
     assert "multiple of 32" in q.qbl_last_error()
+
+
+def test_hbm_probe_rejects_bad_arguments_before_any_device_call():
+    import ctypes
+    lib = q._lib
+    wg = ctypes.c_int32(-5)
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every case fails validation first
+    cases = [
+        (None, 64, fake, 4),          # null buffer
+        (fake, 64, None, 4),          # null sink
+        (fake, 0, fake, 4),           # empty
+        (fake, 40, fake, 4),          # not a multiple of 16
+        (ctypes.c_void_p(4104), 64, fake, 4),  # misaligned
+        (fake, 64, fake, 0),          # no sink words
+    ]
+    for buf, nbytes, sink, words in cases:
+        assert lib.qbl_hbm_probe(buf, nbytes, sink, words, ctypes.addressof(wg), None) == -1, (nbytes, words)
+        assert q.qbl_last_error()
+    assert lib.qbl_hbm_probe(fake, 64, fake, 4, None, None) == -1
+    assert wg.value == -5
