@@ -358,7 +358,9 @@ qbl_status qbl_fault_inject(int32_t point, int32_t after);
  * first use (e.g. hipMemset) so that it holds no stale number; the library
  * keeps it valid afterwards.  Launch numbers repeat after 2^32 launches.  Runs
  * sharing one workspace must be ordered on one stream: concurrent runs on one
- * workspace race on its contents. */
+ * workspace race on its contents.  A launch's number is fixed when the run is
+ * enqueued, so batch-1 runs must not be captured into a HIP graph: a replayed
+ * launch would accept the values its previous replay left. */
 qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index, int32_t m,
                                int64_t* bytes_out);
 
