@@ -154,7 +154,11 @@ __device__ __forceinline__ float dot_q4(const uint4 q, const float4* xv) {
   float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = v[w] & 0x0F0F0F0Fu, hi = (v[w] >> 4) & 0x0F0F0F0Fu;
+    uint32_t lo = v[w] & 0x0F0F0F0Fu, hi = (v[w] >> 4) & 0x0F0F0F0Fu;
+    // The masked words are hidden from the optimiser: knowing the masks, it
+    // would extract every nibble with its own bit-field instruction before the
+    // conversion; opaque, each byte converts in one v_cvt_f32_ubyteN.
+    asm("" : "+v"(lo), "+v"(hi));
     const float4 xa = xv[2 * w], xb = xv[2 * w + 1];
     s0 = fmaf(ub(lo, 0), xa.x, s0);
     s1 = fmaf(ub(hi, 0), xa.y, s1);
