@@ -22,7 +22,9 @@ __device__ __forceinline__ float dpp_mov(float v) {
 // active.
 template <int CTRL>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  // bound_ctrl: no lane keeps an old value (every source lane is in its quad),
+  // so no register needs clearing before the move
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ float lane_value(float v, int lane) {
