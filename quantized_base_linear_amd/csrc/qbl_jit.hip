@@ -107,7 +107,8 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
   uint16_t* Ws0 = jit_lds + 2 * kXsElems;
   uint16_t* As0 = Ws0 + 2 * kWsElems;  // At rows of a K-step, staged once per workgroup
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // the wave index is uniform; conditions derived from it become scalar branches
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, h = lane >> 5;
   const int N = a.n, K = a.k, M = a.m;
   const int n0 = blockIdx.x * JBN, m0 = blockIdx.y * JBM;
@@ -210,47 +211,62 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
         dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, dsum, 0, 0, 0);
       }
     }
-    // a K block past the matrix contributes zeros (d = m = 0 and no adapter term)
-    const bool kin = k0 + 32 * kb < K;
-    float d, mn;
-    if constexpr (QT == QBL_FMT_Q4K) {  // the block is sub-block (k / 32) % 8 of its super-block
-      float D, M;
-      q4k_step_offset(o.hd, (min(k0 + 32 * kb, K - 32) / 32) & 7, D, M);
-      d = kin ? D : 0.0f;
-      mn = kin ? -M : 0.0f;
-    } else {
-      d = kin ? h2f(scv) : 0.0f;
-      mn = QT == QBL_FMT_Q8 ? -128.0f * d : (kin ? h2f(scv >> 16) : 0.0f);
-    }
-    // lane (col, h): weights k = 16 h + v, v = 0..15, of row col
-    uint32_t packed[8];
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      float wv[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // q8_0: d (u - 128) = fma(d, u, -128 d), u the offset-binary byte; q4_sm: fma(d, q, m);
-        // q4_K: fma(D, q, -M).  Each is float32(dequant) (products of at most 21
-        // significant bits, then one rounding for the q4 formats), as in the recipe.
-        const int e = v + j;
-        float deq;
-        if (QT == QBL_FMT_Q8)
-          deq = d * (float)((qw[e >> 2] >> (8 * (e & 3))) & 0xFFu) + mn;
-        else
-          deq = fmaf(d, (float)((qw[e >> 3] >> (4 * (e & 7))) & 0xFu), mn);
-        wv[j] = RS > 0 && kin ? deq + dsum[e] : deq;
+    // a K block past the matrix contributes zeros (the wave's condition, uniform:
+    // a scalar branch, no per-element selects)
+    if (k0 + 32 * kb < K) {
+      float d, mn;
+      if constexpr (QT == QBL_FMT_Q4K) {  // the block is sub-block (k / 32) % 8 of its super-block
+        float D, M;
+        q4k_step_offset(o.hd, ((k0 + 32 * kb) / 32) & 7, D, M);
+        d = D;
+        mn = -M;
+      } else {
+        d = h2f(scv);
+        mn = QT == QBL_FMT_Q8 ? -128.0f * d : h2f(scv >> 16);
       }
-      packed[v >> 1] = pack_bf16(wv[0], wv[1]);
-    }
-    *reinterpret_cast<uint4*>(wrow) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    *reinterpret_cast<uint4*>(wrow + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    uint16_t* xs = Xs0 + b * kXsElems;
+      // lane (col, h): weights k = 16 h + v, v = 0..15, of row col
+      uint32_t packed[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + JTHREADS * c;
-      const int row = idx >> 3, c16 = idx & 7;
-      const bool xin = m0 + row < M && k0 + 8 * c16 < K;
-      *reinterpret_cast<uint4*>(xs + row * JLD + 8 * c16) = xin ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+      for (int v = 0; v < 16; v += 2) {
+        float wv[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          // q8_0: d (u - 128) = fma(d, u, -128 d), u the offset-binary byte; q4_sm: fma(d, q, m);
+          // q4_K: fma(D, q, -M).  Each is float32(dequant) (products of at most 21
+          // significant bits, then one rounding for the q4 formats), as in the recipe.
+          const int e = v + j;
+          float deq;
+          if (QT == QBL_FMT_Q8)
+            deq = d * (float)((qw[e >> 2] >> (8 * (e & 3))) & 0xFFu) + mn;
+          else
+            deq = fmaf(d, (float)((qw[e >> 3] >> (4 * (e & 7))) & 0xFu), mn);
+          wv[j] = RS > 0 ? deq + dsum[e] : deq;
+        }
+        packed[v >> 1] = pack_bf16(wv[0], wv[1]);
+      }
+      *reinterpret_cast<uint4*>(wrow) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      *reinterpret_cast<uint4*>(wrow + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    } else {
+      *reinterpret_cast<uint4*>(wrow) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(wrow + 8) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // the X tile: stored as loaded when it lies inside the matrix (the workgroup's
+    // condition, uniform), else with the parts outside zeroed
+    uint16_t* xs = Xs0 + b * kXsElems;
+    if (m0 + JBM <= M && k0 + JBK <= K) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int idx = tid + JTHREADS * c;
+        *reinterpret_cast<uint4*>(xs + (idx >> 3) * JLD + 8 * (idx & 7)) = xr[c];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int idx = tid + JTHREADS * c;
+        const int row = idx >> 3, c16 = idx & 7;
+        const bool xin = m0 + row < M && k0 + 8 * c16 < K;
+        *reinterpret_cast<uint4*>(xs + row * JLD + 8 * c16) = xin ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   };
 
