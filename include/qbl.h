@@ -433,9 +433,10 @@ qbl_status qbl_requantize(qbl_comp* comp, int32_t linear, void* blocks_out, int6
  * thread t reads 16-byte words g*256 + t + i*stride, stride = 256 * workgroups).
  * Workgroup g writes the XOR of the 32-bit words it read to sink[g] (device,
  * sink_words >= 1 words); *workgroups (host) receives the workgroup count,
- * min(sink_words, 8 per compute unit).  The XOR of sink[0 .. *workgroups) is the
- * XOR of the whole buffer, so every word was read exactly once.  Asynchronous
- * on stream; QBL_E_ARG for a null or misaligned pointer or a bad size. */
+ * min(sink_words, 8 per compute unit).  Reading every word exactly once makes
+ * the XOR of sink[0 .. *workgroups) equal the XOR of the whole buffer (a check
+ * for callers: a word read twice would cancel).  Asynchronous on stream;
+ * QBL_E_ARG for a null or misaligned pointer or a bad size. */
 qbl_status qbl_hbm_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t sink_words,
                          int32_t* workgroups, void* stream);
 
@@ -445,10 +446,9 @@ qbl_status qbl_hbm_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t
  * of the library's kernels is bracketed by a pair of HIP events recorded on the
  * launch stream.  Enabling clears earlier records.  qbl_profile_read waits for
  * the recorded events and returns, per kernel kind (0 = batch-1 / batched
- * dequant-GEMV, 1 = glue/shrink prep, 2 = JIT prefill GEMM), the number of
- * launches and their
- * summed duration in milliseconds (3 = qbl_requantize, 4 = qbl_hbm_probe).  Timing adds host work per launch: leave it
- * off in production. */
+ * dequant-GEMV, 1 = glue/shrink prep, 2 = JIT prefill GEMM, 3 = qbl_requantize,
+ * 4 = qbl_hbm_probe), the number of launches and their summed duration in
+ * milliseconds.  Timing adds host work per launch: leave it off in production. */
 qbl_status qbl_profile_enable(int32_t on);
 qbl_status qbl_profile_read(int32_t kind, int64_t* launches, double* total_ms);
 
