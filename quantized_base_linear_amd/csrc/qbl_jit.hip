@@ -20,6 +20,8 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "qbl_device.h"
 #include "qbl_kernels.h"
 
@@ -52,31 +54,60 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
 // scale folded into B:  At[k][t] = bf16(A_cat[t][k]),  sB[n][t] = bf16(f32(s_i B_i[n][j]))
 // where t runs over the concatenated ranks (zero beyond the total rank).
 // ---------------------------------------------------------------------------
-__global__ void stage_lora_kernel(JitArgs a, int tp) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nat = (int64_t)a.k * tp, nsb = (int64_t)a.n * tp;
-  uint16_t* At = a.ws;
-  uint16_t* sB = a.ws + ((nat * 2 + 255) / 256 * 256) / 2;
-  if (i < nat) {
-    const int k = (int)(i / tp), t = (int)(i % tp);
-    float v = 0.0f;
+// At goes through an LDS tile of 64 ranks x 16 inputs per workgroup: each thread
+// reads 4 consecutive inputs of one rank row of A (16 bytes) and writes 4
+// consecutive ranks of one row of At.  The adapter loop runs over j uniformly, so
+// the factor pointers are scalar loads.
+constexpr int kStageT = 64, kStageK = 16;
+__device__ __forceinline__ void stage_at_tile(const JitArgs& a, int tp, int kx, int ty) {
+  __shared__ float tile[kStageT][kStageK + 1];
+  const int k0 = kx * kStageK, t0 = ty * kStageT;
+  {
+    const int tt = threadIdx.x >> 2, kq = 4 * (threadIdx.x & 3), t = t0 + tt;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     int base = 0;
     for (int j = 0; j < a.n_ad; ++j) {
-      if (t >= base && t < base + a.rank[j]) v = a.A[j][(int64_t)(t - base) * a.k + k];
+      if (t >= base && t < base + a.rank[j] && k0 + kq < a.k)
+        v = *reinterpret_cast<const float4*>(a.A[j] + (int64_t)(t - base) * a.k + k0 + kq);
       base += a.rank[j];
     }
-    At[i] = bf16_rne(v);
-  } else if (i < nat + nsb) {
-    const int64_t o = i - nat;
-    const int n = (int)(o / tp), t = (int)(o % tp);
-    float v = 0.0f;
-    int base = 0;
-    for (int j = 0; j < a.n_ad; ++j) {
-      if (t >= base && t < base + a.rank[j]) v = a.scale[j] * a.B[j][(int64_t)n * a.rank[j] + (t - base)];
-      base += a.rank[j];
-    }
-    sB[o] = bf16_rne(v);
+    tile[tt][kq] = v.x;
+    tile[tt][kq + 1] = v.y;
+    tile[tt][kq + 2] = v.z;
+    tile[tt][kq + 3] = v.w;
   }
+  __syncthreads();
+  uint16_t* At = a.ws;
+  const int kk = threadIdx.x >> 4, tq = 4 * (threadIdx.x & 15), k = k0 + kk;
+  if (k < a.k && t0 + tq < tp) {
+    const uint32_t lo = bf16_rne(tile[tq][kk]) | ((uint32_t)bf16_rne(tile[tq + 1][kk]) << 16);
+    const uint32_t hi = bf16_rne(tile[tq + 2][kk]) | ((uint32_t)bf16_rne(tile[tq + 3][kk]) << 16);
+    *reinterpret_cast<uint2*>(At + (int64_t)k * tp + t0 + tq) = make_uint2(lo, hi);
+  }
+}
+
+// sB[n][t] = bf16(f32(s_j B_j[n][t - base_j])), element o = n * tp + t per
+// thread (32-bit index arithmetic; the adapter loop over j is uniform)
+__device__ __forceinline__ void stage_sb_elem(const JitArgs& a, int tp, uint32_t o) {
+  if (o >= (uint32_t)a.n * (uint32_t)tp) return;
+  const int n = (int)(o / (uint32_t)tp), t = (int)(o % (uint32_t)tp);
+  const int64_t nat = (int64_t)a.k * tp;
+  uint16_t* sB = a.ws + ((nat * 2 + 255) / 256 * 256) / 2;
+  float v = 0.0f;
+  int base = 0;
+  for (int j = 0; j < a.n_ad; ++j) {
+    if (t >= base && t < base + a.rank[j]) v = a.scale[j] * a.B[j][(int64_t)n * a.rank[j] + (t - base)];
+    base += a.rank[j];
+  }
+  sB[o] = bf16_rne(v);
+}
+
+// One launch for both: workgroups [0, at_wgs) stage At tiles (ceil(k/16) along
+// k, then the rank tiles), the rest sB, 256 elements each.
+__global__ __launch_bounds__(256) void stage_lora_kernel(JitArgs a, int tp, int at_kt, int at_wgs) {
+  const int b = blockIdx.x;
+  if (b < at_wgs) stage_at_tile(a, tp, b % at_kt, b / at_kt);
+  else stage_sb_elem(a, tp, (uint32_t)(b - at_wgs) * 256u + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -377,10 +408,11 @@ hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc) {
   if (a.k % 32 || a.n < 1 || a.m < 1) return hipErrorInvalidValue;
   const int tp = rank_pad(a.total_rank);
   if (tp > 0) {
-    const int64_t total = (int64_t)a.k * tp + (int64_t)a.n * tp;
-    const int threads = 256;
-    hipLaunchKernelGGL(stage_lora_kernel, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0,
-                       lc.stream, a, tp);
+    if ((int64_t)a.n * tp >= (int64_t)1 << 32 || a.k % 4) return hipErrorInvalidValue;
+    const int at_kt = (a.k + kStageK - 1) / kStageK, at_wgs = at_kt * ((tp + kStageT - 1) / kStageT);
+    const int64_t sb_wgs = ((int64_t)a.n * tp + 255) / 256;
+    hipLaunchKernelGGL(stage_lora_kernel, dim3((unsigned)(at_wgs + sb_wgs)), dim3(256), 0, lc.stream, a, tp, at_kt,
+                       at_wgs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
