@@ -157,8 +157,12 @@ struct ListImpl {
         hipEventRecord(u.second, st);
         return;
       }
+    // The event only has to tell when the work is done (to free the list's
+    // memory), not make device memory visible to the host: without the
+    // system-scope fence its record costs no cache writeback on the GPU (with
+    // it, ~3 us of every run).
     hipEvent_t ev;
-    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess) {
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence) == hipSuccess) {
       hipEventRecord(ev, st);
       uses.emplace_back(st, ev);
     } else {

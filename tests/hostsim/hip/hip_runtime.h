@@ -28,6 +28,7 @@ typedef enum hipMemcpyKind {
 
 #define hipEventDefault 0x0
 #define hipEventDisableTiming 0x2
+#define hipEventDisableSystemFence 0x20000000
 
 hipError_t hipGetDevice(int* device);
 hipError_t hipSetDevice(int device);
