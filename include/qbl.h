@@ -340,7 +340,27 @@ qbl_status qbl_comp_free(qbl_comp* comp);
 #define QBL_FAULT_DEVICE_ALLOC 1
 #define QBL_FAULT_CORRUPT 2
 #define QBL_FAULT_SWAP 3
+/*   QBL_FAULT_HANDOFF: the next batch-1 launch that hands adapter values over
+ *     inside itself (see qbl_workspace_bytes) has its readers wait, with a zero
+ *     time budget, for a launch number no writer stores: every wait gives up,
+ *     the kernel still ends normally, and the failure is recorded for
+ *     qbl_device_status (the run call itself returns QBL_OK: it only enqueues). */
+#define QBL_FAULT_HANDOFF 4
 qbl_status qbl_fault_inject(int32_t point, int32_t after);
+
+/* Device-side failures that a run call cannot see when it enqueues
+ * ([overlay] "Explicit Correctness and Atomicity Invariants": a hard,
+ * deterministic error rather than a silent wrong result).  Batch-1 launches
+ * hand values over between their workgroups (the adapter shrink, sparse row
+ * sums), and a reader waits for each value under a time budget (50 ms per
+ * thread and launch).  A wait that runs out records the failure in a
+ * process-wide word of host memory, and that run's outputs are wrong.  While a
+ * failure is recorded, every run call (qbl_linear, qbl_linear_jit, qbl_block,
+ * qbl_decode) returns QBL_E_DEVICE without enqueueing anything.  This call
+ * returns QBL_E_DEVICE once per recorded failure and clears the record, else
+ * QBL_OK.  It does not synchronise: synchronise the streams first to include
+ * every finished launch. */
+qbl_status qbl_device_status(void);
 
 /* ------------------------------------------------------------------ runs --- */
 
@@ -356,11 +376,15 @@ qbl_status qbl_fault_inject(int32_t point, int32_t after);
  * consumes it: each shrink value is stored with the launch's number beside it,
  * and readers wait until they see that number.  Zero the buffer once before its
  * first use (e.g. hipMemset) so that it holds no stale number; the library
- * keeps it valid afterwards.  Launch numbers repeat after 2^32 launches.  Runs
- * sharing one workspace must be ordered on one stream: concurrent runs on one
- * workspace race on its contents.  A launch's number is fixed when the run is
- * enqueued, so batch-1 runs must not be captured into a HIP graph: a replayed
- * launch would accept the values its previous replay left. */
+ * keeps it valid afterwards.  Launch numbers are process-wide and repeat after
+ * 2^32 launches: a stale word could only be taken for a fresh one if no launch
+ * had rewritten it in the last 2^32 launches of the process.  Runs sharing one
+ * workspace must be ordered on one stream: concurrent runs on one workspace race
+ * on its contents.  A launch's number is fixed when the run is enqueued, so a
+ * replayed graph would accept the values its previous replay left: batch-1 runs
+ * with adapters return QBL_E_STATE on a stream that is capturing a graph (checked
+ * before anything is enqueued).  A reader's wait is bounded; see
+ * qbl_device_status. */
 qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index, int32_t m,
                                int64_t* bytes_out);
 

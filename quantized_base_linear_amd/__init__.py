@@ -38,7 +38,7 @@ QBL_MAX_RANK = 256
 QBL_MAX_TOTAL_RANK = 512
 QBL_MAX_BATCH = 8
 OP_LINEAR, OP_JIT, OP_BLOCK = 0, 1, 2
-QBL_FAULT_DEVICE_ALLOC, QBL_FAULT_CORRUPT, QBL_FAULT_SWAP = 1, 2, 3
+QBL_FAULT_DEVICE_ALLOC, QBL_FAULT_CORRUPT, QBL_FAULT_SWAP, QBL_FAULT_HANDOFF = 1, 2, 3, 4
 
 STATUS = {0: "QBL_OK", -1: "QBL_E_ARG", -2: "QBL_E_SHAPE", -3: "QBL_E_FORMAT",
           -4: "QBL_E_NONFINITE", -5: "QBL_E_NOMEM", -6: "QBL_E_BUDGET", -7: "QBL_E_BUSY",
@@ -102,6 +102,7 @@ EXPORTS = {
     "qbl_identity_digest": (_i32, [_vp, _vp, _vp, _i32, _vp]),
     "qbl_comp_free": (_i32, [_vp]),
     "qbl_fault_inject": (_i32, [_i32, _i32]),
+    "qbl_device_status": (_i32, []),
     "qbl_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, _vp]),
     "qbl_linear": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
     "qbl_linear_jit": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
@@ -329,6 +330,10 @@ class Library:
 
     def qbl_fault_inject(self, point: int, after: int) -> None:
         self._check(self._lib.qbl_fault_inject(point, after))
+
+    def qbl_device_status(self) -> None:
+        """Raises QblError(QBL_E_DEVICE) once per recorded device-side hand-off failure."""
+        self._check(self._lib.qbl_device_status())
 
     # -- runs --------------------------------------------------------------------
     def qbl_workspace_bytes(self, comp, op: int, index: int = 0, m: int = 1) -> int:

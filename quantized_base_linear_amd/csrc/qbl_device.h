@@ -264,14 +264,38 @@ __device__ __forceinline__ void csr_rows_dot(const uint32_t* const (&col)[R], co
   }
 }
 
-// A value handed from one workgroup to others in the same launch: one 64-bit
-// word, the launch's (or phase's) tag in the high half and the float in the low
-// half, read with device-coherent relaxed loads until the tag matches (bounded).
-__device__ __forceinline__ float tagged_get(const uint64_t* p, uint32_t tag, int spin_limit) {
+// Waits for values handed from one workgroup to others in the same launch.
+// All waits of one thread share one deadline on the 100 MHz wall clock, set at
+// its first wait that finds a stale word; past it the thread records the
+// failure in the host-visible status word (one vector store to coherent host
+// memory) and takes every later word as it finds it, without waiting.  So a
+// broken hand-off costs a launch at most one budget, and the caller learns of
+// it from the library (a run call or the status call) instead of from its
+// numbers.
+struct HandoffWait {
+  uint32_t* fail;      // status word, device address of coherent host memory
+  int64_t budget;      // wall-clock ticks one thread may spend waiting
+  int64_t deadline;
+  bool gave_up;
+  __device__ HandoffWait(uint32_t* f, int64_t b) : fail(f), budget(b), deadline(-1), gave_up(false) {}
+};
+
+// One value handed over: a 64-bit word, the launch's (or phase's) tag in the
+// high half and the float in the low half, read with device-coherent relaxed
+// loads until the tag matches (bounded as above).
+__device__ __forceinline__ float tagged_get(const uint64_t* p, uint32_t tag, HandoffWait& hw) {
   uint64_t w = __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int spins = 0; (uint32_t)(w >> 32) != tag && spins < spin_limit; ++spins) {
+  if ((uint32_t)(w >> 32) == tag || hw.gave_up) return __uint_as_float((uint32_t)w);
+  if (hw.deadline < 0) hw.deadline = wall_clock64() + hw.budget;
+  for (;;) {
     __builtin_amdgcn_s_sleep(1);
     w = __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w >> 32) == tag) break;
+    if (wall_clock64() > hw.deadline) {
+      hw.gave_up = true;
+      __hip_atomic_store(hw.fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      break;
+    }
   }
   return __uint_as_float((uint32_t)w);
 }

@@ -657,14 +657,15 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   }
 
   // ---- shrink values of this launch, then the row outputs
+  HandoffWait hw(f.fail, f.wait_ticks);
   if (!tw_out) issue_t();
 #pragma unroll
   for (int m = 0; m < kTW; ++m) {
     const int j = tid + m * NT;
     if (j < f.rows_total)
-      tl[j] = (uint32_t)(tw[m] >> 32) == f.tag ? __uint_as_float((uint32_t)tw[m]) : tagged_get(tcopy + j, f.tag, f.spin_limit);
+      tl[j] = (uint32_t)(tw[m] >> 32) == f.read_tag ? __uint_as_float((uint32_t)tw[m]) : tagged_get(tcopy + j, f.read_tag, hw);
   }
-  for (int j = tid + kTW * NT; j < f.rows_total; j += NT) tl[j] = tagged_get(tcopy + j, f.tag, f.spin_limit);
+  for (int j = tid + kTW * NT; j < f.rows_total; j += NT) tl[j] = tagged_get(tcopy + j, f.read_tag, hw);
 
   // the first sparse value of each row, requested before the barrier so that
   // its round trip overlaps the wait there
@@ -692,8 +693,8 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
         float p = 0.0f;
         if (row < g.n) {
           const uint64_t* w = f.sp + f.sp_base[slot_seg(s)][i] + row;
-          p = i == sp_first && (uint32_t)(spw >> 32) == f.tag ? __uint_as_float((uint32_t)spw)
-                                                             : tagged_get(w, f.tag, f.spin_limit);
+          p = i == sp_first && (uint32_t)(spw >> 32) == f.read_tag ? __uint_as_float((uint32_t)spw)
+                                                                  : tagged_get(w, f.read_tag, hw);
         }
         v = fmaf(g.lora.scale[i], cscale * p, v);
         continue;

@@ -111,8 +111,10 @@ struct FusedArgs {
   int64_t sp_bytes;    // CSR bytes of the launch (for the launcher's split of the round)
   int sp_base[kMaxSegs][kMaxAdapters];  // first item of (segment, adapter), -1 unless the adapter is sparse
   uint64_t* sp;        // sp_items tagged words (launch number << 32 | float bits)
-  int spin_limit;      // bound on the sleeps of one wait for a shrink result
-  uint32_t tag;        // this launch's number, never 0
+  int64_t wait_ticks;  // wall-clock ticks (100 MHz) a thread may spend waiting for handed-over values
+  uint32_t* fail;      // status word a wait sets when it gives up (coherent host memory)
+  uint32_t tag;        // this launch's number, never 0: written beside every handed-over value
+  uint32_t read_tag;   // the number readers wait for: tag (another value only under test fault injection)
   uint64_t* t;         // kTCopies copies of the rows_total shrink results, (tag << 32) | float bits
   int64_t t_copy_stride;  // words between copies (see t_copy_stride())
   PrepEntry ent[kMaxPrepEntries];

@@ -257,7 +257,7 @@ qbl_status check_device(const qbl_base* b) {
 }
 
 // -- test-only fault points (qbl_fault_inject) --
-constexpr int kFaultPoints = QBL_FAULT_SWAP + 1;
+constexpr int kFaultPoints = QBL_FAULT_HANDOFF + 1;
 std::atomic<int> g_fault[kFaultPoints];
 
 // True once: on the hit that `point` was armed for.
@@ -266,6 +266,60 @@ bool fault_fires(int point) {
   while (v > 0)
     if (g_fault[point].compare_exchange_weak(v, v - 1)) return v == 1;
   return false;
+}
+
+// -- the status word of in-launch hand-offs --
+// One word of coherent pinned host memory for the process: a bounded device
+// wait that gives up stores 1 into it (see HandoffWait in qbl_device.h).  Host
+// code reads it with plain loads, so a run call can refuse while it is set
+// without synchronising anything.
+struct StatusWord {
+  uint32_t* host = nullptr;
+  uint32_t* dev = nullptr;
+  hipError_t err = hipSuccess;
+};
+
+const StatusWord& status_word() {
+  static StatusWord w = [] {
+    StatusWord s;
+    void* h = nullptr;
+    s.err = hipHostMalloc(&h, 256, hipHostMallocCoherent | hipHostMallocMapped);
+    if (s.err != hipSuccess) return s;
+    std::memset(h, 0, 256);
+    void* d = nullptr;
+    s.err = hipHostGetDevicePointer(&d, h, 0);
+    if (s.err != hipSuccess) return s;
+    s.host = static_cast<uint32_t*>(h);
+    s.dev = static_cast<uint32_t*>(d);
+    return s;
+  }();
+  return w;
+}
+
+// QBL_E_DEVICE while a failed hand-off is recorded and not yet read by
+// qbl_device_status; QBL_E_NOMEM if the word could not be allocated.
+qbl_status check_handoffs() {
+  const StatusWord& w = status_word();
+  if (!w.host) return fail(QBL_E_NOMEM, "status word: %s", hipGetErrorString(w.err));
+  if (__atomic_load_n(w.host, __ATOMIC_ACQUIRE))
+    return fail(QBL_E_DEVICE,
+                "a device-side wait for a value handed over inside a launch gave up; an earlier run's "
+                "outputs are wrong (qbl_device_status reads and clears this)");
+  return QBL_OK;
+}
+
+// Batch-1 runs with adapters hand values over inside a launch under a number
+// fixed when the run is enqueued; a replayed graph would accept the words its
+// previous replay left.  Such runs refuse a capturing stream.
+qbl_status refuse_capture(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(QBL_E_STATE,
+                "batch-1 runs with adapters hand values over inside a launch under a number fixed at "
+                "enqueue and cannot be captured into a HIP graph");
+  return QBL_OK;
 }
 
 hipError_t dev_alloc(void** p, int64_t bytes) {
@@ -921,6 +975,16 @@ extern "C" qbl_status qbl_comp_free(qbl_comp* comp) {
   return QBL_OK;
 }
 
+extern "C" qbl_status qbl_device_status(void) {
+  QBL_TRY({
+    const StatusWord& w = status_word();
+    if (!w.host) return fail(QBL_E_NOMEM, "status word: %s", hipGetErrorString(w.err));
+    if (__atomic_exchange_n(w.host, 0u, __ATOMIC_ACQ_REL))
+      return fail(QBL_E_DEVICE, "a device-side wait for a value handed over inside a launch gave up");
+    return QBL_OK;
+  })
+}
+
 extern "C" qbl_status qbl_fault_inject(int32_t point, int32_t after) {
   if (point < 1 || point >= kFaultPoints) return fail(QBL_E_ARG, "unknown fault point %d", point);
   if (after < 0) return fail(QBL_E_ARG, "negative count");
@@ -1096,6 +1160,13 @@ int64_t blocks_spmax(const qbl_base* base, const ListImpl* L, int first_block, i
   return m;
 }
 
+// True when some linear of the blocks in range has an adapter entry.
+bool blocks_have_entries(const ListImpl* L, int first_block, int n_blocks) {
+  for (int i = 7 * first_block; i < 7 * (first_block + n_blocks); ++i)
+    if (!L->plan[(size_t)i].empty()) return true;
+  return false;
+}
+
 int group_rank(const ListImpl* L, const int* lin, int nlin) {
   int t = 0;
   for (int i = 0; i < nlin; ++i) t += L->total_rank[(size_t)lin[i]];
@@ -1120,7 +1191,9 @@ int blocks_tmax(const ListImpl* L, int first_block, int n_blocks) {
 // otherwise the prep kernel (glue and/or shrink) runs first, then one GEMV per
 // quantisation type present: at batch 2..8 the matrix-core GEMV, which stages
 // its inputs in `stage` first.
-constexpr int kSpinLimit = 1 << 22;  // ~0.1 s of s_sleep(1) before a wait gives up
+// Wall-clock budget (100 MHz ticks) of one thread's waits for handed-over
+// values within a launch: 50 ms, far above any legitimate wait (a few us).
+constexpr int64_t kWaitTicks = 5000000;
 
 // Numbers that tag the shrink results one workgroup hands to others within a
 // launch: unique per launch (mod 2^32), never 0, so a zeroed workspace holds
@@ -1215,8 +1288,16 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     }
     if (f.sp_items > 0 && !sp_buf) return fail(QBL_E_ARG, "the workspace has no room for the sparse values");
     f.sp = sp_buf;
-    f.spin_limit = kSpinLimit;
     f.tag = next_tag();
+    f.read_tag = f.tag;
+    f.wait_ticks = kWaitTicks;
+    f.fail = status_word().dev;
+    if ((T > 0 || f.sp_items > 0) && fault_fires(QBL_FAULT_HANDOFF)) {
+      // readers wait for a number no writer stores, with no budget: every wait
+      // gives up at once and records the failure
+      f.read_tag = f.tag ^ 0x5A5A5A5Au;
+      f.wait_ticks = 0;
+    }
     f.t = reinterpret_cast<uint64_t*>(t_buf);
     f.t_copy_stride = qbl::t_copy_stride(T);
     KernelTimer tm(0, st);
@@ -1407,6 +1488,9 @@ extern "C" qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x,
     const int64_t sp_items = group_sp_items(b, L.get(), &linear, 1);
     if (qbl_status s = check_ws(ws, ws_bytes, linear_ws_bytes(batch, T, D.n, D.k, sp_items))) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (qbl_status s = check_handoffs()) return s;
+    if (batch == 1 && (T > 0 || sp_items > 0))
+      if (qbl_status s = refuse_capture(st)) return s;
     const int lin[1] = {linear};
     float* outs[1] = {y};
     const float* v[1] = {x};
@@ -1456,6 +1540,7 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
     a.total_rank = T;
     a.ws = static_cast<uint16_t*>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (qbl_status s = check_handoffs()) return s;
     const ListUse use{L.get(), st, T > 0};
     KernelTimer tm(2, st);
     hipError_t e = qbl::launch_jit(a, tm.ctx());
@@ -1538,6 +1623,9 @@ extern "C" qbl_status qbl_block(qbl_comp* comp, int32_t block, const float* x, f
     if (qbl_status s = check_ws(ws, ws_bytes, need.bytes)) return s;
     const BlockWs w = block_ws(ws, B.d, B.h, blocks_tmax(L.get(), block, 1), blocks_spmax(b, L.get(), block, 1));
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (qbl_status s = check_handoffs()) return s;
+    if (blocks_have_entries(L.get(), block, 1))
+      if (qbl_status s = refuse_capture(st)) return s;
     const ListUse use{L.get(), st, true};
     if (qbl_status s = run_block(b, L.get(), B, x, 0, w, st)) return s;
     return run_rms(w.dd, B.d, y, st);
@@ -1569,6 +1657,9 @@ extern "C" qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_
     if (qbl_status s = check_ws(ws, ws_bytes, block_ws(nullptr, d, h, tmax, spmax).bytes)) return s;
     const BlockWs w = block_ws(ws, d, h, tmax, spmax);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (qbl_status s = check_handoffs()) return s;
+    if (blocks_have_entries(L.get(), first_block, n_blocks))
+      if (qbl_status s = refuse_capture(st)) return s;
     const ListUse use{L.get(), st, true};
     for (int t = 0; t < n_tokens; ++t) {
       const float* in = t == 0 ? x0 : y_tokens + (int64_t)(t - 1) * d;

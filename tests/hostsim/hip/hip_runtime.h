@@ -44,3 +44,16 @@ hipError_t hipEventElapsedTime(float* ms, hipEvent_t start, hipEvent_t stop);
 hipError_t hipEventDestroy(hipEvent_t event);
 hipError_t hipGetLastError(void);
 const char* hipGetErrorString(hipError_t error);
+
+// pinned host memory (plain host memory here) and stream capture (never active)
+#define hipHostMallocDefault 0x0
+#define hipHostMallocMapped 0x2
+#define hipHostMallocCoherent 0x40000000
+hipError_t hipHostMalloc(void** ptr, size_t size, unsigned flags);
+hipError_t hipHostGetDevicePointer(void** dev, void* host, unsigned flags);
+typedef enum hipStreamCaptureStatus {
+  hipStreamCaptureStatusNone = 0,
+  hipStreamCaptureStatusActive = 1,
+  hipStreamCaptureStatusInvalidated = 2,
+} hipStreamCaptureStatus;
+hipError_t hipStreamIsCapturing(hipStream_t stream, hipStreamCaptureStatus* status);

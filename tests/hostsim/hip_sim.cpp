@@ -127,6 +127,25 @@ hipError_t hipEventDestroy(hipEvent_t event) {
 }
 hipError_t hipGetLastError(void) { return hipSuccess; }
 
+// Pinned host memory is ordinary host memory here, outside the device tally.
+hipError_t hipHostMalloc(void** ptr, size_t size, unsigned) {
+  if (!ptr) return hipErrorInvalidValue;
+  *ptr = std::calloc(1, size ? size : 1);
+  return *ptr ? hipSuccess : hipErrorOutOfMemory;
+}
+
+hipError_t hipHostGetDevicePointer(void** dev, void* host, unsigned) {
+  if (!dev || !host) return hipErrorInvalidValue;
+  *dev = host;
+  return hipSuccess;
+}
+
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* status) {
+  if (!status) return hipErrorInvalidValue;
+  *status = hipStreamCaptureStatusNone;
+  return hipSuccess;
+}
+
 const char* hipGetErrorString(hipError_t error) {
   switch (error) {
     case hipSuccess: return "hipSuccess";
