@@ -405,6 +405,24 @@ qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int32_t index, 
 qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x, float* y, int32_t batch,
                       void* ws, int64_t ws_bytes, void* stream);
 
+/* qbl_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, kernels and results (bit for bit) as qbl_linear, but no workspace
+ * argument.  The workspace is a library-owned array of 32 MiB per GPU, a
+ * file-scope device array that each GPU the library runs on holds until the
+ * process ends; a run needing more (qbl_workspace_bytes op 0) returns
+ * QBL_E_LIMIT before enqueueing anything.  The call allocates no device or host
+ * memory (the first run of an attached list on a stream creates that list's
+ * completion event, as every run entry point does).  The first call on a device
+ * sets the array up: it looks up the array's device address and enqueues a
+ * clear on `stream`; that first call returns QBL_E_STATE on a capturing stream.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (concurrent streams or threads) race
+ * on it and must be ordered by the caller.  Capture rules as qbl_linear (batch-1
+ * runs with adapters refuse a capturing stream). */
+qbl_status qbl_linear_static(qbl_comp* comp, int32_t linear, const float* x, float* y, int32_t batch,
+                             void* stream);
+
 /* Per-layer just-in-time path for prefill ([design] sections 1 and 8: for
  * multi-token GEMM, materialise one layer in scratch, use it, discard it):
  *   W_eff = bf16( float32(deq(W)) + sum_i bf16(s_i B_i) bf16(A_i) )    (tile by tile, on chip)

@@ -105,6 +105,7 @@ EXPORTS = {
     "qbl_device_status": (_i32, []),
     "qbl_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, _vp]),
     "qbl_linear": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
+    "qbl_linear_static": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp]),
     "qbl_linear_jit": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
     "qbl_block": (_i32, [_vp, _i32, _vp, _vp, _vp, _i64, _vp]),
     "qbl_decode": (_i32, [_vp, _i32, _i32, _vp, _vp, _i32, _vp, _i64, _vp]),
@@ -352,6 +353,10 @@ class Library:
         wp, wb = _ws(ws)
         self._check(self._lib.qbl_linear(comp, linear, _dev_ptr(x, torch.float32), _dev_ptr(y, torch.float32),
                                          batch, wp, wb, _stream(stream)))
+
+    def qbl_linear_static(self, comp, linear: int, x, y, batch: int, stream=None) -> None:
+        self._check(self._lib.qbl_linear_static(comp, linear, _dev_ptr(x, torch.float32),
+                                                _dev_ptr(y, torch.float32), batch, _stream(stream)))
 
     def qbl_linear_jit(self, comp, linear: int, x_bf16, y, m: int, ws=None, stream=None) -> None:
         if x_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16):

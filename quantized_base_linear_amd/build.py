@@ -12,8 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libqbl.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["qbl_gemv.hip", "qbl_batched.hip", "qbl_jit.hip", "qbl_dar.hip", "qbl_probe.hip", "qbl_format.cpp",
-           "qbl_runtime.cpp"]
+SOURCES = ["qbl_gemv.hip", "qbl_batched.hip", "qbl_jit.hip", "qbl_dar.hip", "qbl_probe.hip", "qbl_static.hip",
+           "qbl_format.cpp", "qbl_runtime.cpp"]
 # Packed fp32 VALU ops are disabled on purpose (the flag only affects device code).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -195,6 +195,14 @@ constexpr int kTCopies = 8;
 inline int64_t t_copy_stride(int64_t rows) { return (rows + 31) / 32 * 32 + 32; }
 hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc);
 
+// The no-allocation variant of qbl_linear uses one file-scope device array per
+// GPU as its workspace: kStaticScratchBytes (32 MiB) each.  static_scratch
+// returns the current device's copy, setting it up on the device's first call
+// (its address, then a clear enqueued on st; hipErrorStreamCaptureUnsupported
+// if st is capturing then).
+constexpr int64_t kStaticScratchBytes = 32ll << 20;
+hipError_t static_scratch(hipStream_t st, void** out);
+
 int64_t jit_workspace_bytes(int n, int k, int total_rank);
 hipError_t launch_dar(const DarArgs& a, const LaunchCtx& lc);
 // Read-only streaming probe: reads `bytes` (a multiple of 16) at buf once; the

@@ -1471,37 +1471,64 @@ extern "C" qbl_status qbl_workspace_bytes(const qbl_comp* comp, int32_t op, int3
   })
 }
 
+namespace {
+
+// qbl_linear with the workspace either the caller's (ws, ws_bytes) or, when
+// `use_static`, the library's per-device scratch array.
+qbl_status linear_run(qbl_comp* comp, int32_t linear, const float* x, float* y, int32_t batch, void* ws,
+                      int64_t ws_bytes, void* stream, bool use_static) {
+  if (!comp || !x || !y) return fail(QBL_E_ARG, "null pointer");
+  const qbl_base* b = comp->base;
+  if (linear < 0 || linear >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", linear);
+  if (batch < 1 || batch > QBL_MAX_BATCH) return fail(QBL_E_LIMIT, "batch %d outside 1..%d", batch, QBL_MAX_BATCH);
+  if (!aligned16(x) || !aligned16(y)) return fail(QBL_E_ARG, "x and y must be 16-byte aligned");
+  if (x == y) return fail(QBL_E_ARG, "y must not alias x");
+  if (qbl_status s = check_device(b)) return s;
+  std::lock_guard<std::mutex> g(comp->mu);
+  auto L = std::atomic_load(&comp->list);
+  const int T = L->total_rank[(size_t)linear];
+  const DevLinear& D = b->lin[(size_t)linear];
+  const int64_t sp_items = group_sp_items(b, L.get(), &linear, 1);
+  const int64_t need = linear_ws_bytes(batch, T, D.n, D.k, sp_items);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (use_static) {
+    if (need > qbl::kStaticScratchBytes)
+      return fail(QBL_E_LIMIT, "this run needs %lld bytes of scratch; the static array holds %lld", (long long)need,
+                  (long long)qbl::kStaticScratchBytes);
+  } else if (qbl_status s = check_ws(ws, ws_bytes, need)) {
+    return s;
+  }
+  if (qbl_status s = check_handoffs()) return s;
+  if (batch == 1 && (T > 0 || sp_items > 0))
+    if (qbl_status s = refuse_capture(st)) return s;
+  if (use_static && need > 0) {
+    hipError_t e = qbl::static_scratch(st, &ws);
+    if (e == hipErrorStreamCaptureUnsupported)
+      return fail(QBL_E_STATE, "the first static-scratch run on a device sets the array up and cannot be captured");
+    if (e != hipSuccess) return hip_fail(e, "static scratch");
+  }
+  const int lin[1] = {linear};
+  float* outs[1] = {y};
+  const float* v[1] = {x};
+  const ListUse use{L.get(), st, !L->plan[(size_t)linear].empty()};
+  void* stage = batch > 1 ? static_cast<char*>(ws) + linear_t_bytes(batch, T) : nullptr;
+  uint64_t* sp = batch == 1 && sp_items > 0
+                     ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + linear_t_bytes(batch, T))
+                     : nullptr;
+  return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), sp, st, false,
+                   nullptr, stage);
+}
+
+}  // namespace
+
 extern "C" qbl_status qbl_linear(qbl_comp* comp, int32_t linear, const float* x, float* y,
                                  int32_t batch, void* ws, int64_t ws_bytes, void* stream) {
-  QBL_TRY({
-    if (!comp || !x || !y) return fail(QBL_E_ARG, "null pointer");
-    const qbl_base* b = comp->base;
-    if (linear < 0 || linear >= (int)b->lin.size()) return fail(QBL_E_ARG, "linear %d out of range", linear);
-    if (batch < 1 || batch > QBL_MAX_BATCH) return fail(QBL_E_LIMIT, "batch %d outside 1..%d", batch, QBL_MAX_BATCH);
-    if (!aligned16(x) || !aligned16(y)) return fail(QBL_E_ARG, "x and y must be 16-byte aligned");
-    if (x == y) return fail(QBL_E_ARG, "y must not alias x");
-    if (qbl_status s = check_device(b)) return s;
-    std::lock_guard<std::mutex> g(comp->mu);
-    auto L = std::atomic_load(&comp->list);
-    const int T = L->total_rank[(size_t)linear];
-    const DevLinear& D = b->lin[(size_t)linear];
-    const int64_t sp_items = group_sp_items(b, L.get(), &linear, 1);
-    if (qbl_status s = check_ws(ws, ws_bytes, linear_ws_bytes(batch, T, D.n, D.k, sp_items))) return s;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (qbl_status s = check_handoffs()) return s;
-    if (batch == 1 && (T > 0 || sp_items > 0))
-      if (qbl_status s = refuse_capture(st)) return s;
-    const int lin[1] = {linear};
-    float* outs[1] = {y};
-    const float* v[1] = {x};
-    const ListUse use{L.get(), st, !L->plan[(size_t)linear].empty()};
-    void* stage = batch > 1 ? static_cast<char*>(ws) + linear_t_bytes(batch, T) : nullptr;
-    uint64_t* sp = batch == 1 && sp_items > 0
-                       ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + linear_t_bytes(batch, T))
-                       : nullptr;
-    return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), sp, st, false,
-                     nullptr, stage);
-  })
+  QBL_TRY({ return linear_run(comp, linear, x, y, batch, ws, ws_bytes, stream, false); })
+}
+
+extern "C" qbl_status qbl_linear_static(qbl_comp* comp, int32_t linear, const float* x, float* y,
+                                        int32_t batch, void* stream) {
+  QBL_TRY({ return linear_run(comp, linear, x, y, batch, nullptr, 0, stream, true); })
 }
 
 extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint16_t* x_bf16,

@@ -13,6 +13,7 @@ typedef enum hipError_t {
   hipErrorOutOfMemory = 2,
   hipErrorNoDevice = 100,
   hipErrorInvalidDevice = 101,
+  hipErrorStreamCaptureUnsupported = 900,
 } hipError_t;
 
 typedef struct ihipStream_t* hipStream_t;

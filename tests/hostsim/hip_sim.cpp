@@ -173,6 +173,7 @@ int64_t jit_workspace_bytes(int, int, int) { return 0; }
 hipError_t launch_dar(const DarArgs&, const LaunchCtx&) { return hipErrorNoDevice; }
 int probe_workgroups(int sink_words) { return sink_words < 2048 ? sink_words : 2048; }
 hipError_t launch_hbm_probe(const void*, int64_t, uint32_t*, int, const LaunchCtx&) { return hipErrorNoDevice; }
+hipError_t static_scratch(hipStream_t, void**) { return hipErrorNoDevice; }
 }  // namespace qbl
 
 // Inspection of the double, for the tests.
