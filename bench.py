@@ -119,10 +119,20 @@ def time_loop(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def counter_traffic(summary):
-    """HBM bytes per launch measured with rocprofv3 byte counters, as recorded in
-    a profiles/ summary; None when the kernel source changed since then."""
+def sources_sha256(paths):
+    """SHA-256 over the concatenated bytes of the given repository files."""
     import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profile_field(summary, key):
+    """A machine-readable figure of a profiles/ summary (indented `key: value`
+    lines), or None when the summary is missing or any source file the kernel
+    compiles from (its `kernel_sources` line) changed since it was taken."""
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
@@ -132,12 +142,19 @@ def counter_traffic(summary):
             k, v = line.strip().split(":", 1)
             fields[k.strip()] = v.strip()
     try:
-        src = open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() != fields["kernel_source_sha256"]:
+        if sources_sha256(fields["kernel_sources"].split()) != fields["kernel_sources_sha256"]:
             return None
-        return int(float(fields["traffic_bytes_per_launch"]))
+        return float(fields[key])
     except (KeyError, OSError, ValueError):
         return None
+
+
+def counter_traffic(summary):
+    """HBM bytes per launch measured with rocprofv3 byte counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by a copy of known size), as recorded in a profiles/
+    summary; None when the kernel's sources changed since then."""
+    v = profile_field(summary, "traffic_bytes_per_launch")
+    return None if v is None else int(v)
 
 
 def bench_block(torch, q, workloads, args):
@@ -154,10 +171,14 @@ def bench_block(torch, q, workloads, args):
     def step(i):
         q.qbl_block(comp, i % copies, x, ys[i % copies], ws)
 
-    ms = time_loop(torch, step, args.steps, args.warmup)
+    # median over repeats of `steps` timed steps each (HIP events on the stream;
+    # batch-1 runs with adapters refuse graph capture, so the steps are stream
+    # launches)
+    reps = [time_loop(torch, step, args.steps, args.warmup if r == 0 else 2) for r in range(args.repeats)]
+    ms = sorted(reps)[len(reps) // 2]
     step_bytes = sum(linear_bytes(wl, i) for i in range(7))
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"[block] {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+    log(f"[block] {ms * 1e3:.1f} us/step (median of {len(reps)}: {[round(r * 1e3, 1) for r in reps]}), {gbs:.0f} GB/s")
 
     # kernel durations: the same loop with timing events around every launch
     q.qbl_profile_enable(True)
@@ -180,32 +201,159 @@ def bench_block(torch, q, workloads, args):
             "launches_per_step": launches_per_step, "avg_launch_us": round(avg_us, 2),
             "bytes_per_launch": int(gemv_bytes_step / launches_per_step),
             "prep_avg_launch_us": round(ms_prep / max(n_prep, 1) * 1e3, 2) if n_prep else None,
-            "step_us_with_timing_events": round(ms_prof * 1e3, 1)}
+            "step_us_with_timing_events": round(ms_prof * 1e3, 1),
+            "step_us_repeats": [round(r * 1e3, 2) for r in reps]}
+    # the same kernel's average duration from the committed rocprofv3 kernel
+    # trace (kernel-only clock, no timing events), while its sources are unchanged
+    k_only = profile_field("gemv_block7b_q8_r16_kernel_trace.md", "avg_launch_us")
+    roof["rocprof_avg_launch_us"] = k_only
+    if k_only:
+        roof["rocprof_frac"] = round(gemv_bytes_step / launches_per_step / (k_only * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     free_all(q, base, ads, comp)
     return wl, blocks, ms, step_bytes, gbs, roof
 
 
-def cpu_baseline(oracle, wl, blocks, seconds):
-    """The oracle's dual path over the block's seven linears, repeated for about
-    `seconds` of wall time on all host cores."""
+def cpu_block(oracle, wl, blocks, seconds, threads):
+    """GB/s of the oracle's dual path over the block's seven linears, repeated
+    (whole linears, at least one) for about `seconds` of wall time."""
     import numpy as np
     xs = [wl.x(i).astype(np.float64) for i in range(7)]
     ads = [[oracle.Lora(wl.lora_a(i, 0), wl.lora_b(i, 0), 1.0)] for i in range(7)]
-    threads = oracle.default_threads()
     done, total_bytes = 0, 0
     t0 = time.time()
-    while True:
-        for i, L in enumerate(wl.linears):
-            oracle.linear_dual(L.qtype, blocks[i], L.n_out, L.k_in, xs[i], ads[i],
-                               nthreads=threads)
-            total_bytes += linear_bytes(wl, i)
+    while time.time() - t0 < seconds or done == 0:
+        i = done % 7
+        L = wl.linears[i]
+        oracle.linear_dual(L.qtype, blocks[i], L.n_out, L.k_in, xs[i], ads[i], nthreads=threads)
+        total_bytes += linear_bytes(wl, i)
         done += 1
-        if time.time() - t0 >= seconds:
-            break
     el = time.time() - t0
-    return {"value": round(total_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} full passes over the block's 7 linears (float64, row-parallel), {el:.1f}s"}
+    return total_bytes / el / 1e9, done, el
+
+
+def cpu_baseline(oracle, workloads, wl, seconds):
+    """The oracle (float64, C) timed on the host cores, beside the GPU figures:
+    the headline leg (the block's linears, GB/s, all cores) and bounded samples of
+    the other workloads, each scaled to its line's unit.  Every input is the
+    oracle's own (its quantiser on the seeded weights)."""
+    import numpy as np
+    threads = oracle.default_threads()
+    blocks = [oracle.quantize(L.qtype, wl.weight(i)) for i, L in enumerate(wl.linears)]
+    gbs, done, el = cpu_block(oracle, wl, blocks, seconds, threads)
+    out = {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} linears of the block (whole linears in order, float64, row-parallel), {el:.1f}s",
+           "legs": {}}
+    legs = out["legs"]
+    short = max(1.0, seconds / 4)
+
+    # the same leg on one core (one thread; the process is pinned to one CPU
+    # where the platform allows it)
+    pinned = False
+    try:
+        keep = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(keep)})
+        pinned = True
+    except (AttributeError, OSError):
+        keep = None
+    try:
+        g1, d1, e1 = cpu_block(oracle, wl, blocks, short, 1)
+    finally:
+        if pinned:
+            os.sched_setaffinity(0, keep)
+    legs["block_single_core"] = {"value": round(g1, 3), "unit": "GB/s", "cores": 1, "pinned": pinned,
+                                 "sample": f"{d1} linears of the block, {e1:.1f}s"}
+
+    # the 32-block stack: the block's base (the stack's block shape) with the
+    # stack's two adapters (r16 @ 1.0, r64 @ 0.5), one token at a time, the
+    # oracle's block glue included; tokens/s = 1 / (32 x the block's time)
+    st = workloads.stack()
+    layers = []
+    for i in range(7):
+        L = st.linears[i]
+        ads = [oracle.Lora(st.lora_a(i, a), st.lora_b(i, a), spec.scale) for a, spec in enumerate(st.adapters)]
+        layers.append(oracle.Layer(L.qtype, blocks[i], L.n_out, L.k_in, ads))
+    h = st.x0()[0].astype(np.float64)
+    nblk, t0 = 0, time.time()
+    while time.time() - t0 < short or nblk == 0:
+        h = oracle.block(layers, h, nthreads=threads)
+        nblk += 1
+    el = time.time() - t0
+    per_tok = el / nblk * st.blocks
+    legs["stack"] = {"value": round(1.0 / per_tok, 4), "unit": "tokens/s", "cores": threads,
+                     "sample": f"{nblk} block-tokens of the stack's block shape and adapters in {el:.1f}s, "
+                               f"scaled by {st.blocks} blocks per token"}
+
+    # the 70B q4_sm MLP at batch 1: the first 1024 rows of gate (the shrink over
+    # all of A, the base and B rows of the sample); GB/s over those bytes
+    mlp = workloads.mlp70b()
+    L = mlp.linears[0]
+    rows = 1024
+    wq = oracle.quantize(L.qtype, mlp.weight_rows(0, 0, rows))
+    A, B = mlp.lora_a(0, 0), mlp.lora_b(0, 0)[:rows].copy()
+    x = mlp.x(0, 1).astype(np.float64)
+    ad = [oracle.Lora(A, B, mlp.adapters[0].scale)]
+    nb = (mlp.base_bytes(0) * rows) // L.n_out + 4 * A.size + 4 * B.size + 4 * (L.k_in + rows)
+    n4, t0 = 0, time.time()
+    while time.time() - t0 < short or n4 == 0:
+        oracle.linear_dual(L.qtype, wq, rows, L.k_in, x, ad, nthreads=threads)
+        n4 += 1
+    el = time.time() - t0
+    legs["q4_mlp_batch1"] = {"value": round(nb * n4 / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+                             "sample": f"{n4} passes over rows 0..{rows - 1} of the 28672x8192 q4_sm gate "
+                                       f"linear (r32 shrink over all of A), {el:.1f}s"}
+
+    # the prefill JIT recipe: 512 tokens against the first 256 rows of the
+    # 14336x4096 layer (W_eff rows materialised, then the bf16 GEMM); GFLOP/s
+    # counted as the GPU line counts them (2mnk + 2rnk)
+    pf = workloads.prefill()
+    L = pf.linears[0]
+    rows = 256
+    wq = oracle.quantize(L.qtype, pf.weight_rows(0, 0, rows))
+    ad = [oracle.Lora(pf.lora_a(0, 0), pf.lora_b(0, 0)[:rows].copy(), pf.adapters[0].scale)]
+    X = oracle.bf16_from_f32(pf.x_prefill_f32())
+    r = pf.adapters[0].rank
+    flop = 2 * pf.m_tokens * rows * L.k_in + 2 * r * rows * L.k_in
+    n5, t0 = 0, time.time()
+    while time.time() - t0 < short or n5 == 0:
+        oracle.linear_jit(L.qtype, wq, rows, L.k_in, X, ad, nthreads=threads)
+        n5 += 1
+    el = time.time() - t0
+    legs["prefill"] = {"value": round(flop * n5 / el / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+                       "sample": f"{n5} passes of {pf.m_tokens} tokens x rows 0..{rows - 1} of the 14336x4096 "
+                                 f"q8_0 layer (r64), {el:.1f}s"}
+    return out
+
+
+def bench_single(torch, q, workloads, oracle, args):
+    """The 256x256 q8_0 linear with its two rank-8 adapters at 2.0, batch 1:
+    microseconds per qbl_linear call (median of repeats), beside the oracle's
+    microseconds for the same call on one core."""
+    import numpy as np
+    wl = workloads.single()
+    L = wl.linears[0]
+    blocks = q.qbl_quantize(L.qtype, wl.weight(0))
+    base = q.qbl_base_load([(L.qtype, L.n_out, L.k_in, blocks)])
+    ads = [q.qbl_adapter_load(base, [(0, wl.lora_a(0, a), wl.lora_b(0, a))]) for a in range(2)]
+    comp = q.qbl_comp_create(base)
+    q.qbl_comp_attach(comp, ads, [a.scale for a in wl.adapters])
+    x = torch.from_numpy(wl.x(0, 1)).cuda()
+    y = torch.empty((1, L.n_out), dtype=torch.float32, device="cuda")
+    ws = q.workspace(comp, q.OP_LINEAR, 0, 1)
+    reps = [time_loop(torch, lambda i: q.qbl_linear(comp, 0, x, y, 1, ws), 200, 20) for _ in range(args.repeats)]
+    us = sorted(reps)[len(reps) // 2] * 1e3
+    free_all(q, base, ads, comp)
+    ob = oracle.quantize(L.qtype, wl.weight(0))
+    oads = [oracle.Lora(wl.lora_a(0, a), wl.lora_b(0, a), s.scale) for a, s in enumerate(wl.adapters)]
+    xo = wl.x(0, 1).astype(np.float64)
+    n, t0 = 0, time.time()
+    while time.time() - t0 < 0.5 or n < 10:
+        oracle.linear_dual(L.qtype, ob, L.n_out, L.k_in, xo, oads, nthreads=1)
+        n += 1
+    cpu_us = (time.time() - t0) / n * 1e6
+    log(f"[single] {us:.2f} us per call (oracle, one core: {cpu_us:.1f} us)")
+    return {"us_per_call": round(us, 2), "repeats_us": [round(r * 1e3, 2) for r in reps],
+            "bytes": wl.base_bytes(0) + wl.lora_bytes(0) + 4 * (L.n_out + L.k_in),
+            "cpu_oracle_us_one_core": round(cpu_us, 1)}
 
 
 def bench_stack(torch, q, workloads, args):
@@ -515,6 +663,7 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step (>= 600 MB)")
     ap.add_argument("--stack-tokens", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--repeats", type=int, default=5, help="timed repeats; the median is reported")
     ap.add_argument("--no-extras", action="store_true", help="skip the stack / q4 / prefill lines")
     ap.add_argument("--extras", default=",".join(EXTRAS),
                     help="comma-separated extra lines to run (default: all of " + ",".join(EXTRAS) + ")")
@@ -571,8 +720,9 @@ def main():
         if e in extras:
             result[e] = runs[e]()
     import oracle
+    result["single_linear"] = bench_single(torch, q, workloads, oracle, args)
     log("[cpu] timing the oracle")
-    result["cpu_baseline"] = cpu_baseline(oracle, wl, blocks, args.cpu_seconds)
+    result["cpu_baseline"] = cpu_baseline(oracle, workloads, wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
