@@ -19,6 +19,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <utility>
 
 #include "qbl_device.h"
 #include "qbl_kernels.h"
@@ -801,19 +802,53 @@ hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
   return hipGetLastError();
 }
 
+// The workgroup shapes (W waves, CPW chunks per lane) of the batch-1 kernel.
+// Up to one block of 64 chunks per lane, four waves suffice (K <= 4096 for
+// q8_0); longer rows take more waves before more chunks per lane, which keeps
+// more rows in flight per register.  Shapes whose registers would spill at
+// their wave count are left out (q4 formats hold twice the inputs per chunk).
+struct B1ShapeW { int w, cpw; };
+constexpr B1ShapeW kB1ShapesQ8[] = {{4, 1},  {6, 1},  {8, 1},  {11, 1}, {12, 1}, {14, 1},
+                                    {16, 1}, {12, 2}, {14, 2}, {16, 2}, {16, 3}};
+constexpr B1ShapeW kB1ShapesQ4[] = {{4, 1}, {6, 1}, {8, 1}, {11, 1}, {12, 1}, {14, 1}, {16, 1}, {12, 2}};
+constexpr int kB1MaxBlocksQ8 = 48, kB1MaxBlocksQ4 = 24;
+
+// For a row of `blocks` blocks of 64 chunks: the shape with the fewest chunk
+// slots (lanes past the row end do no useful work), then the fewest chunks per
+// lane; -1 if none holds the row.
+template <int N>
+constexpr int b1_pick(const B1ShapeW (&t)[N], int blocks) {
+  int best = -1;
+  for (int i = 0; i < N; ++i) {
+    if (t[i].w * t[i].cpw < blocks) continue;
+    if (best < 0 || t[i].w * t[i].cpw < t[best].w * t[best].cpw) best = i;
+  }
+  return best;
+}
+
+template <int QT, int I>
+hipError_t launch_b1_shape(FusedArgs& f, const LaunchCtx& lc) {
+  constexpr B1ShapeW sh = QT == QBL_FMT_Q8 ? kB1ShapesQ8[I] : kB1ShapesQ4[I];
+  return launch_b1_t<QT, sh.w, sh.cpw>(f, lc);
+}
+
+template <int QT, int... I>
+hipError_t launch_b1_index(FusedArgs& f, const LaunchCtx& lc, int i, std::integer_sequence<int, I...>) {
+  hipError_t e = hipErrorInvalidValue;
+  ((i == I ? (e = launch_b1_shape<QT, I>(f, lc), true) : false) || ...);
+  return e;
+}
+
 template <int QT>
 hipError_t launch_b1_q(FusedArgs& f, const LaunchCtx& lc) {
   const int blocks = (f.g.k / Fmt<QT>::kWeightsPerChunk + 63) / 64;
-  constexpr int kMaxCpw = QT == QBL_FMT_Q8 ? 4 : 2;  // input registers per lane: 64 floats
-  // up to one block of chunks per lane: 4 waves; past that, more waves beat
-  // more blocks per lane (fewer registers, more rows in flight)
-  if (blocks <= 4) return launch_b1_t<QT, 4, 1>(f, lc);
-  const int cpw = (blocks + 7) / 8;
-  if (cpw <= 1) return launch_b1_t<QT, 8, 1>(f, lc);
-  if (cpw <= 2) return launch_b1_t<QT, 8, 2>(f, lc);
-  if constexpr (kMaxCpw >= 3) if (cpw <= 3) return launch_b1_t<QT, 8, 3>(f, lc);
-  if constexpr (kMaxCpw >= 4) if (cpw <= 4) return launch_b1_t<QT, 8, 4>(f, lc);
-  return hipErrorInvalidValue;
+  if constexpr (QT == QBL_FMT_Q8) {
+    constexpr int n = sizeof(kB1ShapesQ8) / sizeof(kB1ShapesQ8[0]);
+    return launch_b1_index<QT>(f, lc, b1_pick(kB1ShapesQ8, blocks), std::make_integer_sequence<int, n>{});
+  } else {
+    constexpr int n = sizeof(kB1ShapesQ4) / sizeof(kB1ShapesQ4[0]);
+    return launch_b1_index<QT>(f, lc, b1_pick(kB1ShapesQ4, blocks), std::make_integer_sequence<int, n>{});
+  }
 }
 
 template <int QT, int BB, int CPL, int RPW>
@@ -935,8 +970,8 @@ hipError_t launch_rms(const float* v, int n, float* y, const LaunchCtx& lc) {
 
 bool fused_supported(int qtype, int k) {
   const int wpc = qtype == QBL_FMT_Q8 ? 16 : 32;
-  const int max_cpw = qtype == QBL_FMT_Q8 ? 4 : 2;
-  return k % (qtype == QBL_FMT_Q4K ? 256 : 32) == 0 && (k / wpc + 63) / 64 <= 8 * max_cpw;
+  const int max_blocks = qtype == QBL_FMT_Q8 ? kB1MaxBlocksQ8 : kB1MaxBlocksQ4;
+  return k % (qtype == QBL_FMT_Q4K ? 256 : 32) == 0 && (k / wpc + 63) / 64 <= max_blocks;
 }
 
 hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc) {

@@ -141,6 +141,36 @@ def test_ragged_shapes_and_batches(torch_cuda, qtype, n, k, batch):
         b.close()
 
 
+# One row length per workgroup shape of the batch-1 kernel (waves x chunks per
+# lane, chosen from the row's blocks of 64 chunks: 1024 weights for q8_0, 2048
+# for the q4 formats), each with a ragged last block of chunk slots.
+_B1_SHAPE_KS = ([(1, k) for k in (4096, 6016, 7168, 11008, 12288, 13312, 15360, 17408, 26624, 30720, 40960)] +
+                [(qt, k) for qt in (2, 3) for k in (8192, 11264, 14336, 22528, 24576, 28672, 30720, 34816)])
+
+
+@pytest.mark.parametrize("qtype,k", _B1_SHAPE_KS)
+def test_batch1_every_workgroup_shape(torch_cuda, qtype, k):
+    torch = torch_cuda
+    n = 70
+    wl = workloads.Workload(f"b1shape_{qtype}_{k}", [workloads.LinearSpec(f"b1shape/{qtype}/{k}", n, k, qtype)],
+                            [workloads.AdapterSpec("A1", 16, 1.0), workloads.AdapterSpec("A2", 8, -0.5)])
+    log(f"batch-1 shape: qtype={qtype} n={n} k={k}")
+    b = Built(wl)
+    try:
+        x = wl.x(0, 1)
+        b.attach([0, 1])
+        y = _run(b, torch, 0, x)
+        ref = oracle.linear_dual(qtype, b.or_blocks[0], n, k, x, b.oracle_ads(0, [0, 1]))
+        assert rel_l2(y, ref) <= TOL
+        b.q.qbl_comp_clear(b.comp)
+        y0 = _run(b, torch, 0, x)
+        ref0 = oracle.linear_dual(qtype, b.or_blocks[0], n, k, x)
+        assert rel_l2(y0, ref0) <= TOL
+        assert rel_l2(y - y0, ref - ref0) <= TOL
+    finally:
+        b.close()
+
+
 def test_batch1_mixed_ranks_tall_linear(torch_cuda):
     """Batch 1 with four adapters of ranks 16, 64, 6 and 36 on a tall linear
     (16384 rows: 13 or more rows per workgroup): ranks that are and are not
