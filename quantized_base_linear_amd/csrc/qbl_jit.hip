@@ -126,12 +126,17 @@ constexpr int kALD = 16 * JRMAX + 8;         // LDS pitch of a staged At row (bf
 constexpr int kAsElems = JBK * kALD;         // one K-step of At (rank <= 64)
 constexpr size_t kJitLds = 2 * (size_t)(kXsElems + kWsElems + kAsElems) * sizeof(uint16_t);
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two floats to bf16 (round to nearest even), lo in the low half: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int QT, int RS>
+// FULL: every tile lies inside the matrix (M a multiple of 256, K of 64): the
+// K-step body has no branches, one basic block that the scheduler interleaves.
+template <int QT, int RS, bool FULL>
 __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
   extern __shared__ __attribute__((aligned(16))) uint16_t jit_lds[];
   uint16_t* Xs0 = jit_lds;
@@ -163,40 +168,59 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
     for (int r = 0; r < RS; ++r) sbf[r] = ld_bf16x8(sB + (int64_t)nrow * tp + 16 * r + 8 * h);
   }
 
-  // Operands of a K-step in registers: two sets, so the loads of step k + 3 are
-  // issued while step k + 1 is built and step k + 2's are in flight (X and the
-  // quantised weights); At is loaded one step before it is staged in LDS.
+  // Operands of K-step s in registers (Ops(s)): the X tile and the quantised
+  // weights of step s, and the At rows of step s + 1.  Two sets: at K-step ks
+  // the set holding Ops(ks + 1) is consumed and reloaded with Ops(ks + 3) while
+  // Ops(ks + 2), issued one step earlier, is still in flight.  Every load is
+  // unconditional (clamped in-bounds addresses; what lies outside the matrix is
+  // zeroed or skipped where it is used), so the compiler's in-order wait counts
+  // keep the later set in flight.
   struct Ops {
-    uint4 xr[4];
-    uint4 qv;  // 16 consecutive weights of this lane's row: 16 bytes (q8_0) or 8 (q4_sm, q4_K)
     uint32_t scv;
     uint4 hd;  // q4_K: the super-block header of the lane's block
+    uint4 qv;  // 16 consecutive weights of this lane's row: 16 bytes (q8_0) or 8 (q4_sm, q4_K)
+    uint4 xr[4];
+    uint4 atr;
   };
   Ops opa, opb;
-  uint4 atr = make_uint4(0u, 0u, 0u, 0u);
   // At of a K-step: 64 rows of tp bf16, one 16-byte piece per thread
+  constexpr bool kAtRegs = RS > 0 && RS <= JRMAX;
   const int arow = tid / (tp > 0 ? tp / 8 : 1), apiece = tid % (tp > 0 ? tp / 8 : 1);
-  const bool aload = RS > 0 && RS <= JRMAX && tid < 8 * tp;
-  auto load_at = [&](int k0) {
-    if (aload) {
-      const int k = min(k0 + arow, K - 1);
-      atr = *reinterpret_cast<const uint4*>(At + (int64_t)k * tp + 8 * apiece);
+  const bool aload = kAtRegs && tid < 8 * tp;
+  auto load_at = [&](uint4& r, int k0) {
+    if constexpr (kAtRegs) {
+      const int k = aload ? min(k0 + arow, K - 1) : 0;
+      r = *reinterpret_cast<const uint4*>(At + (int64_t)k * tp + (aload ? 8 * apiece : 0));
     }
   };
   // At row k_local = 16 h' + v of a 32-row half goes to LDS row 8 (v / 4) + 4 h' + v % 4:
   // the LoRA MFMA's output row r then holds k_local = perm(r), and lane (col, h)
   // holds k_local = 16 h + v in dsum[v], 16 contiguous k, the same k its single
   // 16-byte load of quantised weights covers.
-  auto store_at = [&](int b) {
+  auto store_at = [&](const uint4& r, int b) {
     const int half = arow >> 5, kl = arow & 31, hh = kl >> 4, v = kl & 15;
     const int lrow = 32 * half + 8 * (v >> 2) + 4 * hh + (v & 3);
-    if (aload) *reinterpret_cast<uint4*>(As0 + b * kAsElems + lrow * kALD + 8 * apiece) = atr;
+    if (aload) *reinterpret_cast<uint4*>(As0 + b * kAsElems + lrow * kALD + 8 * apiece) = r;
   };
 
-  // Loads are unconditional (clamped in-bounds addresses; what lies outside the
-  // matrix is zeroed or skipped where it is used), so the loop has no branches
-  // around them.
-  auto prefetch = [&](Ops& o, int k0) {
+  // K offset of K-step st (steps past the end build tiles nobody reads)
+  auto koff = [&](int st) { return st * JBK; };
+
+  auto prefetch = [&](Ops& o, int st) {
+    const int k0 = koff(st);
+    const int kbase = min(k0 + 32 * kb, K - 32);
+    if (QT == QBL_FMT_Q8) {
+      o.scv = reinterpret_cast<const uint16_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+      o.qv = *reinterpret_cast<const uint4*>(a.qs + (int64_t)nrow * K + kbase + 16 * h);
+    } else {
+      if constexpr (QT == QBL_FMT_Q4K)
+        o.hd = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sc) +
+                                               ((int64_t)nrow * (K / 256) + kbase / 256) * 16);
+      else
+        o.scv = reinterpret_cast<const uint32_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+      const uint2 q2 = *reinterpret_cast<const uint2*>(a.qs + (int64_t)nrow * (K / 2) + (kbase + 16 * h) / 2);
+      o.qv = make_uint4(q2.x, q2.y, 0u, 0u);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int idx = tid + JTHREADS * c;
@@ -204,31 +228,16 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
       const int m = min(m0 + row, M - 1), kk = min(k0 + 8 * c16, K - 8);
       o.xr[c] = *reinterpret_cast<const uint4*>(a.X + (int64_t)m * K + kk);
     }
-    const int kbase = min(k0 + 32 * kb, K - 32);
-    if (QT == QBL_FMT_Q8) {
-      o.qv = *reinterpret_cast<const uint4*>(a.qs + (int64_t)nrow * K + kbase + 16 * h);
-      o.scv = reinterpret_cast<const uint16_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
-    } else {
-      const uint2 q2 = *reinterpret_cast<const uint2*>(a.qs + (int64_t)nrow * (K / 2) + (kbase + 16 * h) / 2);
-      o.qv = make_uint4(q2.x, q2.y, 0u, 0u);
-      if constexpr (QT == QBL_FMT_Q4K)
-        o.hd = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sc) +
-                                               ((int64_t)nrow * (K / 256) + kbase / 256) * 16);
-      else
-        o.scv = reinterpret_cast<const uint32_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
-    }
+    load_at(o.atr, koff(st + 1));
   };
 
-  // this wave's 32 x 32 block of W_eff for K-step at k0, and the X tile, into buffer b
-  auto build = [&](const Ops& o, int k0, int b) {
-    const uint4* xr = o.xr;
-    const uint32_t qw[4] = {o.qv.x, o.qv.y, o.qv.z, o.qv.w};
-    const uint32_t scv = o.scv;
-    uint16_t* wrow = Ws0 + b * kWsElems + (32 * nb + col) * JLD + 32 * kb + 16 * h;
+  // The low-rank sum of this wave's 32 x 32 block of W_eff at K-step k0, from
+  // the At rows staged in As[b]: lane (col, h) gets k = 16 h + v in dsum[v].
+  auto lora = [&](int k0, int b) {
     f32x16 dsum;
 #pragma unroll
     for (int v = 0; v < 16; ++v) dsum[v] = 0.0f;
-    if constexpr (RS > 0 && RS <= JRMAX) {
+    if constexpr (kAtRegs) {
       const uint16_t* arow_p = As0 + b * kAsElems + (32 * kb + col) * kALD + 8 * h;
 #pragma unroll
       for (int r = 0; r < RS; ++r)
@@ -242,9 +251,19 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
         dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, dsum, 0, 0, 0);
       }
     }
+    return dsum;
+  };
+
+  // this wave's 32 x 32 block of W_eff for K-step at k0 (low-rank sum dsum), and
+  // the X tile, into buffer b
+  auto build = [&](const Ops& o, int k0, int b, const f32x16& dsum) {
+    const uint4* xr = o.xr;
+    const uint32_t qw[4] = {o.qv.x, o.qv.y, o.qv.z, o.qv.w};
+    const uint32_t scv = o.scv;
+    uint16_t* wrow = Ws0 + b * kWsElems + (32 * nb + col) * JLD + 32 * kb + 16 * h;
     // a K block past the matrix contributes zeros (the wave's condition, uniform:
     // a scalar branch, no per-element selects)
-    if (k0 + 32 * kb < K) {
+    if (FULL || k0 + 32 * kb < K) {
       float d, mn;
       if constexpr (QT == QBL_FMT_Q4K) {  // the block is sub-block (k / 32) % 8 of its super-block
         float D, M;
@@ -284,7 +303,7 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
     // the X tile: stored as loaded when it lies inside the matrix (the workgroup's
     // condition, uniform), else with the parts outside zeroed
     uint16_t* xs = Xs0 + b * kXsElems;
-    if (m0 + JBM <= M && k0 + JBK <= K) {
+    if (FULL || (m0 + JBM <= M && k0 + JBK <= K)) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int idx = tid + JTHREADS * c;
@@ -310,22 +329,30 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   // At of steps 0 and 1 into LDS first; then step 0's tiles
-  load_at(0);
-  store_at(0);
-  load_at(JBK);
-  store_at(1);
+  {
+    uint4 r0 = make_uint4(0u, 0u, 0u, 0u), r1 = r0;
+    load_at(r0, koff(0));
+    load_at(r1, koff(1));
+    store_at(r0, 0);
+    store_at(r1, 1);
+  }
   __syncthreads();
   prefetch(opa, 0);
-  build(opa, 0, 0);
-  prefetch(opa, JBK);
-  prefetch(opb, 2 * JBK);
-  load_at(2 * JBK);
+  build(opa, koff(0), 0, lora(koff(0), 0));
+  // Ops(1) strictly before Ops(2): the loop's wait counts assume the older set
+  // was issued first (the barrier keeps the scheduler from swapping them)
+  prefetch(opa, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  prefetch(opb, 2);
   __syncthreads();
 
-  // One K-step: MFMAs on buffer cur; build step ks + 1 from `next`, then reload
-  // `next` with step ks + 3 (`after` holds step ks + 2 meanwhile).
+  // One K-step: the low-rank sum of the next W tile first (its MFMAs overlap the
+  // main ones), the MFMAs on buffer cur, then the next step's tiles from `next`
+  // (Ops(ks + 1)) into the other buffer, At(ks + 2) into As[cur], and `next`
+  // reloaded with Ops(ks + 3).
   auto step = [&](int ks, Ops& next) {
     const int cur = ks & 1;
+    const f32x16 dsum = lora(koff(ks + 1), cur ^ 1);  // At(ks + 1) in As[cur ^ 1]
     const uint16_t* xs = Xs0 + cur * kXsElems;
     const uint16_t* ws = Ws0 + cur * kWsElems;
 #pragma unroll
@@ -340,19 +367,30 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    // next K-step's tiles into the other buffer (unconditional, so the body is
-    // one block the scheduler can interleave with the MFMAs; past the end they
-    // build tiles nobody reads)
-    build(next, (ks + 1) * JBK, cur ^ 1);  // reads At(ks + 1) in As[cur ^ 1]
-    store_at(cur);                         // At(ks + 2): As[cur] was last read by build(ks)
-    prefetch(next, (ks + 3) * JBK);
-    load_at((ks + 3) * JBK);
+    // (unconditional, so the body is one block the scheduler can interleave with
+    // the MFMAs; past the end they build tiles nobody reads)
+    build(next, koff(ks + 1), cur ^ 1, dsum);
+    store_at(next.atr, cur);  // At(ks + 2): As[cur] was last read by the low-rank sum of step ks - 1
+    prefetch(next, ks + 3);
+    if constexpr (FULL) {
+      // one MFMA, then a few vector instructions: the dequantisation of the next
+      // tile runs while the matrix core works
+#pragma unroll
+      for (int i = 0; i < 16 + (RS <= JRMAX ? RS : 0); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    }
     __syncthreads();
   };
-  for (int ks = 0; ks < nk; ks += 2) {
+  // two steps per iteration with no exit between them (an exit there would merge
+  // into the loop head and shorten the compiler's wait counts); an odd last step after
+  int ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
     step(ks, opa);
-    if (ks + 1 < nk) step(ks + 1, opb);
+    step(ks + 1, opb);
   }
+  if (ks < nk) step(ks, opa);
 
   // ---- write Y (float32)
 #pragma unroll
@@ -371,16 +409,22 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
 
 int rank_pad(int t) { return t <= 0 ? 0 : t <= 16 * JRMAX ? (t + 15) / 16 * 16 : (t + 63) / 64 * 64; }
 
-template <int QT, int RS>
-hipError_t launch_rs(const JitArgs& a, int tp, const LaunchCtx& lc) {
+template <int QT, int RS, bool FULL>
+hipError_t launch_full(const JitArgs& a, int tp, const LaunchCtx& lc) {
   // (the two M-blocks of an N tile are 112 = 0 mod 8 workgroups apart for the
   // prefill shape, so they share an XCD and its L2 copy of the weight rows)
   const dim3 grid((a.n + JBN - 1) / JBN, (a.m + JBM - 1) / JBM);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&jit_kernel<QT, RS>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&jit_kernel<QT, RS, FULL>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kJitLds);
   if (e != hipSuccess) return e;
-  QBL_LAUNCH((jit_kernel<QT, RS>), grid, dim3(JTHREADS), kJitLds, lc, a, tp);
+  QBL_LAUNCH((jit_kernel<QT, RS, FULL>), grid, dim3(JTHREADS), kJitLds, lc, a, tp);
   return hipGetLastError();
+}
+
+template <int QT, int RS>
+hipError_t launch_rs(const JitArgs& a, int tp, const LaunchCtx& lc) {
+  if (a.m % JBM == 0 && a.k % JBK == 0) return launch_full<QT, RS, true>(a, tp, lc);
+  return launch_full<QT, RS, false>(a, tp, lc);
 }
 
 template <int QT>
