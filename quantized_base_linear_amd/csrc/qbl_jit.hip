@@ -353,6 +353,9 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
   auto step = [&](int ks, Ops& next) {
     const int cur = ks & 1;
     const f32x16 dsum = lora(koff(ks + 1), cur ^ 1);  // At(ks + 1) in As[cur ^ 1]
+    // the low-rank MFMAs go out first and alone: the build that uses their sum
+    // then comes after the main MFMAs, by which time the chain has finished
+    if constexpr (FULL) __builtin_amdgcn_sched_barrier(0);
     const uint16_t* xs = Xs0 + cur * kXsElems;
     const uint16_t* ws = Ws0 + cur * kWsElems;
 #pragma unroll
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
       // one MFMA, then a few vector instructions: the dequantisation of the next
       // tile runs while the matrix core works
 #pragma unroll
-      for (int i = 0; i < 16 + (RS <= JRMAX ? RS : 0); ++i) {
+      for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
@@ -407,6 +410,247 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same GEMM for full tiles with the waves split by role: 8 waves issue the
+// main MFMAs (64 x 64 outputs each, as above) and stage the X tile (loads two
+// steps ahead, stores: no arithmetic); 8 builder waves load the quantised
+// weights and the A-factor rows two steps ahead and build each W_eff tile
+// (a 32 x 32 block per wave, the low-rank sum on their own MFMAs).
+// Both roles meet at the one barrier per K-step of the double-buffered layout,
+// so the matrix cores of a SIMD keep working while its builder wave does the
+// vector work of the next step.
+// ---------------------------------------------------------------------------
+constexpr int JWS_MFMA = 8, JWS_BUILD = 8, JWS_THREADS = (JWS_MFMA + JWS_BUILD) * 64;
+
+template <int QT, int RS>
+__global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) {
+  static_assert(RS <= JRMAX, "ranks held in registers");
+  extern __shared__ __attribute__((aligned(16))) uint16_t jit_lds[];
+  uint16_t* Xs0 = jit_lds;
+  uint16_t* Ws0 = jit_lds + 2 * kXsElems;
+  uint16_t* As0 = Ws0 + 2 * kWsElems;
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int col = lane & 31, h = lane >> 5;
+  const int N = a.n, K = a.k;
+  const int n0 = blockIdx.x * JBN, m0 = blockIdx.y * JBM;
+  const int nblk = K / 32;
+  const int nk = K / JBK;  // K is a multiple of the K-step here
+
+  if (w < JWS_MFMA) {
+    // ---- MFMA role: 64 x 64 outputs at (wm, wn)
+    const int wm = w & 3, wn = w >> 2;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // X tile of K-step st: 256 rows x 64 bf16, 4 16-byte pieces per lane (plain
+    // arrays and macros: held in registers, two sets, as the builders' operands)
+    uint4 xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3;
+    // piece c of a lane: row (tid + 512 c) / 8, 16-byte column (tid + 512 c) % 8
+    const uint16_t* xg = a.X + (int64_t)(m0 + (tid >> 3)) * K + 8 * (tid & 7);
+    const int64_t xrow64 = (int64_t)64 * K;  // 512 pieces = 64 rows further
+    const int xl = (tid >> 3) * JLD + 8 * (tid & 7);
+#define QBL_XLOAD(R, ST)                                                                 \
+  do {                                                                                   \
+    const int k0_ = min((ST), nk - 1) * JBK; /* steps past the end reload the last one */ \
+    R##0 = *reinterpret_cast<const uint4*>(xg + k0_);                                    \
+    R##1 = *reinterpret_cast<const uint4*>(xg + xrow64 + k0_);                           \
+    R##2 = *reinterpret_cast<const uint4*>(xg + 2 * xrow64 + k0_);                       \
+    R##3 = *reinterpret_cast<const uint4*>(xg + 3 * xrow64 + k0_);                       \
+  } while (0)
+#define QBL_XSTORE(R, B)                                                  \
+  do {                                                                    \
+    uint16_t* xs_ = Xs0 + (B) * kXsElems + xl;                            \
+    *reinterpret_cast<uint4*>(xs_) = R##0;                                \
+    *reinterpret_cast<uint4*>(xs_ + 64 * JLD) = R##1;                     \
+    *reinterpret_cast<uint4*>(xs_ + 128 * JLD) = R##2;                    \
+    *reinterpret_cast<uint4*>(xs_ + 192 * JLD) = R##3;                    \
+  } while (0)
+#define QBL_MSTEP(KS, NEXT)                                                                              \
+  do {                                                                                                   \
+    const int cur = (KS) & 1;                                                                            \
+    const uint16_t* xs = Xs0 + cur * kXsElems;                                                           \
+    const uint16_t* ws = Ws0 + cur * kWsElems;                                                           \
+    _Pragma("unroll") for (int kk = 0; kk < JBK / 16; ++kk) {                                            \
+      bf16x8 af[2], bf[2];                                                                               \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i) af[i] =                                             \
+          ld_bf16x8(xs + (64 * wm + 32 * i + col) * JLD + 16 * kk + 8 * h);                              \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) bf[j] =                                             \
+          ld_bf16x8(ws + (64 * wn + 32 * j + col) * JLD + 16 * kk + 8 * h);                              \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int j = 0; j < 2; ++j)       \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);          \
+    }                                                                                                    \
+    QBL_XSTORE(NEXT, cur ^ 1); /* X(ks + 1) */                                                           \
+    QBL_XLOAD(NEXT, (KS) + 3);                                                                           \
+    __syncthreads();                                                                                     \
+  } while (0)
+    __syncthreads();  // the builders' At(0), At(1)
+    QBL_XLOAD(xa, 0);
+    QBL_XSTORE(xa, 0);
+    QBL_XLOAD(xa, 1);
+    __builtin_amdgcn_sched_barrier(0);  // X(1) strictly before X(2) (the loop's wait counts)
+    QBL_XLOAD(xb, 2);
+    __syncthreads();  // step 0's tiles
+    int ks = 0;
+    for (; ks + 1 < nk; ks += 2) {
+      QBL_MSTEP(ks, xa);
+      QBL_MSTEP(ks + 1, xb);
+    }
+    if (ks < nk) QBL_MSTEP(ks, xa);
+#undef QBL_MSTEP
+#undef QBL_XSTORE
+#undef QBL_XLOAD
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + 64 * wn + 32 * j + col;
+        if (n >= N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + 64 * wm + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
+          a.Y[(int64_t)m * N + n] = acc[i][j][v];
+        }
+      }
+    return;
+  }
+
+  // ---- builder role: wave bw builds the 32 x 32 block (kb, nb) = (bw & 1,
+  // bw >> 1) of each W tile, and with the other builders stages At
+  const int bw = w - JWS_MFMA, bt = tid - JWS_MFMA * 64;  // 0..7, 0..511
+  const int kb = bw & 1, nb = bw >> 1;
+  const int nrow = min(n0 + 32 * nb + col, N - 1);
+  const int64_t nat = (int64_t)K * tp;
+  const uint16_t* At = a.ws;
+  const uint16_t* sB = a.ws + ((nat * 2 + 255) / 256 * 256) / 2;
+  bf16x8 sbf[RS > 0 ? RS : 1];
+  if constexpr (RS > 0) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) sbf[r] = ld_bf16x8(sB + (int64_t)nrow * tp + 16 * r + 8 * h);
+  }
+  // Operands of K-step s (Ops(s)): the lane's 16-weight run and its scale, and
+  // its At piece of step s + 1; loaded two steps ahead as unconditional clamped
+  // loads (exact in-order wait counts).
+  struct Ops {
+    uint32_t scv;
+    uint4 hd;
+    uint4 qv;
+    uint4 atr;
+  };
+  Ops opa, opb;
+  const int apr = tp > 0 ? tp / 8 : 1;  // 16-byte pieces per At row
+  const bool aok = RS > 0 && bt < 8 * tp;
+  const int arow = aok ? bt / apr : 0, apc = aok ? bt % apr : 0;
+  auto load_at = [&](uint4& r, int k0) __attribute__((always_inline)) {
+    if constexpr (RS > 0) r = *reinterpret_cast<const uint4*>(At + (int64_t)min(k0 + arow, K - 1) * tp + 8 * apc);
+  };
+  // At row k_local = 16 h' + v of a 32-row half goes to LDS row 8 (v / 4) + 4 h' + v % 4
+  // (see jit_kernel): lane (col, h) then holds k_local = 16 h + v in dsum[v]
+  auto store_at = [&](const uint4& r, int b) __attribute__((always_inline)) {
+    if constexpr (RS > 0) {
+      const int half = arow >> 5, kl = arow & 31, hh = kl >> 4, v = kl & 15;
+      const int lrow = 32 * half + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (aok) *reinterpret_cast<uint4*>(As0 + b * kAsElems + lrow * kALD + 8 * apc) = r;
+    }
+  };
+  auto prefetch = [&](Ops& o, int st) __attribute__((always_inline)) {
+    const int k0 = min(st, nk - 1) * JBK;  // steps past the end reload the last one
+    const int kbase = k0 + 32 * kb;
+    if (QT == QBL_FMT_Q8) {
+      o.scv = reinterpret_cast<const uint16_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+      o.qv = *reinterpret_cast<const uint4*>(a.qs + (int64_t)nrow * K + kbase + 16 * h);
+    } else {
+      if constexpr (QT == QBL_FMT_Q4K)
+        o.hd = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sc) +
+                                               ((int64_t)nrow * (K / 256) + kbase / 256) * 16);
+      else
+        o.scv = reinterpret_cast<const uint32_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+      const uint2 q2 = *reinterpret_cast<const uint2*>(a.qs + (int64_t)nrow * (K / 2) + (kbase + 16 * h) / 2);
+      o.qv = make_uint4(q2.x, q2.y, 0u, 0u);
+    }
+    load_at(o.atr, min(st + 1, nk - 1) * JBK);
+  };
+  // block (kb, nb) of the W tile of K-step k0 into buffer b; the low-rank sum
+  // from the At rows in As[b]
+  auto build = [&](const Ops& o, int k0, int b) __attribute__((always_inline)) {
+    f32x16 dsum;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dsum[v] = 0.0f;
+    if constexpr (RS > 0) {
+      const uint16_t* arow_p = As0 + b * kAsElems + (32 * kb + col) * kALD + 8 * h;
+#pragma unroll
+      for (int r = 0; r < RS; ++r)
+        dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(arow_p + 16 * r), sbf[r], dsum, 0, 0, 0);
+    }
+    float d, mn;
+    if constexpr (QT == QBL_FMT_Q4K) {
+      float D, M;
+      q4k_step_offset(o.hd, ((k0 + 32 * kb) / 32) & 7, D, M);
+      d = D;
+      mn = -M;
+    } else {
+      d = h2f(o.scv);
+      mn = QT == QBL_FMT_Q8 ? -128.0f * d : h2f(o.scv >> 16);
+    }
+    const uint32_t qw[4] = {o.qv.x, o.qv.y, o.qv.z, o.qv.w};
+    uint32_t packed[8];
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      float wv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // as in jit_kernel: float32(dequant), plus the low-rank sum, one bf16 rounding
+        const int e = v + j;
+        float deq;
+        if (QT == QBL_FMT_Q8)
+          deq = d * (float)((qw[e >> 2] >> (8 * (e & 3))) & 0xFFu) + mn;
+        else
+          deq = fmaf(d, (float)((qw[e >> 3] >> (4 * (e & 7))) & 0xFu), mn);
+        wv[j] = RS > 0 ? deq + dsum[e] : deq;
+      }
+      packed[v >> 1] = pack_bf16(wv[0], wv[1]);
+    }
+    uint16_t* wrow = Ws0 + b * kWsElems + (32 * nb + col) * JLD + 32 * kb + 16 * h;
+    *reinterpret_cast<uint4*>(wrow) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *reinterpret_cast<uint4*>(wrow + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  };
+
+  {
+    uint4 r0 = make_uint4(0u, 0u, 0u, 0u), r1 = r0;
+    load_at(r0, 0);
+    load_at(r1, min(1, nk - 1) * JBK);
+    store_at(r0, 0);
+    store_at(r1, 1);
+  }
+  __syncthreads();
+  prefetch(opa, 0);
+  build(opa, 0, 0);
+  prefetch(opa, 1);
+  __builtin_amdgcn_sched_barrier(0);  // Ops(1) strictly before Ops(2) (the loop's wait counts)
+  prefetch(opb, 2);
+  __syncthreads();
+  // step ks: the next W tile (step ks + 1) from `next` into the other buffer,
+  // At(ks + 2) into As[cur], `next` reloaded with Ops(ks + 3); the MFMA waves
+  // work on step ks and stage X(ks + 1)
+  auto step = [&](int ks, Ops& next) __attribute__((always_inline)) {
+    const int cur = ks & 1;
+    build(next, (ks + 1) * JBK, cur ^ 1);
+    store_at(next.atr, cur);
+    prefetch(next, ks + 3);
+    __syncthreads();
+  };
+  int ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
+    step(ks, opa);
+    step(ks + 1, opb);
+  }
+  if (ks < nk) step(ks, opa);
+}
+
 int rank_pad(int t) { return t <= 0 ? 0 : t <= 16 * JRMAX ? (t + 15) / 16 * 16 : (t + 63) / 64 * 64; }
 
 template <int QT, int RS, bool FULL>
@@ -422,8 +666,21 @@ hipError_t launch_full(const JitArgs& a, int tp, const LaunchCtx& lc) {
 }
 
 template <int QT, int RS>
+hipError_t launch_ws(const JitArgs& a, int tp, const LaunchCtx& lc) {
+  const dim3 grid((a.n + JBN - 1) / JBN, a.m / JBM);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&jit_ws_kernel<QT, RS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kJitLds);
+  if (e != hipSuccess) return e;
+  QBL_LAUNCH((jit_ws_kernel<QT, RS>), grid, dim3(JWS_THREADS), kJitLds, lc, a, tp);
+  return hipGetLastError();
+}
+
+template <int QT, int RS>
 hipError_t launch_rs(const JitArgs& a, int tp, const LaunchCtx& lc) {
-  if (a.m % JBM == 0 && a.k % JBK == 0) return launch_full<QT, RS, true>(a, tp, lc);
+  if (a.m % JBM == 0 && a.k % JBK == 0) {
+    if constexpr (RS <= JRMAX) return launch_ws<QT, RS>(a, tp, lc);
+    return launch_full<QT, RS, true>(a, tp, lc);
+  }
   return launch_full<QT, RS, false>(a, tp, lc);
 }
 
