@@ -470,11 +470,22 @@ __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) 
     *reinterpret_cast<uint4*>(xs_ + 128 * JLD) = R##2;                    \
     *reinterpret_cast<uint4*>(xs_ + 192 * JLD) = R##3;                    \
   } while (0)
+// One K-step: per 16-K group, the group's four operand reads, two MFMAs, the
+// store of one X(ks + 1) piece and the reload of that piece's register with
+// X(ks + 3), two MFMAs (the LDS write and the load issue hide under the matrix
+// core instead of queueing before the barrier).
+#define QBL_XPIECE(NEXT, C, XSN, K3)                                                        \
+  do {                                                                                      \
+    *reinterpret_cast<uint4*>((XSN) + (C) * 64 * JLD) = NEXT##C;                            \
+    NEXT##C = *reinterpret_cast<const uint4*>(xg + (C) * xrow64 + (K3));                    \
+  } while (0)
 #define QBL_MSTEP(KS, NEXT)                                                                              \
   do {                                                                                                   \
     const int cur = (KS) & 1;                                                                            \
     const uint16_t* xs = Xs0 + cur * kXsElems;                                                           \
     const uint16_t* ws = Ws0 + cur * kWsElems;                                                           \
+    uint16_t* xsn = Xs0 + (cur ^ 1) * kXsElems + xl;                                                     \
+    const int k3 = min((KS) + 3, nk - 1) * JBK; /* steps past the end reload the last one */             \
     _Pragma("unroll") for (int kk = 0; kk < JBK / 16; ++kk) {                                            \
       bf16x8 af[2], bf[2];                                                                               \
       _Pragma("unroll") for (int i = 0; i < 2; ++i) af[i] =                                             \
@@ -483,9 +494,16 @@ __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) 
           ld_bf16x8(ws + (64 * wn + 32 * j + col) * JLD + 16 * kk + 8 * h);                              \
       _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int j = 0; j < 2; ++j)       \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);          \
+      if (kk == 0) QBL_XPIECE(NEXT, 0, xsn, k3);                                                         \
+      if (kk == 1) QBL_XPIECE(NEXT, 1, xsn, k3);                                                         \
+      if (kk == 2) QBL_XPIECE(NEXT, 2, xsn, k3);                                                         \
+      if (kk == 3) QBL_XPIECE(NEXT, 3, xsn, k3);                                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); /* LDS reads */                                 \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); /* MFMA */                                      \
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); /* LDS write */                                 \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* global load */                               \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); /* MFMA */                                      \
     }                                                                                                    \
-    QBL_XSTORE(NEXT, cur ^ 1); /* X(ks + 1) */                                                           \
-    QBL_XLOAD(NEXT, (KS) + 3);                                                                           \
     __syncthreads();                                                                                     \
   } while (0)
     __syncthreads();  // the builders' At(0), At(1)
@@ -502,6 +520,7 @@ __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) 
     }
     if (ks < nk) QBL_MSTEP(ks, xa);
 #undef QBL_MSTEP
+#undef QBL_XPIECE
 #undef QBL_XSTORE
 #undef QBL_XLOAD
 #pragma unroll
