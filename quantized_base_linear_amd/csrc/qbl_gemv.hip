@@ -373,14 +373,18 @@ hipError_t allow_dyn_lds(const void* fn, size_t bytes) {
 // same workgroups and written as one vector y0 = y_seg0 + y_seg1 (+ y_seg2): the
 // block's glue needs only the sum of parallel projections.
 //
-// Shrink.  Workgroups [0, shrink_wgs) compute t = c (A s), kRS rows of A each,
-// and store each value as one 64-bit word tagged with the launch's number.  The
-// dispatcher hands out workgroups in index order, so they are resident before
-// any GEMV workgroup, and they never wait.  GEMV workgroups read t only after
-// their row loop, waiting (bounded) until each word carries this launch's tag:
-// the data is its own flag, so the hand-off needs no counters, fences or cache
-// maintenance and nothing is reset afterwards.  A violated assumption shows as
-// wrong values, never as a hang.
+// Shrink.  t = c (A s), each value stored as one 64-bit word tagged with the
+// launch's number.  GEMV workgroup i < rows_total computes t[i] from the input
+// it holds anyway (one A row: its load rides with the first weight loads)
+// before its own rows; only when a launch has fewer GEMV workgroups than A rows
+// do separate workgroups [0, shrink_wgs) compute t, kRS rows of A each.
+// (Separate shrink workgroups land as an extra workgroup on a few compute units
+// and make those the last to finish: in the 7B block's q+k+v launch, 12 of
+// them, 64 KiB of A each, ended the launch ~2.6 us after the other units.)
+// The producers are dispatched first and never wait.  GEMV workgroups read t
+// only after their row loop, waiting (bounded) until each word carries this
+// launch's tag: the data is its own flag, so the hand-off needs no counters,
+// fences or cache maintenance and nothing is reset afterwards.
 // ---------------------------------------------------------------------------
 constexpr int kB1MaxSlots = 64;   // output rows (over all segments) per workgroup
 constexpr int kB1MaxT = kMaxSegs * 512;
@@ -390,6 +394,7 @@ struct B1Shape {
   static constexpr int kNS = Fmt<QT>::kSlots;
   static constexpr int kG = CPW >= 3 ? 1 : 2;                                   // rows per load group
   static constexpr int kRS = CPW * kNS >= 16 ? 1 : 16 / (CPW * kNS);           // A rows per shrink workgroup
+  static constexpr bool kShrinkInGemv = CPW == 1;                               // GEMV workgroups compute t
 };
 
 // waves per SIMD the register budget targets: 4 waves, one q8_0 block of chunks
@@ -408,6 +413,7 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   constexpr int LG = G == 8 ? 3 : G == 4 ? 2 : G == 2 ? 1 : 0;
   __shared__ float red[W][kB1MaxSlots][4];  // per wave, slot, 16-lane row
   __shared__ float ssred[W];
+  __shared__ float tred[W];
   __shared__ float tl[kB1MaxT];
   __shared__ float outl[kB1MaxSlots];
 
@@ -417,6 +423,10 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   const int64_t row_bytes = F::row_bytes(K);
   const bool shrinker = (int)blockIdx.x < f.shrink_wgs;
   const int wg = (int)blockIdx.x - f.shrink_wgs - f.sparse_wgs;
+  // GEMV workgroup wg < rows_total computes t[wg] (no shrink workgroups; shapes
+  // with one chunk per lane, where the A row's registers fit beside the first
+  // weight loads)
+  const bool trow = S::kShrinkInGemv && f.shrink_in_gemv && !shrinker && wg >= 0 && wg < f.rows_total;
 
   // ---- sparse workgroups [shrink_wgs, shrink_wgs + sparse_wgs): a wave per
   // (segment, sparse adapter, row) item, its lanes strided over the row's
@@ -554,6 +564,18 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
                             : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   } else {
+    if (trow) {
+      int e = 0, base = 0;
+      while (base + f.ent[e].rank <= wg) {
+        base += f.ent[e].rank;
+        ++e;
+      }
+      const float* Ar = f.ent[e].A + (int64_t)(wg - base) * K;
+#pragma unroll
+      for (int u = 0; u < CPW; ++u)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) av[0][u][j] = *reinterpret_cast<const float4*>(Ar + (int64_t)cidx[u] * WPC + 4 * j);
+    }
     if (ngroups > 0) load_group(qa, sa, 0);
     if (ngroups > 1) load_group(qb, sb, 1);
   }
@@ -614,6 +636,29 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
+  }
+  if (trow) {  // t[wg], as a shrink workgroup would (inputs past the row end are zero)
+    float p = 0.0f;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        p = fmaf(av[0][u][j].x, xr[u][j].x, p);
+        p = fmaf(av[0][u][j].y, xr[u][j].y, p);
+        p = fmaf(av[0][u][j].z, xr[u][j].z, p);
+        p = fmaf(av[0][u][j].w, xr[u][j].w, p);
+      }
+    p = wave_sum(p);
+    if (lane == 0) tred[wave] = p;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < W; ++i) s += tred[i];
+      const uint64_t word = ((uint64_t)f.tag << 32) | __float_as_uint(cscale * s);
+      for (int c = 0; c < kTCopies; ++c)
+        __hip_atomic_store(f.t + (int64_t)c * f.t_copy_stride + wg, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // ---- row loop: two groups in flight; each group's rows reduced together
@@ -764,8 +809,12 @@ template <int QT, int W, int CPW, int G = B1Shape<QT, CPW>::kG>
 hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
   using S = B1Shape<QT, CPW>;
   GemvArgs& a = f.g;
-  f.shrink_wgs = (f.rows_total + S::kRS - 1) / S::kRS;
+  // first as if the GEMV workgroups compute t (no shrink workgroups); the
+  // separate shrink workgroups only when there are fewer GEMV workgroups than A rows
+  f.shrink_wgs = 0;
+  f.shrink_in_gemv = S::kShrinkInGemv ? 1 : 0;
   const int resident = b1_resident_per_cu<QT, W, CPW, G>() * device_cus();
+  const int rows_in = f.rows_per_wg;
   // sparse workgroups: their share of the round is twice their share of the
   // launch's bytes (a gathering workgroup moves about half the bytes per unit
   // time of a streaming one; measured on the 10 %-dense 7B block), at least one,
@@ -780,22 +829,35 @@ hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
     sw = std::min(std::max(sw, 1), (f.sp_items + W - 1) / W);
     f.sparse_wgs = sw;
   }
-  if (f.rows_per_wg <= 0) {
+  auto pick_rows = [&] {
+    f.rows_per_wg = rows_in;
+    if (f.rows_per_wg > 0) return;
     // one round: as many GEMV workgroups as the chip holds next to the shrink and sparse ones
     const int units = f.sum ? a.seg[0].n : [&] { int u = 0; for (int i = 0; i < a.nseg; ++i) u += a.seg[i].n; return u; }();
     const int slots = resident - f.shrink_wgs - f.sparse_wgs;
     const int rmax = kB1MaxSlots / (f.sum ? a.nseg : 1);
     int r = slots > 0 ? (units + slots - 1) / slots : rmax;
     f.rows_per_wg = r < 1 ? 1 : (r > rmax ? rmax : r);
-  }
-  int wg = 0;
-  if (f.sum) {
-    wg = (a.seg[0].n + f.rows_per_wg - 1) / f.rows_per_wg;
-  } else {
-    for (int i = 0; i < a.nseg; ++i) {
-      a.seg[i].wg_begin = wg;
-      wg += (a.seg[i].n + f.rows_per_wg - 1) / f.rows_per_wg;
+  };
+  auto gemv_wgs = [&] {
+    int wg = 0;
+    if (f.sum) {
+      wg = (a.seg[0].n + f.rows_per_wg - 1) / f.rows_per_wg;
+    } else {
+      for (int i = 0; i < a.nseg; ++i) {
+        a.seg[i].wg_begin = wg;
+        wg += (a.seg[i].n + f.rows_per_wg - 1) / f.rows_per_wg;
+      }
     }
+    return wg;
+  };
+  pick_rows();
+  int wg = gemv_wgs();
+  if (!f.shrink_in_gemv || wg < f.rows_total) {
+    f.shrink_in_gemv = 0;
+    f.shrink_wgs = (f.rows_total + S::kRS - 1) / S::kRS;
+    pick_rows();
+    wg = gemv_wgs();
   }
   a.grid = f.shrink_wgs + f.sparse_wgs + wg;
   QBL_LAUNCH((gemv_b1_kernel<QT, W, CPW, G>), dim3(a.grid), dim3(W * 64), 0, lc, f);

@@ -90,11 +90,13 @@ struct PrepArgs {
   PrepEntry ent[kMaxPrepEntries];
 };
 
-// Batch-1 GEMV with the glue and the shrink in the same launch.  Workgroups
-// [0, shrink_wgs) compute t (kRS rows of A each) and store each value as one
-// 64-bit word tagged with the launch's number; the GEMV workgroups after them
-// read t only after their row loop, waiting (bounded) until each word carries
-// this launch's tag.  Input: s = v0 + v1 + v2, scaled by c (RMS or 1).
+// Batch-1 GEMV with the glue and the shrink in the same launch.  The first
+// GEMV workgroups compute one value of t each (or, when the launch has fewer
+// GEMV workgroups than A rows, workgroups [0, shrink_wgs) compute t, kRS rows
+// of A each) and store each value as one 64-bit word tagged with the launch's
+// number; every GEMV workgroup reads t only after its row loop, waiting
+// (bounded) until each word carries this launch's tag.  Input: s = v0 + v1 +
+// v2, scaled by c (RMS or 1).
 struct FusedArgs {
   GemvArgs g;          // segments (qs, sc, y, n, lora), nseg, qtype, k; wg_begin set by the launcher
   const float* v[3];
@@ -106,6 +108,7 @@ struct FusedArgs {
   int rows_total;      // A rows = shrink results
   int has_sparse;      // 1: some segment has a sparse delta
   int shrink_wgs;      // set by the launcher
+  int shrink_in_gemv;  // set by the launcher: 1 = no shrink workgroups; GEMV workgroup i < rows_total computes t[i]
   int sparse_wgs;      // set by the launcher (0 when sp_items == 0)
   int sp_items;        // sparse (segment, adapter, row) items: S x values handed to the GEMV workgroups
   int64_t sp_bytes;    // CSR bytes of the launch (for the launcher's split of the round)
