@@ -809,11 +809,16 @@ template <int QT, int W, int CPW, int G = B1Shape<QT, CPW>::kG>
 hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
   using S = B1Shape<QT, CPW>;
   GemvArgs& a = f.g;
-  // first as if the GEMV workgroups compute t (no shrink workgroups); the
-  // separate shrink workgroups only when there are fewer GEMV workgroups than A rows
+  // The GEMV workgroups compute t when several share a compute unit (a separate
+  // shrink workgroup would be an extra one on a unit with a full share of rows);
+  // with one workgroup per unit, separate shrink workgroups take units of their
+  // own and the rows spread over the others.  Separate ones also when there are
+  // fewer GEMV workgroups than A rows.
+  const int per_cu = b1_resident_per_cu<QT, W, CPW, G>();
   f.shrink_wgs = 0;
-  f.shrink_in_gemv = S::kShrinkInGemv ? 1 : 0;
-  const int resident = b1_resident_per_cu<QT, W, CPW, G>() * device_cus();
+  f.shrink_in_gemv = S::kShrinkInGemv && per_cu > 1 ? 1 : 0;
+  if (!f.shrink_in_gemv) f.shrink_wgs = (f.rows_total + S::kRS - 1) / S::kRS;
+  const int resident = per_cu * device_cus();
   const int rows_in = f.rows_per_wg;
   // sparse workgroups: their share of the round is twice their share of the
   // launch's bytes (a gathering workgroup moves about half the bytes per unit
@@ -853,7 +858,7 @@ hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
   };
   pick_rows();
   int wg = gemv_wgs();
-  if (!f.shrink_in_gemv || wg < f.rows_total) {
+  if (f.shrink_in_gemv && wg < f.rows_total) {
     f.shrink_in_gemv = 0;
     f.shrink_wgs = (f.rows_total + S::kRS - 1) / S::kRS;
     pick_rows();
