@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "qbl_device.h"
@@ -240,6 +241,10 @@ __global__ __launch_bounds__(256) void stage_kernel(const float* x, int64_t x_st
 // lo part.  With split-K each workgroup stores its partial sums and a second
 // launch adds the KS partial sums of each output in split order and finishes
 // the rows (the kernel boundary orders the two; no fence inside a launch).
+// Tall linears that need no split but leave some compute units one workgroup
+// more than others take the even spread instead: each unit gets the same
+// number of 16-row tiles (to one), in 2 to 4 tile workgroups, and the slab
+// loop is compiled per tile count, so a shorter workgroup issues less.
 // ---------------------------------------------------------------------------
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRowStride = 80;  // LDS bytes per slab row
@@ -274,7 +279,22 @@ struct MfmaSplit {
   int per;                 // blocks per split (a multiple of the slab)
   float* partial;          // ks > 1: [seg][ks][8][n] partial sums
   int64_t poff[kMaxSegs];  // segment offsets into partial (floats)
+  // bal_k > 0 (one segment, no split): the rows' 16-row tiles spread evenly over
+  // bal_c compute units, bal_k workgroups per unit (see tiles_of)
+  int bal_k, bal_c, bal_t;
 };
+
+// Rows of workgroup wg under the even spread: the dispatcher fills compute
+// units breadth first, so workgroups wg, wg + c, wg + 2c, ... share unit wg % c.
+// Unit u owns a contiguous run of t / c (+1 for the first t % c units) tiles,
+// split over its k workgroups the same way.  First tile and tile count.
+__device__ __forceinline__ void tiles_of(const MfmaSplit& sp, int wg, int& first, int& nt) {
+  const int c = sp.bal_c, u = wg % c, s = wg / c;
+  const int tu = sp.bal_t / c + (u < sp.bal_t % c ? 1 : 0);
+  const int u0 = u * (sp.bal_t / c) + min(u, sp.bal_t % c);
+  nt = tu / sp.bal_k + (s < tu % sp.bal_k ? 1 : 0);
+  first = u0 + s * (tu / sp.bal_k) + min(s, tu % sp.bal_k);
+}
 
 // Output (b, n) of segment g from its base sum s (before the 2^e_b scale):
 // scale, then the adapters in list order, then the store.
@@ -312,7 +332,17 @@ __global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_
   const GemvSeg& g = a.seg[si];
   const int local = wg - g.wg_begin;
   const int rg = local / sp.ks, ks = local % sp.ks;
-  const int row0 = rg * 64;
+  // 64 rows (4 tiles of 16) per workgroup, or fewer under the even spread
+  int row0 = rg * 64, nt = 4;
+  if (sp.bal_k > 0) {
+    int first;
+    tiles_of(sp, wg, first, nt);
+    row0 = 16 * first;
+  }
+  // loads of rows past the workgroup's tiles go past the buffer end: they
+  // return zero without a memory access (buffers and slab offsets stay below
+  // 2^31 bytes, so the sum stays below 2^32)
+  constexpr uint32_t kPastEnd = 0x80000000u;
   const int K = a.k, nblk = K / 32;
   const int kb0 = min(nblk, ks * sp.per), kb1 = min(nblk, kb0 + sp.per);
   const int nsl = (kb1 - kb0 + S - 1) / S;
@@ -340,19 +370,23 @@ __global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(xsum), 0, (int)(nb32 * 64u), kRsrcWord3);
   uint32_t w_off[4], s_off[F::kScLoads > 0 ? F::kScLoads : 1];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w_off[i] = (uint32_t)(row0 + 16 * i + (lane >> 2)) * (uint32_t)rbytes + 16u * (lane & 3);
+  for (int i = 0; i < 4; ++i)
+    w_off[i] = i < nt ? (uint32_t)(row0 + 16 * i + (lane >> 2)) * (uint32_t)rbytes + 16u * (lane & 3) : kPastEnd;
 #pragma unroll
   for (int i = 0; i < F::kScLoads; ++i) {
     const int e = 64 * i + lane, rl = e / S, j = e % S;
-    s_off[i] = ((uint32_t)(row0 + rl) * nb32 + (uint32_t)j) * (uint32_t)F::kScE;
+    s_off[i] = rl < 16 * nt ? ((uint32_t)(row0 + rl) * nb32 + (uint32_t)j) * (uint32_t)F::kScE : kPastEnd;
   }
-  const uint32_t h_off = (uint32_t)(row0 + lane) * (uint32_t)(K / 256) * 16u;
+  const uint32_t h_off = lane < 16 * nt ? (uint32_t)(row0 + lane) * (uint32_t)(K / 256) * 16u : kPastEnd;
   const uint32_t x_off = (uint32_t)((lane >> 2) & (S - 1)) * 64u + 16u * (lane & 3);
 
-  auto issue = [&](SlabRegs<QT>& r, int sl) {
+  // NT: the tiles the slab loop covers (a compile-time count, so that a
+  // workgroup with fewer tiles also issues fewer instructions)
+  auto issue = [&](SlabRegs<QT>& r, int sl, auto ntc) {
+    constexpr int NT = decltype(ntc)::value;
     const int b0 = kb0 + S * sl;  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NT; ++i)
       r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(qs_r, w_off[i], b0 * F::kBpb, 0);
     if constexpr (QT == QBL_FMT_Q4K) {
       r.hd = __builtin_amdgcn_raw_buffer_load_b128(sc_r, h_off, (b0 / 8) * 16, 0);
@@ -371,9 +405,10 @@ __global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_
       r.X = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xs_r, x_off, b0 * 64, 0));
   };
   // the loaded slab into this wave's LDS region
-  auto stash = [&](const SlabRegs<QT>& r) {
+  auto stash = [&](const SlabRegs<QT>& r, auto ntc) {
+    constexpr int NT = decltype(ntc)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NT; ++i)
       *reinterpret_cast<u32x4*>(W + (16 * i + (lane >> 2)) * kRowStride + 16 * (lane & 3)) = r.w[i];
     if constexpr (QT == QBL_FMT_Q4K) {
       *reinterpret_cast<u32x4*>(SC + lane * 16) = r.hd;
@@ -400,62 +435,69 @@ __global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_
   uint32_t k_lo = 0x000F000Fu, k_hi = 0x00F000F0u, k_magic = 0x64006400u;
   asm("" : "+v"(k_lo), "+v"(k_hi), "+v"(k_magic));
 
-  SlabRegs<QT> r;
-  if (wave < nsl) issue(r, wave);
-  for (int sl = wave; sl < nsl; sl += kWaves) {
-    stash(r);
-    u32x4 xf[S];
+  auto slabs = [&](auto ntc) {
+    constexpr int NT = decltype(ntc)::value;
+    SlabRegs<QT> r;
+    if (wave < nsl) issue(r, wave, ntc);
+    for (int sl = wave; sl < nsl; sl += kWaves) {
+      stash(r, ntc);
+      u32x4 xf[S];
 #pragma unroll
-    for (int j = 0; j < S; ++j) xf[j] = r.xf[j];
-    if (sl + kWaves < nsl) issue(r, sl + kWaves);
-    const int nb = min(S, kb1 - (kb0 + S * sl));
-    u32x4 hd[4];
-    if constexpr (QT == QBL_FMT_Q4K) {
+      for (int j = 0; j < S; ++j) xf[j] = r.xf[j];
+      if (sl + kWaves < nsl) issue(r, sl + kWaves, ntc);
+      const int nb = min(S, kb1 - (kb0 + S * sl));
+      u32x4 hd[NT];
+      if constexpr (QT == QBL_FMT_Q4K) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) hd[t] = *reinterpret_cast<const u32x4*>(SC + (16 * t + col) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      if (j >= nb) break;
-      const half8 xv = __builtin_bit_cast(half8, xf[j]);
-      f32x4 xs = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (QT != QBL_FMT_Q8) xs = *reinterpret_cast<const f32x4*>(XL + 64 * j + 16 * grp);
-      f32x4v o[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const unsigned char* wr = W + (16 * t + col) * kRowStride;
-        half8 wv;
-        if constexpr (QT == QBL_FMT_Q8) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(wr + 32 * j + 8 * grp);
-          wv = codes_q8(w.x, w.y);
-        } else {
-          wv = codes_q4(*reinterpret_cast<const uint32_t*>(wr + 16 * j + 4 * grp), k_lo, k_hi, k_magic);
-        }
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, zero, 0, 0, 0);
+        for (int t = 0; t < NT; ++t) hd[t] = *reinterpret_cast<const u32x4*>(SC + (16 * t + col) * 16);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if constexpr (QT == QBL_FMT_Q8) {
-          const float d = h2f(*reinterpret_cast<const uint16_t*>(SC + (16 * t + col) * F::kScStride + 2 * j));
+      for (int j = 0; j < S; ++j) {
+        if (j >= nb) break;
+        const half8 xv = __builtin_bit_cast(half8, xf[j]);
+        f32x4 xs = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (QT != QBL_FMT_Q8) xs = *reinterpret_cast<const f32x4*>(XL + 64 * j + 16 * grp);
+        f32x4v o[NT];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(d, o[t][q], acc[t][q]);
-        } else {
-          float d, m;
-          if constexpr (QT == QBL_FMT_Q4) {
-            const uint32_t dm = *reinterpret_cast<const uint32_t*>(SC + (16 * t + col) * F::kScStride + 4 * j);
-            d = h2f(dm);
-            m = h2f(dm >> 16);
+        for (int t = 0; t < NT; ++t) {
+          const unsigned char* wr = W + (16 * t + col) * kRowStride;
+          half8 wv;
+          if constexpr (QT == QBL_FMT_Q8) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(wr + 32 * j + 8 * grp);
+            wv = codes_q8(w.x, w.y);
           } else {
-            float M;
-            q4k_step_offset(make_uint4(hd[t].x, hd[t].y, hd[t].z, hd[t].w), (kb0 + S * sl + j) & 7, d, M);
-            m = -M;
+            wv = codes_q4(*reinterpret_cast<const uint32_t*>(wr + 16 * j + 4 * grp), k_lo, k_hi, k_magic);
           }
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, zero, 0, 0, 0);
+        }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(m, xs[q], fmaf(d, o[t][q], acc[t][q]));
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (QT == QBL_FMT_Q8) {
+            const float d = h2f(*reinterpret_cast<const uint16_t*>(SC + (16 * t + col) * F::kScStride + 2 * j));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(d, o[t][q], acc[t][q]);
+          } else {
+            float d, m;
+            if constexpr (QT == QBL_FMT_Q4) {
+              const uint32_t dm = *reinterpret_cast<const uint32_t*>(SC + (16 * t + col) * F::kScStride + 4 * j);
+              d = h2f(dm);
+              m = h2f(dm >> 16);
+            } else {
+              float M;
+              q4k_step_offset(make_uint4(hd[t].x, hd[t].y, hd[t].z, hd[t].w), (kb0 + S * sl + j) & 7, d, M);
+              m = -M;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(m, xs[q], fmaf(d, o[t][q], acc[t][q]));
+          }
         }
       }
     }
-  }
+  };
+  // nt is 4 without the even spread, 2 to 4 with it (rows past nt read as zero)
+  if (nt >= 4) slabs(std::integral_constant<int, 4>{});
+  else if (nt == 3) slabs(std::integral_constant<int, 3>{});
+  else slabs(std::integral_constant<int, 2>{});
 
   // the four waves' sums (the slab regions are reused: wait until every wave is done with them)
   __syncthreads();
@@ -481,7 +523,7 @@ __global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_
   if (sp.ks == 1) {  // thread -> (row rr, batch row b), b fastest: 8 lanes share a row of each B_i
     for (int idx = tid; idx < 64 * 8; idx += kMfmaThreads) {
       const int b = idx & 7, rr = idx >> 3, n = row0 + rr;
-      if (b < a.batch && n < g.n) finish_output(a, g, ex, b, n, wg_sum(b, rr));
+      if (b < a.batch && rr < 16 * nt && n < g.n) finish_output(a, g, ex, b, n, wg_sum(b, rr));
     }
     return;
   }
@@ -511,6 +553,19 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemvArgs a, MfmaSplit
 // Workgroups per 64 rows: none split when the rows alone give 1.5 workgroups
 // per compute unit (256 of them), else about as many workgroups as the chip
 // holds at once (4 per compute unit), each keeping at least 8 slabs.
+int cu_count() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (!n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 1;
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 int split_ks(int64_t row_groups, int nblk, int slab) {
   if (row_groups >= 384) return 1;
   const int64_t want = 1024 / row_groups;
@@ -568,6 +623,22 @@ hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, float*
     rows += a.seg[i].n;
   }
   if (sp.ks > 1 && po * 4 > mfma_partial_bytes(row_groups * 64)) return hipErrorInvalidValue;
+  // Even spread: with 64-row workgroups some compute units hold one more
+  // workgroup than others (the 70B gate/up: 448 workgroups on 256 units, 192 of
+  // them holding two and finishing ~1.7x later).  One segment without split: k
+  // workgroups per unit share the unit's ceil(tiles / units) tiles, taken
+  // where that lowers the most tiles any unit holds.
+  if (sp.ks == 1 && a.nseg == 1) {
+    const int c = cu_count(), t = (a.seg[0].n + 15) / 16;
+    const int most_even = (t + c - 1) / c, k = (most_even + 3) / 4;
+    const int most_now = 4 * ((wg + c - 1) / c);
+    if (k >= 2 && most_even < most_now) {
+      sp.bal_k = k;
+      sp.bal_c = c;
+      sp.bal_t = t;
+      wg = k * c;
+    }
+  }
   a.grid = wg;
   if (sp.ks == 1) {
     QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(kMfmaThreads), 0, lc, a, sp, frag, xsum, ex);

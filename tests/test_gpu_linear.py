@@ -108,7 +108,10 @@ def test_one_hot_and_block_indicator_are_exact(torch_cuda):
     (1, 1000, 4128, 1), (1, 333, 1056, 3), (1, 96, 12288, 1), (1, 130, 20480, 2),
     (2, 1000, 4160, 1), (2, 257, 1088, 8), (2, 64, 28672, 1), (2, 40, 9216, 5),
     (3, 1000, 4096, 1), (3, 257, 1280, 8), (3, 96, 28672, 1), (3, 130, 11008, 3), (3, 40, 9216, 5),
-    (3, 33, 256, 2)])
+    (3, 33, 256, 2),
+    # tall linears above batch 1: 16-row tiles spread evenly over the compute
+    # units, two or three workgroups per unit, ragged last tile
+    (1, 24600, 256, 8), (2, 40000, 512, 4), (3, 25000, 256, 7)])
 def test_ragged_shapes_and_batches(torch_cuda, qtype, n, k, batch):
     torch = torch_cuda
     wl = workloads.Workload(f"ragged_{qtype}_{n}_{k}_{batch}",
