@@ -38,8 +38,12 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kStageThreads = 256;
-constexpr int kWaves = 4;  // waves of a GEMV workgroup, splitting the blocks of K
-constexpr int kMfmaThreads = 64 * kWaves;
+// Waves of a GEMV workgroup, splitting the blocks of K: 8 for q4_sm (two
+// workgroups of 8 waves per compute unit ran the 70B MLP at batch 8 2.5 % faster
+// than 4 waves), 4 for q8_0 (the same either way) and q4_K (above 128 VGPRs it
+// holds one workgroup of 8 waves per unit and ran slower).
+template <int QT>
+constexpr int mfma_waves() { return QT == QBL_FMT_Q4 ? 8 : 4; }
 
 // Codes of one lane's 8 weights as exact f16 values, in the lane's input order.
 // Bits 0x64XX are the f16 value 1024 + XX.
@@ -229,8 +233,8 @@ __global__ __launch_bounds__(256) void stage_kernel(const float* x, int64_t x_st
 // ---------------------------------------------------------------------------
 // GEMV.  A workgroup owns 64 consecutive rows of one segment (4 tiles of 16)
 // and a range of the blocks of K (split-K over KS workgroups when the rows
-// alone give too few workgroups).  Its 4 waves take the range's slabs in turn
-// (wave w: slabs w, w + 4, ...); a slab is the next 64 bytes of all 64 rows
+// alone give too few workgroups).  Its W waves (mfma_waves) take the range's
+// slabs in turn (wave w: slabs w, w + W, ...); a slab is the next 64 bytes of all 64 rows
 // (2 q8_0 blocks or 4 q4 blocks).  A wave loads a slab with 16-byte loads that
 // run along the rows (a quarter-wave covers 64 contiguous bytes of each of four
 // rows), together with the slab's scales and the A operands of its blocks, one
@@ -320,10 +324,11 @@ __device__ __forceinline__ void finish_output(const GemvArgs& a, const GemvSeg& 
 }
 
 template <int QT>
-__global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_mfma_kernel(GemvArgs a, MfmaSplit sp, const u32x4* frag,
-                                                                 const float* xsum, const int* ex) {
+__global__ __launch_bounds__(64 * mfma_waves<QT>(), QT == QBL_FMT_Q4K ? 3 : 4) void gemv_mfma_kernel(
+    GemvArgs a, MfmaSplit sp, const u32x4* frag, const float* xsum, const int* ex) {
   using F = SlabFmt<QT>;
   constexpr int S = F::S;
+  constexpr int kWaves = mfma_waves<QT>(), kMfmaThreads = 64 * kWaves;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * F::kWave];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
@@ -499,7 +504,7 @@ __global__ __launch_bounds__(kMfmaThreads, QT == QBL_FMT_Q4K ? 3 : 4) void gemv_
   else if (nt == 3) slabs(std::integral_constant<int, 3>{});
   else slabs(std::integral_constant<int, 2>{});
 
-  // the four waves' sums (the slab regions are reused: wait until every wave is done with them)
+  // the waves' sums (the slab regions are reused: wait until every wave is done with them)
   __syncthreads();
   f32x4v* part = reinterpret_cast<f32x4v*>(lds);  // [wave][tile][lane]
 #pragma unroll
@@ -566,9 +571,9 @@ int cu_count() {
   return n;
 }
 
-int split_ks(int64_t row_groups, int nblk, int slab) {
+int split_ks(int64_t row_groups, int nblk, int slab, int waves) {
   if (row_groups >= 384) return 1;
-  const int64_t want = 1024 / row_groups;
+  const int64_t want = 4096 / waves / row_groups;
   const int64_t most = std::max<int64_t>(1, (nblk + slab - 1) / slab / 8);
   return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, 16}));
 }
@@ -609,7 +614,7 @@ hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, float*
   int64_t row_groups = 0;
   for (int i = 0; i < a.nseg; ++i) row_groups += (a.seg[i].n + 63) / 64;
   MfmaSplit sp{};
-  sp.ks = ks_force > 0 ? ks_force : split_ks(row_groups, nblk, S);
+  sp.ks = ks_force > 0 ? ks_force : split_ks(row_groups, nblk, S, mfma_waves<QT>());
   const int nslab = (nblk + S - 1) / S;
   sp.per = (nslab + sp.ks - 1) / sp.ks * S;
   sp.partial = reinterpret_cast<float*>(st + mfma_stage_only_bytes(a.k) + mfma_scan_bytes(a.k, T));
@@ -641,14 +646,14 @@ hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, float*
   }
   a.grid = wg;
   if (sp.ks == 1) {
-    QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(kMfmaThreads), 0, lc, a, sp, frag, xsum, ex);
+    QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(64 * mfma_waves<QT>()), 0, lc, a, sp, frag, xsum, ex);
     return hipGetLastError();
   }
   // the timing events of lc go around both launches
   LaunchCtx first = lc, second = lc;
   first.stop = nullptr;
   second.start = nullptr;
-  QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(kMfmaThreads), 0, first, a, sp, frag, xsum, ex);
+  QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(64 * mfma_waves<QT>()), 0, first, a, sp, frag, xsum, ex);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   QBL_LAUNCH(split_reduce_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, second, a, sp, ex);
