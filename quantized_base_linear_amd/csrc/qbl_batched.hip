@@ -3,9 +3,9 @@
 // The base product of the dual path for a few inputs ("Deep Technical Design",
 // section 8: the decode GEMV), y[b][n] = sum_k deq(W)[n][k] x[b][k], is a skinny
 // matrix product: every 32-weight block is one v_mfma_f32_16x16x32_f16 with the
-// block's integer codes (exact in f16) as the B operand (16 weight rows) and the
-// inputs as the A operand (16 rows).  The block's scale and minimum multiply the
-// float32 result, so no weight is ever rounded:
+// block's integer codes as the B operand (16 weight rows) and the inputs as the
+// A operand (16 rows).  The block's scale and minimum multiply float32 results,
+// so no weight is ever rounded:
 //   y[b][n] = 2^e_b sum_blk ( d[n][blk] S[b][n][blk] + m[n][blk] X[b][blk] ),
 //   S = sum over the block of code * x', X = sum over the block of x',
 // with x' = x 2^-e_b, e_b chosen per batch row so that its largest |x'| lies in
@@ -16,11 +16,25 @@
 // the two halves of the result are added at the end.  X is the float32 sum of
 // x' itself.  Low-rank and sparse terms follow in float32, in list order.
 //
+// Codes enter as exact f16 integers.  q8_0 codes are stored offset-binary
+// (u = q + 128): a byte permute puts u under the f16 exponent of 1024, and one
+// subtraction per pair leaves q.  q4 codes go through the gfx950 fp8 (e4m3)
+// conversion: a byte c < 16 is the e4m3 value c 2^-9 (subnormals and the first
+// binade share one spacing), so the conversion with scale 2^9 yields c exactly,
+// two codes per instruction.  (Codes as f16 subnormals, c 2^-24, would need no
+// conversion at all, but measured on the device each instruction's sum then
+// loses about 2^-20 relative, against 2^-26 with normal codes.)  Scales and
+// minima are converted to float32 once per slab (below), and for the q4
+// formats the minimum terms of a slab's blocks, sum_blk m[n][blk] X[b][blk],
+// are one v_mfma_f32_16x16x4_f32 per 16-row tile (X in A, m in B, float32).
+//
 // v_mfma_f32_16x16x32_f16 lanes (checked on the device): A lane l holds row
 // l % 16, inputs 8 (l / 16) .. +7; B lane l holds column l % 16, the same
 // inputs; D lane l holds rows 4 (l / 16) + j, j = 0..3, of column l % 16.  The
 // order of the 32 inputs inside one instruction is free as long as A and B
 // agree, which the q4 formats use to unpack nibbles with two masks (below).
+// v_mfma_f32_16x16x4_f32: A lane l holds A[l % 16][l / 16], B lane l holds
+// B[l / 16][l % 16], D as above (checked on the device).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -46,10 +60,10 @@ template <int QT>
 constexpr int mfma_waves() { return QT == QBL_FMT_Q4 ? 8 : 4; }
 
 // Codes of one lane's 8 weights as exact f16 values, in the lane's input order.
-// Bits 0x64XX are the f16 value 1024 + XX.
-//   q8_0: 8 offset-binary bytes u (= q + 128), in order: u - 128.  v_perm_b32
-//   picks bytes from {w (bytes 4..7), 0x64646464 (bytes 0..3)}: selector
-//   0x00050004 gives (w.b0, 0x64, w.b1, 0x64), 0x00070006 the upper two.
+//   q8_0: 8 offset-binary bytes u (= q + 128), in order.  Bits 0x64XX are the
+//   f16 value 1024 + XX.  v_perm_b32 picks bytes from {w (bytes 4..7),
+//   0x64646464 (bytes 0..3)}: selector 0x00050004 gives (w.b0, 0x64, w.b1,
+//   0x64), 0x00070006 the upper two; then u - 128 - 1024.
 __device__ __forceinline__ half8 codes_q8(uint32_t w0, uint32_t w1) {
   const uint32_t d0 = __builtin_amdgcn_perm(w0, 0x64646464u, 0x00050004u);
   const uint32_t d1 = __builtin_amdgcn_perm(w0, 0x64646464u, 0x00070006u);
@@ -58,26 +72,20 @@ __device__ __forceinline__ half8 codes_q8(uint32_t w0, uint32_t w1) {
   const half8 h = __builtin_bit_cast(half8, make_uint4(d0, d1, d2, d3));
   return h - (half8)(_Float16)1152.0f;
 }
-// (a & m) | o in one instruction; a VOP3 encoding takes no literal operand, so
-// the masks come in registers.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
 //   q4_sm / q4_K: one 32-bit word of nibbles, weights 0..7 of the lane's share
-//   (byte i: weight 2i in the low nibble, 2i+1 in the high one).  The high
-//   nibbles stay in place, so they read as 16 q; the matching inputs carry a
-//   factor 1/16 instead (exact).  Input order: w0, w4, w1, w5, w2, w6, w3, w7.
-//   lo, hi, magic: 0x000F000F, 0x00F000F0, 0x64006400 (kept in registers).
-__device__ __forceinline__ half8 codes_q4(uint32_t w, uint32_t lo, uint32_t hi, uint32_t magic) {
-  const uint32_t s = w >> 8;
-  const uint32_t d0 = and_or(w, lo, magic);
-  const uint32_t d1 = and_or(w, hi, magic);
-  const uint32_t d2 = and_or(s, lo, magic);
-  const uint32_t d3 = and_or(s, hi, magic);
-  const half8 h = __builtin_bit_cast(half8, make_uint4(d0, d1, d2, d3));
-  return h - (half8)(_Float16)1024.0f;
+//   (byte i: weight 2i in the low nibble, 2i+1 in the high one).  Low nibbles
+//   (weights 0, 2, 4, 6) and high nibbles (1, 3, 5, 7) each into the bytes of
+//   one word, then two e4m3 bytes per conversion.  Input order: w0, w2, w4,
+//   w6, w1, w3, w5, w7.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half8 codes_q4(uint32_t w) {
+  constexpr float kFp8Scale = 512.0f;  // 2^9
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const half2v c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, kFp8Scale, false);
+  const half2v c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, kFp8Scale, true);
+  const half2v c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, kFp8Scale, false);
+  const half2v c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, kFp8Scale, true);
+  return (half8){c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
 }
 
 // ---------------------------------------------------------------------------
@@ -154,8 +162,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 // Stage: workgroups [0, nblk / 32): thread (b = tid / 32, block 32 wg + tid % 32)
 // writes the A-operand values of the block in instruction order:
 //   frag[blk][l] for lane l = 16 g + r: row r < 8: hi of batch row r, r >= 8:
-//   lo of batch row r - 8, inputs 8 g .. 8 g + 7 of the block (permuted and
-//   scaled for the q4 formats as codes_q4 expects);
+//   lo of batch row r - 8, inputs 8 g .. 8 g + 7 of the block (permuted for
+//   the q4 formats as codes_q4 expects);
 //   xsum[blk][r] = X of batch row r for r < 8 (float32, input order), 0 for r >= 8;
 //   ex[b] = e_b, from the scan's partial maxima.
 // Rows b >= batch are zero.  The workgroups after those add the scan's partial
@@ -207,8 +215,8 @@ __global__ __launch_bounds__(256) void stage_kernel(const float* x, int64_t x_st
       o[i] = ldexpf(v[i], -e);
       s += o[i];
     }
-    if constexpr (QT != QBL_FMT_Q8) {  // input order of codes_q4, high-nibble inputs / 16
-      const float tt[8] = {o[0], o[4], o[1] * 0.0625f, o[5] * 0.0625f, o[2], o[6], o[3] * 0.0625f, o[7] * 0.0625f};
+    if constexpr (QT != QBL_FMT_Q8) {  // input order of codes_q4
+      const float tt[8] = {o[0], o[2], o[4], o[6], o[1], o[3], o[5], o[7]};
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = tt[i];
     }
@@ -259,12 +267,14 @@ struct SlabFmt {
   static constexpr int S = QT == QBL_FMT_Q8 ? 2 : 4;           // blocks per slab
   static constexpr int kBpb = QT == QBL_FMT_Q8 ? 32 : 16;      // weight bytes per block
   static constexpr int kScE = QT == QBL_FMT_Q8 ? 2 : 4;        // q8_0 d, q4_sm (d | m << 16)
-  static constexpr int kScStride = QT == QBL_FMT_Q8 ? 4 : QT == QBL_FMT_Q4 ? 20 : 16;
   static constexpr int kScLoads = QT == QBL_FMT_Q4K ? 0 : S;    // 64 S scale values / 64 lanes
-  static constexpr int kXBytes = QT == QBL_FMT_Q8 ? 0 : S * 64; // block sums X, [j][16] floats
+  // float32 scales and minima (q4) of the slab, [block j][row], rows of
+  // block j at 80 j: the stash's writes and the minimum operand's reads (lane
+  // -> block l / 16, row l % 16) both fall on 64 different banks
+  static constexpr int kDmStride = 80;
   static constexpr int kScOff = 64 * kRowStride;
-  static constexpr int kXOff = kScOff + 64 * kScStride;
-  static constexpr int kWave = kXOff + kXBytes;                 // LDS bytes per wave
+  static constexpr int kMOff = kScOff + S * kDmStride * 4;
+  static constexpr int kWave = kMOff + (QT == QBL_FMT_Q8 ? 0 : S * kDmStride * 4);  // LDS bytes per wave
 };
 
 // What a wave loads for one slab.
@@ -275,7 +285,7 @@ struct SlabRegs {
   uint32_t sc[F::kScLoads > 0 ? F::kScLoads : 1];
   u32x4 hd;                // q4_K: the row's super-block header (lane = row)
   u32x4 xf[F::S];
-  f32x4 X;                 // q4: lanes 0..31, X of block lane / 4, batch rows 4 (lane % 4) ..
+  float xa = 0.0f;         // q4: X of block l / 16 of the slab, batch row l % 16 (the minimum operand)
 };
 
 struct MfmaSplit {
@@ -354,8 +364,8 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), QT == QBL_FMT_Q4K ? 3 : 4) v
   const int64_t rbytes = Fmt<QT>::row_bytes(K);
 
   unsigned char* W = lds + wave * F::kWave;
-  unsigned char* SC = W + F::kScOff;
-  unsigned char* XL = W + F::kXOff;
+  float* DL = reinterpret_cast<float*>(W + F::kScOff);
+  float* ML = reinterpret_cast<float*>(W + F::kMOff);
 
   // Slab loads are buffer loads: a per-lane byte offset fixed for the whole
   // loop plus the slab's offset (wave-uniform).  Reads past the end of a
@@ -383,7 +393,6 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), QT == QBL_FMT_Q4K ? 3 : 4) v
     s_off[i] = rl < 16 * nt ? ((uint32_t)(row0 + rl) * nb32 + (uint32_t)j) * (uint32_t)F::kScE : kPastEnd;
   }
   const uint32_t h_off = lane < 16 * nt ? (uint32_t)(row0 + lane) * (uint32_t)(K / 256) * 16u : kPastEnd;
-  const uint32_t x_off = (uint32_t)((lane >> 2) & (S - 1)) * 64u + 16u * (lane & 3);
 
   // NT: the tiles the slab loop covers (a compile-time count, so that a
   // workgroup with fewer tiles also issues fewer instructions)
@@ -407,61 +416,54 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), QT == QBL_FMT_Q4K ? 3 : 4) v
 #pragma unroll
     for (int j = 0; j < S; ++j) r.xf[j] = __builtin_amdgcn_raw_buffer_load_b128(fr_r, 16u * lane, (b0 + j) * 1024, 0);
     if constexpr (QT != QBL_FMT_Q8)
-      r.X = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xs_r, x_off, b0 * 64, 0));
+      r.xa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_r, 4u * lane, b0 * 64, 0));
   };
-  // the loaded slab into this wave's LDS region
-  auto stash = [&](const SlabRegs<QT>& r, auto ntc) {
+  // the loaded slab into this wave's LDS region; scales and minima as float32
+  auto stash = [&](const SlabRegs<QT>& r, int sl, auto ntc) {
     constexpr int NT = decltype(ntc)::value;
 #pragma unroll
     for (int i = 0; i < NT; ++i)
       *reinterpret_cast<u32x4*>(W + (16 * i + (lane >> 2)) * kRowStride + 16 * (lane & 3)) = r.w[i];
-    if constexpr (QT == QBL_FMT_Q4K) {
-      *reinterpret_cast<u32x4*>(SC + lane * 16) = r.hd;
+    if constexpr (QT == QBL_FMT_Q4K) {  // lane = row: step and offset of the slab's sub-blocks
+      const uint4 h = make_uint4(r.hd.x, r.hd.y, r.hd.z, r.hd.w);
+#pragma unroll
+      for (int j = 0; j < S; ++j) {
+        float D, M;
+        q4k_step_offset(h, (kb0 + S * sl + j) & 7, D, M);
+        DL[j * F::kDmStride + lane] = D;
+        ML[j * F::kDmStride + lane] = -M;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < F::kScLoads; ++i) {
         const int e = 64 * i + lane, rl = e / S, j = e % S;
-        if constexpr (QT == QBL_FMT_Q8)
-          *reinterpret_cast<uint16_t*>(SC + rl * F::kScStride + 2 * j) = (uint16_t)r.sc[i];
-        else
-          *reinterpret_cast<uint32_t*>(SC + rl * F::kScStride + 4 * j) = r.sc[i];
+        DL[j * F::kDmStride + rl] = h2f(r.sc[i]);
+        if constexpr (QT != QBL_FMT_Q8) ML[j * F::kDmStride + rl] = h2f(r.sc[i] >> 16);
       }
     }
-    if constexpr (QT != QBL_FMT_Q8)
-      if (lane < 4 * S) *reinterpret_cast<f32x4*>(XL + 16 * lane) = r.X;
   };
 
   f32x4v acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = (f32x4v){0.0f, 0.0f, 0.0f, 0.0f};
   const f32x4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  // nibble masks for codes_q4, in registers (opaque to the optimiser so that
-  // they stay there instead of being folded back into literal operands)
-  uint32_t k_lo = 0x000F000Fu, k_hi = 0x00F000F0u, k_magic = 0x64006400u;
-  asm("" : "+v"(k_lo), "+v"(k_hi), "+v"(k_magic));
 
   auto slabs = [&](auto ntc) {
     constexpr int NT = decltype(ntc)::value;
     SlabRegs<QT> r;
     if (wave < nsl) issue(r, wave, ntc);
     for (int sl = wave; sl < nsl; sl += kWaves) {
-      stash(r, ntc);
+      stash(r, sl, ntc);
       u32x4 xf[S];
 #pragma unroll
       for (int j = 0; j < S; ++j) xf[j] = r.xf[j];
+      const float xa = r.xa;
       if (sl + kWaves < nsl) issue(r, sl + kWaves, ntc);
       const int nb = min(S, kb1 - (kb0 + S * sl));
-      u32x4 hd[NT];
-      if constexpr (QT == QBL_FMT_Q4K) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) hd[t] = *reinterpret_cast<const u32x4*>(SC + (16 * t + col) * 16);
-      }
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         if (j >= nb) break;
         const half8 xv = __builtin_bit_cast(half8, xf[j]);
-        f32x4 xs = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (QT != QBL_FMT_Q8) xs = *reinterpret_cast<const f32x4*>(XL + 64 * j + 16 * grp);
         f32x4v o[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -471,31 +473,23 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), QT == QBL_FMT_Q4K ? 3 : 4) v
             const u32x2 w = *reinterpret_cast<const u32x2*>(wr + 32 * j + 8 * grp);
             wv = codes_q8(w.x, w.y);
           } else {
-            wv = codes_q4(*reinterpret_cast<const uint32_t*>(wr + 16 * j + 4 * grp), k_lo, k_hi, k_magic);
+            wv = codes_q4(*reinterpret_cast<const uint32_t*>(wr + 16 * j + 4 * grp));
           }
           o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, wv, zero, 0, 0, 0);
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          if constexpr (QT == QBL_FMT_Q8) {
-            const float d = h2f(*reinterpret_cast<const uint16_t*>(SC + (16 * t + col) * F::kScStride + 2 * j));
+          const float d = DL[j * F::kDmStride + 16 * t + col];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(d, o[t][q], acc[t][q]);
-          } else {
-            float d, m;
-            if constexpr (QT == QBL_FMT_Q4) {
-              const uint32_t dm = *reinterpret_cast<const uint32_t*>(SC + (16 * t + col) * F::kScStride + 4 * j);
-              d = h2f(dm);
-              m = h2f(dm >> 16);
-            } else {
-              float M;
-              q4k_step_offset(make_uint4(hd[t].x, hd[t].y, hd[t].z, hd[t].w), (kb0 + S * sl + j) & 7, d, M);
-              m = -M;
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(m, xs[q], fmaf(d, o[t][q], acc[t][q]));
-          }
+          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(d, o[t][q], acc[t][q]);
         }
+      }
+      // the slab's minimum terms (q4): block grp of the slab (none past nb), row col
+      if constexpr (QT != QBL_FMT_Q8)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float m = grp < nb ? ML[(grp & (S - 1)) * F::kDmStride + 16 * t + col] : 0.0f;
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, m, acc[t], 0, 0, 0);
       }
     }
   };
