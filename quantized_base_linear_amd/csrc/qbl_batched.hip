@@ -52,12 +52,11 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kStageThreads = 256;
-// Waves of a GEMV workgroup, splitting the blocks of K: 8 for q4_sm (two
-// workgroups of 8 waves per compute unit ran the 70B MLP at batch 8 2.5 % faster
-// than 4 waves), 4 for q8_0 (the same either way) and q4_K (above 128 VGPRs it
-// holds one workgroup of 8 waves per unit and ran slower).
+// Waves of a GEMV workgroup, splitting the blocks of K: 8 for the q4 formats
+// (two workgroups of 8 waves per compute unit ran the 70B MLP at batch 8 2.5 %
+// (q4_sm) and 3 % (q4_K) faster than 4 waves), 4 for q8_0 (the same either way).
 template <int QT>
-constexpr int mfma_waves() { return QT == QBL_FMT_Q4 ? 8 : 4; }
+constexpr int mfma_waves() { return QT == QBL_FMT_Q8 ? 4 : 8; }
 
 // Codes of one lane's 8 weights as exact f16 values, in the lane's input order.
 //   q8_0: 8 offset-binary bytes u (= q + 128), in order.  Bits 0x64XX are the
@@ -334,7 +333,7 @@ __device__ __forceinline__ void finish_output(const GemvArgs& a, const GemvSeg& 
 }
 
 template <int QT>
-__global__ __launch_bounds__(64 * mfma_waves<QT>(), QT == QBL_FMT_Q4K ? 3 : 4) void gemv_mfma_kernel(
+__global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
     GemvArgs a, MfmaSplit sp, const u32x4* frag, const float* xsum, const int* ex) {
   using F = SlabFmt<QT>;
   constexpr int S = F::S;
