@@ -20,13 +20,20 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I" + os.path.join(ROOT, "include")]
 
 
+# Per-source flags.  qbl_gemv.hip: leading scalar kernel arguments arrive
+# preloaded in registers at wave launch (the batch-1 kernel's first loads then
+# wait for no argument fetch); firmware without preloading runs the compiler's
+# fallback prologue, which loads them.
+EXTRA = {"qbl_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"]}
+
+
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
 
     def compile_one(src):
         obj = os.path.join(objdir, src + ".o")
-        cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -109,11 +109,11 @@ struct Fmt {
   // scale data of chunk c (global chunk index along k) of a row
   __device__ static __forceinline__ Sc load_sc(const void* sc, int row, int k, int c) {
     if constexpr (QT == QBL_FMT_Q8)
-      return reinterpret_cast<const uint16_t*>(sc)[(int64_t)row * (k / 32) + (c >> 1)];
+      return *gp(reinterpret_cast<const uint16_t*>(sc) + (int64_t)row * (k / 32) + (c >> 1));
     else if constexpr (QT == QBL_FMT_Q4)
-      return reinterpret_cast<const uint32_t*>(sc)[(int64_t)row * (k / 32) + c];
+      return *gp(reinterpret_cast<const uint32_t*>(sc) + (int64_t)row * (k / 32) + c);
     else  // dword (c & 3) of the super-block header; the quad's 4 lanes hold all four
-      return reinterpret_cast<const uint32_t*>(sc)[((int64_t)row * (k / 256) + (c >> 3)) * 4 + (c & 3)];
+      return *gp(reinterpret_cast<const uint32_t*>(sc) + ((int64_t)row * (k / 256) + (c >> 3)) * 4 + (c & 3));
   }
 };
 

@@ -367,7 +367,8 @@ hipError_t allow_dyn_lds(const void* fn, size_t bytes) {
 // current one is consumed; a row's partial sums are reduced within each wave,
 // then across the W waves in LDS, in a fixed order.
 //
-// Glue.  The input is s = v0 + v1 + v2 (left to right), scaled by the RMS factor
+// Glue.  The input is one vector s (the launcher sends inputs that are sums of
+// several vectors to the prep + GEMV path), scaled by the RMS factor
 // c = 1/sqrt(mean(s^2) + 1e-6) when rms is set; c multiplies the finished dot
 // products.  With `sum` set, the segments (same height) are computed by the
 // same workgroups and written as one vector y0 = y_seg0 + y_seg1 (+ y_seg2): the
@@ -402,8 +403,33 @@ struct B1Shape {
 template <int QT, int W, int CPW>
 constexpr int b1_min_waves() { return W == 4 && CPW * Fmt<QT>::kSlots <= 4 ? 5 : 1; }
 
+// v0, v1 or v2 by a wave-uniform index i < 3, as two conditional moves (a
+// three-way ?: chain may be compiled into a table in scratch memory)
+template <class T>
+__device__ __forceinline__ T pick3(int i, T v0, T v1, T v2) {
+  T r = v0;
+  asm volatile("" : "+s"(r));
+  r = i >= 1 ? v1 : r;
+  asm volatile("" : "+s"(r));
+  return i >= 2 ? v2 : r;
+}
+
+// Flags word of the batch-1 launch's leading scalar arguments.
+__host__ __device__ constexpr int b1_flags(int sum, int nseg, int shrink_in_gemv, int shrink_wgs) {
+  return sum | nseg << 3 | shrink_in_gemv << 5 | shrink_wgs << 8;
+}
+
+// The first scalar arguments (segment 0's weights and scales, the input, the
+// row length, the first GEMV workgroup, rows per workgroup, segment 0's height,
+// the flags word, the number of shrink values) repeat fields of f.  The
+// library is compiled to preload leading scalar arguments into registers at
+// wave launch, so the first weight and input loads wait for no argument
+// fetch; everything else is read from f, and only behind uniform branches that
+// the first loads do not take.
 template <int QT, int W, int CPW, int G>
-__global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_kernel(FusedArgs f) {
+__global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_kernel(
+    const uint8_t* p_qs0, const void* p_sc0, const float* p_v0, int p_k, int p_first, int p_rows, int p_n0,
+    int p_flags, int p_rt, FusedArgs f) {
   using F = Fmt<QT>;
   using S = B1Shape<QT, CPW>;
   constexpr int WPC = F::kWeightsPerChunk;
@@ -419,18 +445,20 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
 
   const GemvArgs& a = f.g;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int K = a.k, CT = K / WPC;
+  const int h_sum = p_flags & 1, h_nseg = (p_flags >> 3) & 3, h_sig = (p_flags >> 5) & 1;
+  const int h_shrink = p_flags >> 8, h_sparse = p_first - h_shrink, h_rt = p_rt, h_R = p_rows, h_K = p_k;
+  const int K = h_K, CT = K / WPC;
   const int64_t row_bytes = F::row_bytes(K);
-  const bool shrinker = (int)blockIdx.x < f.shrink_wgs;
-  const int wg = (int)blockIdx.x - f.shrink_wgs - f.sparse_wgs;
+  const bool shrinker = (int)blockIdx.x < h_shrink;
+  const int wg = (int)blockIdx.x - h_shrink - h_sparse;
   // GEMV workgroup wg < rows_total computes t[wg] (no shrink workgroups; shapes
   // with one chunk per lane, where the A row's registers fit beside the first
   // weight loads)
-  const bool trow = S::kShrinkInGemv && f.shrink_in_gemv && !shrinker && wg >= 0 && wg < f.rows_total;
+  const bool trow = S::kShrinkInGemv && h_sig && !shrinker && wg >= 0 && wg < h_rt;
 
   // ---- sparse workgroups [shrink_wgs, shrink_wgs + sparse_wgs): a wave per
   // (segment, sparse adapter, row) item, its lanes strided over the row's
-  // entries, gathering the unscaled input s = v0 + v1 + v2 (the RMS factor is
+  // entries, gathering the unscaled input s (the RMS factor is
   // applied by the row's GEMV workgroup); one wave reduction per item, stored
   // as a tagged word like the shrink values.  They precede every GEMV
   // workgroup in dispatch order and never wait.
@@ -460,12 +488,7 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
         }
       }
       float p[kSpR];
-      csr_rows_dot<kSpR, 4>(col, val, e0, e1, lane, [&](uint32_t c) {
-        float xv = *gp(f.v[0] + c);
-        if (f.nv > 1) xv += *gp(f.v[1] + c);
-        if (f.nv > 2) xv += *gp(f.v[2] + c);
-        return xv;
-      }, p);
+      csr_rows_dot<kSpR, 4>(col, val, e0, e1, lane, [&](uint32_t c) { return *gp(p_v0 + c); }, p);
 #pragma unroll
       for (int r = 0; r < kSpR; ++r) {
         const float w = wave_sum(p[r]);
@@ -491,19 +514,24 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   }
 
   // ---- the workgroup's rows (GEMV role)
-  int sg0 = 0, row0 = 0, nslots = 0, R = f.rows_per_wg;
+  int sg0 = 0, row0 = 0, nslots = 0, R = h_R;
   if (!shrinker) {
-    if (f.sum) {
+    if (h_sum) {
       row0 = wg * R;
-      nslots = R * a.nseg;
+      nslots = R * h_nseg;
     } else {
-      sg0 = (a.nseg > 2 && wg >= a.seg[2].wg_begin) ? 2 : (a.nseg > 1 && wg >= a.seg[1].wg_begin) ? 1 : 0;
-      row0 = (wg - a.seg[sg0].wg_begin) * R;
+      row0 = wg * R;
       nslots = R;
+      if (h_nseg > 1) {  // several segments side by side: which one holds wg
+        asm volatile("");
+        const int wgb1 = a.seg[1].wg_begin, wgb2 = a.seg[2].wg_begin;
+        sg0 = (h_nseg > 2 && wg >= wgb2) ? 2 : wg >= wgb1 ? 1 : 0;
+        row0 = (wg - pick3(sg0, 0, wgb1, wgb2)) * R;
+      }
     }
   }
-  auto slot_seg = [&](int s) { return f.sum ? s / R : sg0; };
-  auto slot_row = [&](int s) { return row0 + (f.sum ? s % R : s); };
+  auto slot_seg = [&](int s) { return h_sum ? s / R : sg0; };
+  auto slot_row = [&](int s) { return row0 + (h_sum ? s % R : s); };
 
   // ---- loads: the input (L2-resident), then the weight stream (or the A rows
   // when shrinking); the expand's B values are read after the row loop
@@ -515,9 +543,7 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
       float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
       if (cval[u]) {
         const int64_t o = (int64_t)cidx[u] * WPC + 4 * j;
-        t4 = *reinterpret_cast<const float4*>(f.v[0] + o);
-        if (f.nv > 1) t4 = add4(t4, *reinterpret_cast<const float4*>(f.v[1] + o));
-        if (f.nv > 2) t4 = add4(t4, *reinterpret_cast<const float4*>(f.v[2] + o));
+        t4 = gload4(p_v0 + o);
       }
       xr[u][j] = t4;
     }
@@ -531,13 +557,22 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
     for (int r = 0; r < G; ++r) {
       const int s = grp * G + r;
       if (s < nslots) {
-        const GemvSeg& g = a.seg[slot_seg(s)];
-        const int row = min(slot_row(s), g.n - 1);
-        const uint8_t* qrow = g.qs + (int64_t)row * row_bytes;
+        const int sg = slot_seg(s);
+        const uint8_t* qs = p_qs0;
+        const void* scp = p_sc0;
+        int n = p_n0;
+        if (sg != 0) {  // segment 0's values come with the launch; the others from f
+          asm volatile("");
+          qs = pick3(sg, p_qs0, a.seg[1].qs, a.seg[2].qs);
+          scp = pick3(sg, p_sc0, a.seg[1].sc, a.seg[2].sc);
+          n = pick3(sg, p_n0, a.seg[1].n, a.seg[2].n);
+        }
+        const int row = min(slot_row(s), n - 1);
+        const uint8_t* qrow = qs + (int64_t)row * row_bytes;
 #pragma unroll
         for (int u = 0; u < CPW; ++u) {
           q[r][u] = stream_load16(qrow + (int64_t)cidx[u] * 16);
-          sc[r][u] = F::load_sc(g.sc, row, K, cidx[u]);
+          sc[r][u] = F::load_sc(scp, row, K, cidx[u]);
         }
       }
     }
@@ -564,7 +599,9 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
                             : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   } else {
-    if (trow) {
+    if (ngroups > 0) load_group(qa, sa, 0);
+    if (ngroups > 1) load_group(qb, sb, 1);
+    if (trow) {  // after the first weight loads: finding the A row reads the entry list
       int e = 0, base = 0;
       while (base + f.ent[e].rank <= wg) {
         base += f.ent[e].rank;
@@ -576,8 +613,6 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
 #pragma unroll
         for (int j = 0; j < NS; ++j) av[0][u][j] = *reinterpret_cast<const float4*>(Ar + (int64_t)cidx[u] * WPC + 4 * j);
     }
-    if (ngroups > 0) load_group(qa, sa, 0);
-    if (ngroups > 1) load_group(qb, sb, 1);
   }
 
   // ---- chunk sums and sum of squares of the input
@@ -865,7 +900,9 @@ hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
     wg = gemv_wgs();
   }
   a.grid = f.shrink_wgs + f.sparse_wgs + wg;
-  QBL_LAUNCH((gemv_b1_kernel<QT, W, CPW, G>), dim3(a.grid), dim3(W * 64), 0, lc, f);
+  const int flags = b1_flags(f.sum, a.nseg, f.shrink_in_gemv, f.shrink_wgs);
+  QBL_LAUNCH((gemv_b1_kernel<QT, W, CPW, G>), dim3(a.grid), dim3(W * 64), 0, lc, a.seg[0].qs, a.seg[0].sc, f.v[0], a.k,
+             f.shrink_wgs + f.sparse_wgs, f.rows_per_wg, a.seg[0].n, flags, f.rows_total, f);
   return hipGetLastError();
 }
 
@@ -1044,7 +1081,9 @@ bool fused_supported(int qtype, int k) {
 hipError_t launch_fused(FusedArgs& f, const LaunchCtx& lc) {
   (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   GemvArgs& a = f.g;
-  if (a.batch != 1 || !fused_supported(a.qtype, a.k) || f.rows_total > kB1MaxT) return hipErrorInvalidValue;
+  if (a.batch != 1 || f.nv != 1 || !fused_supported(a.qtype, a.k) || f.rows_total > kB1MaxT) return hipErrorInvalidValue;
+  // the flags word (b1_flags) holds the shrink workgroup count in 24 bits
+  if (f.rows_total > (1 << 23)) return hipErrorInvalidValue;
   for (int i = 0; i < a.nseg; ++i)
     if (f.sum && a.seg[i].n != a.seg[0].n) return hipErrorInvalidValue;
   // sparse items: every (segment, sparse adapter) has its n rows at sp_base, all below sp_items

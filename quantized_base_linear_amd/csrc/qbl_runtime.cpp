@@ -1258,7 +1258,9 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
   };
 
   const int qt0 = base->lin[(size_t)lin[0]].qtype;
-  if (batch == 1 && same_type && qbl::fused_supported(qt0, (int)K) &&
+  // the fused batch-1 launch takes a single input vector; the sum of several
+  // (q, k and v written apart) goes through the prep + GEMV path
+  if (batch == 1 && nv == 1 && same_type && qbl::fused_supported(qt0, (int)K) &&
       (T == 0 || t_buf) && v_stride == K) {
     qbl::FusedArgs f{};
     fill_segments(f.g, qt0);
