@@ -51,7 +51,6 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kStageThreads = 256;
 // Waves of a GEMV workgroup, splitting the blocks of K: 8 for the q4 formats
 // (two workgroups of 8 waves per compute unit ran the 70B MLP at batch 8 2.5 %
 // (q4_sm) and 3 % (q4_K) faster than 4 waves), 4 for q8_0 (the same either way).
@@ -88,118 +87,65 @@ __device__ __forceinline__ half8 codes_q4(uint32_t w) {
 }
 
 // ---------------------------------------------------------------------------
-// Scan: workgroup (p, q) covers inputs [256 p, 256 p + 256) of every batch row
-// and adapter rows [16 q, 16 q + 16):
-//   mxpart[p][b] = largest |x[b][k]| over the range (q = 0 only; 0 for rows
-//   b >= batch),
-//   tpart[p][j][b] = sum over the range of A[j][k] x[b][k] (the low-rank shrink
-//   split by range: lane l takes inputs 4 l .. 4 l + 3, then a fixed-order wave
-//   sum).  Wave w takes rows 16 q + 4 w .. + 3, their loads issued together.
+// Prep: one launch before the GEMV, two kinds of workgroup.
+//   Row workgroups [0, 8 nrw): row b = wg / nrw, blocks [256 (wg % nrw), +256)
+//   of it.  Each finds the row's largest |x| itself (the whole row, from L2),
+//   sets e_b, and writes the A-operand values of its blocks in instruction order:
+//   frag[blk][l] for lane l = 16 g + r: row r < 8: hi of batch row r, r >= 8: lo
+//   of batch row r - 8, inputs 8 g .. 8 g + 7 of the block (permuted for the q4
+//   formats as codes_q4 expects); xsum[blk][r] = X of batch row r for r < 8
+//   (float32, input order), 0 for r >= 8; ex[b] = e_b.  Rows b >= batch are zero.
+//   Shrink workgroups (range p, adapter rows [16 q, 16 q + 16)) follow:
+//   tpart[p][j][b] = sum over inputs [1024 p, 1024 p + 1024) of A[j][k] x[b][k]
+//   (lane l takes inputs 4 l + 256 c, c = 0..3, in order, then a fixed-order
+//   wave sum); the GEMV adds the ranges in order.  Wave w takes rows 16 q + 4 w
+//   .. + 3, their loads issued together.
 // ---------------------------------------------------------------------------
-constexpr int kScanK = 256;
+constexpr int kScanK = 1024;
 constexpr int kScanJ = 16;
+constexpr int kRowBlocks = 256;  // blocks per row workgroup
 
 struct ScanArgs {
   const float* x;
   int64_t x_stride;
   int batch, k, T, n_ent;
+  int nrw;         // row workgroups per batch row
   PrepEntry ent[kMaxPrepEntries];
-  float* mxpart;   // [P][8]
   float* tpart;    // [P][T][8]
+  u32x4* frag;     // [nblk][64]
+  float* xsum;     // [nblk][16]
+  int* ex;         // [8]
 };
 
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
-  __shared__ __attribute__((aligned(16))) float xs[8][kScanK];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int p = blockIdx.x, k0 = p * kScanK, kn = min(kScanK, a.k - k0);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {  // thread: rows wave and wave + 4, inputs 4 lane ..
-    const int b = wave + 4 * i;
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (b < a.batch && 4 * lane < kn) v = *gp(reinterpret_cast<const f32x4*>(a.x + (int64_t)b * a.x_stride + k0) + lane);
-    *reinterpret_cast<f32x4*>(&xs[b][4 * lane]) = v;
-    if (blockIdx.y == 0) {
-      float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      if (lane == 0) a.mxpart[p * 8 + b] = mx;
-    }
-  }
-  const int j0 = blockIdx.y * kScanJ + 4 * wave;
-  f32x4 w[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    w[u] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    if (j0 + u < a.T && 4 * lane < kn) {
-      const int j = j0 + u;
-      int e = 0, base = 0;
-      while (base + a.ent[e].rank <= j) base += a.ent[e++].rank;
-      w[u] = *gp(reinterpret_cast<const f32x4*>(a.ent[e].A + (int64_t)(j - base) * a.k + k0) + lane);
-    }
-  }
-  __syncthreads();
-  if (j0 >= a.T) return;
-  f32x4 xv[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) xv[b] = *reinterpret_cast<const f32x4*>(&xs[b][4 * lane]);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    if (j0 + u >= a.T) break;
-    float acc[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-      acc[b] = wave_sum(fmaf(w[u].x, xv[b].x, fmaf(w[u].y, xv[b].y, fmaf(w[u].z, xv[b].z, w[u].w * xv[b].w))));
-    if (lane < 8) {
-      float v = acc[0];
-#pragma unroll
-      for (int b = 1; b < 8; ++b) v = lane == b ? acc[b] : v;
-      a.tpart[((int64_t)p * a.T + j0 + u) * 8 + lane] = v;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Stage: workgroups [0, nblk / 32): thread (b = tid / 32, block 32 wg + tid % 32)
-// writes the A-operand values of the block in instruction order:
-//   frag[blk][l] for lane l = 16 g + r: row r < 8: hi of batch row r, r >= 8:
-//   lo of batch row r - 8, inputs 8 g .. 8 g + 7 of the block (permuted for
-//   the q4 formats as codes_q4 expects);
-//   xsum[blk][r] = X of batch row r for r < 8 (float32, input order), 0 for r >= 8;
-//   ex[b] = e_b, from the scan's partial maxima.
-// Rows b >= batch are zero.  The workgroups after those add the scan's partial
-// shrink sums in range order: t[b][j] = sum_p tpart[p][j][b].
-// ---------------------------------------------------------------------------
 template <int QT>
-__global__ __launch_bounds__(256) void stage_kernel(const float* x, int64_t x_stride, int batch, int K, int P, int T,
-                                                    const float* mxpart, const float* tpart, float* t, u32x4* frag,
-                                                    float* xsum, int* ex) {
-  const int tid = threadIdx.x, nblk = K / 32, conv = (nblk + 31) / 32;
-  if ((int)blockIdx.x >= conv) {  // 16 lanes per output (j, b): ranges l16, l16 + 16, ..., then a fixed-order sum
-    const int idx = ((int)blockIdx.x - conv) * 16 + (tid >> 4), l16 = tid & 15;
-    const int j = idx >> 3, b = idx & 7;
-    const bool ok = j < T && b < batch;
-    float s = 0.0f;
-    if (ok)
-      for (int q = l16; q < P; q += 16) s += tpart[((int64_t)q * T + j) * 8 + b];
-    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (ok && l16 == 0) t[(int64_t)b * T + j] = s;
-    return;
-  }
-  const int b = tid >> 5, l32 = tid & 31;
+__device__ __forceinline__ void prep_rows(const ScanArgs& a, int wg) {
+  __shared__ float mxw[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = wg / a.nrw, part = wg % a.nrw, K = a.k, nblk = K / 32;
+  const bool live = b < a.batch;
+  const float* xr = a.x + (int64_t)b * a.x_stride;
   float mx = 0.0f;
-  for (int q = l32; q < P; q += 32) mx = fmaxf(mx, mxpart[q * 8 + b]);
-  for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (live) {
+#pragma unroll 8
+    for (int i = tid; i < K / 4; i += 256) {
+      const float4 v = gload4(xr + 4 * i);
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) mxw[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(mxw[0], mxw[1]), fmaxf(mxw[2], mxw[3]));
   int e = 0;
   if (mx > 0.0f) {
     int me;
     frexpf(mx, &me);  // mx in [2^(me-1), 2^me)
     e = me - 15;
   }
-  if (blockIdx.x == 0 && l32 == 0) ex[b] = e;
-  const int blk = blockIdx.x * 32 + l32;
+  if (part == 0 && tid == 0) a.ex[b] = e;
+  const int blk = part * kRowBlocks + tid;
   if (blk >= nblk) return;
-  const bool live = b < batch;
-  const float* xr = x + (int64_t)b * x_stride;
-  u32x4* dst = frag + (int64_t)blk * 64 + b;
+  u32x4* dst = a.frag + (int64_t)blk * 64 + b;
   float s = 0.0f;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -232,9 +178,97 @@ __global__ __launch_bounds__(256) void stage_kernel(const float* x, int64_t x_st
     dst[16 * g] = hv;
     dst[16 * g + 8] = lv;
   }
-  float* xs = xsum + (int64_t)blk * 16;
+  float* xs = a.xsum + (int64_t)blk * 16;
   xs[b] = s;
   xs[b + 8] = 0.0f;
+}
+
+__device__ __forceinline__ void prep_shrink(const ScanArgs& a, int wg) {
+  __shared__ __attribute__((aligned(16))) float xs[8][kScanK];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nq = (a.T + kScanJ - 1) / kScanJ;
+  const int p = wg / nq, q = wg % nq, k0 = p * kScanK, kn = min(kScanK, a.k - k0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // thread: rows wave and wave + 4, inputs 4 lane + 256 c
+    const int b = wave + 4 * i;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = 4 * lane + 256 * c;
+      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (b < a.batch && k < kn) v = *gp(reinterpret_cast<const f32x4*>(a.x + (int64_t)b * a.x_stride + k0 + k));
+      *reinterpret_cast<f32x4*>(&xs[b][k]) = v;
+    }
+  }
+  const int j0 = q * kScanJ + 4 * wave;
+  f32x4 w[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float* Ar = nullptr;
+    if (j0 + u < a.T) {
+      const int j = j0 + u;
+      int e = 0, base = 0;
+      while (base + a.ent[e].rank <= j) base += a.ent[e++].rank;
+      Ar = a.ent[e].A + (int64_t)(j - base) * a.k + k0;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = 4 * lane + 256 * c;
+      w[u][c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      if (Ar && k < kn) w[u][c] = *gp(reinterpret_cast<const f32x4*>(Ar + k));
+    }
+  }
+  __syncthreads();
+  if (j0 >= a.T) return;
+  float acc[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[u][b] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(&xs[b][4 * lane + 256 * c]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc[u][b] = fmaf(w[u][c].x, xv.x, fmaf(w[u][c].y, xv.y, fmaf(w[u][c].z, xv.z, fmaf(w[u][c].w, xv.w, acc[u][b]))));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (j0 + u >= a.T) break;
+    float sum[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) sum[b] = wave_sum(acc[u][b]);
+    if (lane < 8) {
+      float v = sum[0];
+#pragma unroll
+      for (int b = 1; b < 8; ++b) v = lane == b ? sum[b] : v;
+      a.tpart[((int64_t)p * a.T + j0 + u) * 8 + lane] = v;
+    }
+  }
+}
+
+template <int QT>
+__global__ __launch_bounds__(256) void prep8_kernel(ScanArgs a) {
+  const int wg = blockIdx.x, nrow = 8 * a.nrw;
+  if (wg < nrow) prep_rows<QT>(a, wg);
+  else prep_shrink(a, wg - nrow);
+}
+
+// t[b][j] = the range partial sums tpart[p][j][b] added in range order; the
+// loads go out 8 at a time.
+__device__ __forceinline__ float t_value(const float* tpart, int P, int T, int j, int b) {
+  float s = 0.0f;
+  for (int p0 = 0; p0 < P; p0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p0 + u < P ? tpart[((int64_t)(p0 + u) * T + j) * 8 + b] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (p0 + u < P) s += v[u];
+  }
+  return s;
 }
 
 // ---------------------------------------------------------------------------
@@ -295,7 +329,10 @@ struct MfmaSplit {
   // bal_k > 0 (one segment, no split): the rows' 16-row tiles spread evenly over
   // bal_c compute units, bal_k workgroups per unit (see tiles_of)
   int bal_k, bal_c, bal_t;
+  const float* tpart;      // the prep launch's shrink partial sums [P][T][8]
+  int P, T;
 };
+constexpr int kMaxT = 512;   // summed rank of a linear's list (the attach limit)
 
 // Rows of workgroup wg under the even spread: the dispatcher fills compute
 // units breadth first, so workgroups wg, wg + c, wg + 2c, ... share unit wg % c.
@@ -312,7 +349,7 @@ __device__ __forceinline__ void tiles_of(const MfmaSplit& sp, int wg, int& first
 // Output (b, n) of segment g from its base sum s (before the 2^e_b scale):
 // scale, then the adapters in list order, then the store.
 __device__ __forceinline__ void finish_output(const GemvArgs& a, const GemvSeg& g, const int* ex, int b, int n,
-                                              float s) {
+                                              float s, const float* tl, int T) {  // t[b][j] at tl[b T + j]
   float v = ldexpf(s, ex[b]);
   for (int i = 0; i < g.lora.n_ad; ++i) {
     const int rk = g.lora.rank[i];
@@ -323,7 +360,7 @@ __device__ __forceinline__ void finish_output(const GemvArgs& a, const GemvSeg& 
       for (uint32_t e = g.lora.rp[i][n]; e < e1; ++e) p = fmaf(h2f(g.lora.sv[i][e]), xb[g.lora.ci[i][e]], p);
     } else {
       const float* Br = g.lora.B[i] + (int64_t)n * rk;
-      const float* tb = a.t + (int64_t)b * a.t_stride + g.lora.toff[i];
+      const float* tb = tl + b * T + g.lora.toff[i];
 #pragma unroll 8
       for (int q = 0; q < rk; ++q) p = fmaf(Br[q], tb[q], p);
     }
@@ -338,7 +375,11 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
   using F = SlabFmt<QT>;
   constexpr int S = F::S;
   constexpr int kWaves = mfma_waves<QT>(), kMfmaThreads = 64 * kWaves;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * F::kWave];
+  // the slab regions (reused after the slab loop for the waves' sums, 4 KiB per
+  // wave), then the shrink results t[b][j] (without split-K)
+  constexpr int kSlabLds = kWaves * F::kWave > kWaves * 4096 ? kWaves * F::kWave : kWaves * 4096;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kSlabLds + 8 * kMaxT * 4];
+  float* tl = reinterpret_cast<float*>(lds + kSlabLds);
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int wg = blockIdx.x;
@@ -451,6 +492,20 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
     constexpr int NT = decltype(ntc)::value;
     SlabRegs<QT> r;
     if (wave < nsl) issue(r, wave, ntc);
+    // the shrink results, behind the first slab loads: into LDS for this
+    // workgroup's rows, or (split-K) one value per thread of the first
+    // workgroups into a.t for the reduce launch
+    if (sp.ks == 1) {
+      for (int i = tid; i < 8 * sp.T; i += kMfmaThreads) {
+        const int j = i >> 3, b = i & 7;
+        if (b < a.batch) tl[b * sp.T + j] = t_value(sp.tpart, sp.P, sp.T, j, b);
+      }
+    } else {
+      for (int i = wg * kMfmaThreads + tid; i < 8 * sp.T; i += a.grid * kMfmaThreads) {
+        const int j = i >> 3, b = i & 7;
+        if (b < a.batch) const_cast<float*>(a.t)[(int64_t)b * sp.T + j] = t_value(sp.tpart, sp.P, sp.T, j, b);
+      }
+    }
     for (int sl = wave; sl < nsl; sl += kWaves) {
       stash(r, sl, ntc);
       u32x4 xf[S];
@@ -521,7 +576,7 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
   if (sp.ks == 1) {  // thread -> (row rr, batch row b), b fastest: 8 lanes share a row of each B_i
     for (int idx = tid; idx < 64 * 8; idx += kMfmaThreads) {
       const int b = idx & 7, rr = idx >> 3, n = row0 + rr;
-      if (b < a.batch && rr < 16 * nt && n < g.n) finish_output(a, g, ex, b, n, wg_sum(b, rr));
+      if (b < a.batch && rr < 16 * nt && n < g.n) finish_output(a, g, ex, b, n, wg_sum(b, rr), tl, sp.T);
     }
     return;
   }
@@ -545,7 +600,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemvArgs a, MfmaSplit
   const float* p = sp.partial + sp.poff[si] + (int64_t)b * g.n + n;
   float s = 0.0f;
   for (int q = 0; q < sp.ks; ++q) s += p[(int64_t)q * 8 * g.n];
-  finish_output(a, g, ex, b, n, s);
+  finish_output(a, g, ex, b, n, s, a.t, sp.T);
 }
 
 // Workgroups per 64 rows: none split when the rows alone give 1.5 workgroups
@@ -572,15 +627,14 @@ int split_ks(int64_t row_groups, int nblk, int slab, int waves) {
 }
 
 template <int QT>
-hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, float* t, void* stage, int ks_force,
+hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, void* stage, int ks_force,
                      const LaunchCtx& prep_lc, const LaunchCtx& lc) {
   const int nblk = a.k / 32, P = (a.k + kScanK - 1) / kScanK;
   char* st = static_cast<char*>(stage);
   u32x4* frag = reinterpret_cast<u32x4*>(st);
   float* xsum = reinterpret_cast<float*>(st + (int64_t)nblk * 1024);
   int* ex = reinterpret_cast<int*>(xsum + (int64_t)nblk * 16);
-  float* mxpart = reinterpret_cast<float*>(st + mfma_stage_only_bytes(a.k));
-  float* tpart = mxpart + (int64_t)P * 8;
+  float* tpart = reinterpret_cast<float*>(st + mfma_stage_only_bytes(a.k));
   ScanArgs sa{};
   sa.x = a.x;
   sa.x_stride = a.x_stride;
@@ -588,25 +642,23 @@ hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, float*
   sa.k = a.k;
   sa.T = T;
   sa.n_ent = n_ent;
+  sa.nrw = (nblk + kRowBlocks - 1) / kRowBlocks;
   for (int i = 0; i < n_ent; ++i) sa.ent[i] = ent[i];
-  sa.mxpart = mxpart;
   sa.tpart = tpart;
-  // the timing events of prep_lc go around the scan and the stage launches
-  LaunchCtx p1 = prep_lc, p2 = prep_lc;
-  p1.stop = nullptr;
-  p2.start = nullptr;
-  QBL_LAUNCH(scan_kernel, dim3(P, std::max(1, (T + kScanJ - 1) / kScanJ)), dim3(256), 0, p1, sa);
+  sa.frag = frag;
+  sa.xsum = xsum;
+  sa.ex = ex;
+  const int shrink_wgs = T > 0 ? P * ((T + kScanJ - 1) / kScanJ) : 0;
+  QBL_LAUNCH(prep8_kernel<QT>, dim3(8 * sa.nrw + shrink_wgs), dim3(256), 0, prep_lc, sa);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int conv = (nblk + 31) / 32, tred = (T * 8 + 15) / 16;
-  QBL_LAUNCH(stage_kernel<QT>, dim3(conv + tred), dim3(256), 0, p2, a.x, a.x_stride, a.batch, a.k, P, T, mxpart,
-             tpart, t, frag, xsum, ex);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int S = SlabFmt<QT>::S;
   int64_t row_groups = 0;
   for (int i = 0; i < a.nseg; ++i) row_groups += (a.seg[i].n + 63) / 64;
   MfmaSplit sp{};
+  sp.tpart = tpart;
+  sp.P = P;
+  sp.T = T;
   sp.ks = ks_force > 0 ? ks_force : split_ks(row_groups, nblk, S, mfma_waves<QT>());
   const int nslab = (nblk + S - 1) / S;
   sp.per = (nslab + sp.ks - 1) / sp.ks * S;
@@ -656,15 +708,15 @@ hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, float*
 }  // namespace
 
 // Staging layout: A operands [nblk][64] x 16 bytes, block sums [nblk][16]
-// floats, 8 exponents; the scan's partial maxima [P][8] and partial shrink sums
-// [P][T][8]; then the split-K partial sums.
+// floats, 8 exponents; the prep launch's partial shrink sums [P][T][8]; then
+// the split-K partial sums.
 int64_t mfma_stage_only_bytes(int k) {
   const int64_t nblk = k / 32;
   return (nblk * (1024 + 64) + 32 + 255) / 256 * 256;
 }
 int64_t mfma_scan_bytes(int k, int T) {
   const int64_t P = (k + kScanK - 1) / kScanK;
-  return (P * 8 * 4 * (1 + (int64_t)T) + 255) / 256 * 256;
+  return (P * 8 * 4 * (int64_t)T + 255) / 256 * 256;
 }
 int64_t mfma_partial_bytes(int64_t rows) { return rows * 8 * 16 * 4; }  // up to 16 splits
 int64_t mfma_stage_bytes(int64_t rows, int k, int T) {
@@ -678,7 +730,7 @@ hipError_t launch_gemv_mfma(GemvArgs& a, const PrepEntry* ent, int n_ent, int T,
   if (a.batch < 2 || a.batch > 8 || a.nseg < 1 || a.nseg > kMaxSegs || !stage) return hipErrorInvalidValue;
   if (a.k < 32 || a.k % (a.qtype == QBL_FMT_Q4K ? 256 : 32) || a.x_stride % 4) return hipErrorInvalidValue;
   if (reinterpret_cast<uintptr_t>(stage) % 256 || reinterpret_cast<uintptr_t>(a.x) % 16) return hipErrorInvalidValue;
-  if (ks < 0 || ks > 16 || n_ent < 0 || n_ent > kMaxPrepEntries || T < 0 || (T > 0 && !a.t)) return hipErrorInvalidValue;
+  if (ks < 0 || ks > 16 || n_ent < 0 || n_ent > kMaxPrepEntries || T < 0 || T > kMaxT) return hipErrorInvalidValue;
   int rk = 0;
   for (int i = 0; i < n_ent; ++i) {
     if (ent[i].toff != rk || ent[i].rank <= 0) return hipErrorInvalidValue;
@@ -692,12 +744,11 @@ hipError_t launch_gemv_mfma(GemvArgs& a, const PrepEntry* ent, int n_ent, int T,
     if ((int64_t)(a.seg[i].n + 63) / 64 * 64 * rbytes >= (int64_t)1 << 31 ||
         (int64_t)(a.seg[i].n + 63) / 64 * 64 * sbytes >= (int64_t)1 << 31)
       return hipErrorInvalidValue;
-  if (rk != T || (T > 0 && a.t_stride != T)) return hipErrorInvalidValue;
-  float* t = const_cast<float*>(a.t);
+  if (rk != T || (T > 0 && !a.t)) return hipErrorInvalidValue;
   switch (a.qtype) {
-    case QBL_FMT_Q8: return launch_qt<QBL_FMT_Q8>(a, ent, n_ent, T, t, stage, ks, prep_lc, lc);
-    case QBL_FMT_Q4: return launch_qt<QBL_FMT_Q4>(a, ent, n_ent, T, t, stage, ks, prep_lc, lc);
-    case QBL_FMT_Q4K: return launch_qt<QBL_FMT_Q4K>(a, ent, n_ent, T, t, stage, ks, prep_lc, lc);
+    case QBL_FMT_Q8: return launch_qt<QBL_FMT_Q8>(a, ent, n_ent, T, stage, ks, prep_lc, lc);
+    case QBL_FMT_Q4: return launch_qt<QBL_FMT_Q4>(a, ent, n_ent, T, stage, ks, prep_lc, lc);
+    case QBL_FMT_Q4K: return launch_qt<QBL_FMT_Q4K>(a, ent, n_ent, T, stage, ks, prep_lc, lc);
     default: return hipErrorInvalidValue;
   }
 }

@@ -172,11 +172,11 @@ hipError_t launch_prep(const PrepArgs& a, const LaunchCtx& lc);
 // y = v / sqrt(mean(v^2) + 1e-6), one vector of n floats (n a multiple of 4)
 hipError_t launch_rms(const float* v, int n, float* y, const LaunchCtx& lc);
 hipError_t launch_gemv(GemvArgs& a, const LaunchCtx& lc);
-// Batch 2..8 on the matrix cores (no input glue): a scan launch (maxima of the
-// inputs and the low-rank shrink by input range), a stage launch (the inputs as
-// f16 instruction operands, the shrink results t into a.t, [batch][T]) -- both
-// timed by prep_lc -- then the GEMV launch and, when K is split, a reduce launch
-// (both timed by lc).  `stage`: mfma_stage_bytes(rows, k, T) bytes, rows = all
+// Batch 2..8 on the matrix cores (no input glue): a prep launch (the inputs as
+// f16 instruction operands with their per-row exponents, and the low-rank
+// shrink summed by input range), timed by prep_lc, then the GEMV launch and,
+// when K is split, a reduce launch (both timed by lc); the launch that finishes
+// the rows adds the shrink's ranges in order (a.t is not used).  `stage`: mfma_stage_bytes(rows, k, T) bytes, rows = all
 // output rows of the launch, 256-byte aligned.  ent: the shrink entries with
 // toff = running sum of the ranks.  ks: workgroups per 64 rows splitting K
 // (1..16; 0 picks it from the shape).
