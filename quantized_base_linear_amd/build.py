@@ -20,11 +20,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I" + os.path.join(ROOT, "include")]
 
 
-# Per-source flags.  qbl_gemv.hip: leading scalar kernel arguments arrive
-# preloaded in registers at wave launch (the batch-1 kernel's first loads then
-# wait for no argument fetch); firmware without preloading runs the compiler's
-# fallback prologue, which loads them.
-EXTRA = {"qbl_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"]}
+# Per-source flags.  qbl_gemv.hip, qbl_batched.hip: leading scalar kernel
+# arguments arrive preloaded in registers at wave launch (the GEMV kernels'
+# first loads then wait for no argument fetch); firmware without preloading
+# runs the compiler's fallback prologue, which loads them.
+EXTRA = {"qbl_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"],
+         "qbl_batched.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"]}
 
 
 def build(verbose: bool = False) -> str:

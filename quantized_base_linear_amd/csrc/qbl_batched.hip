@@ -117,13 +117,23 @@ struct ScanArgs {
   int* ex;         // [8]
 };
 
+// The prep launch's leading scalar arguments (preloaded into SGPRs at wave
+// launch), repeating fields of ScanArgs.
+struct PrepHot {
+  const float* x;
+  u32x4* frag;
+  float* xsum;
+  float* tpart;
+  int x_stride, batch, k, nrw, T;
+};
+
 template <int QT>
-__device__ __forceinline__ void prep_rows(const ScanArgs& a, int wg) {
+__device__ __forceinline__ void prep_rows(const PrepHot& h, const ScanArgs& a, int wg) {
   __shared__ float mxw[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int b = wg / a.nrw, part = wg % a.nrw, K = a.k, nblk = K / 32;
-  const bool live = b < a.batch;
-  const float* xr = a.x + (int64_t)b * a.x_stride;
+  const int b = wg / h.nrw, part = wg % h.nrw, K = h.k, nblk = K / 32;
+  const bool live = b < h.batch;
+  const float* xr = h.x + (int64_t)b * h.x_stride;
   float mx = 0.0f;
   if (live) {
 #pragma unroll 8
@@ -145,7 +155,7 @@ __device__ __forceinline__ void prep_rows(const ScanArgs& a, int wg) {
   if (part == 0 && tid == 0) a.ex[b] = e;
   const int blk = part * kRowBlocks + tid;
   if (blk >= nblk) return;
-  u32x4* dst = a.frag + (int64_t)blk * 64 + b;
+  u32x4* dst = h.frag + (int64_t)blk * 64 + b;
   float s = 0.0f;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -178,16 +188,16 @@ __device__ __forceinline__ void prep_rows(const ScanArgs& a, int wg) {
     dst[16 * g] = hv;
     dst[16 * g + 8] = lv;
   }
-  float* xs = a.xsum + (int64_t)blk * 16;
+  float* xs = h.xsum + (int64_t)blk * 16;
   xs[b] = s;
   xs[b + 8] = 0.0f;
 }
 
-__device__ __forceinline__ void prep_shrink(const ScanArgs& a, int wg) {
+__device__ __forceinline__ void prep_shrink(const PrepHot& h, const ScanArgs& a, int wg) {
   __shared__ __attribute__((aligned(16))) float xs[8][kScanK];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nq = (a.T + kScanJ - 1) / kScanJ;
-  const int p = wg / nq, q = wg % nq, k0 = p * kScanK, kn = min(kScanK, a.k - k0);
+  const int nq = (h.T + kScanJ - 1) / kScanJ;
+  const int p = wg / nq, q = wg % nq, k0 = p * kScanK, kn = min(kScanK, h.k - k0);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {  // thread: rows wave and wave + 4, inputs 4 lane + 256 c
     const int b = wave + 4 * i;
@@ -195,7 +205,7 @@ __device__ __forceinline__ void prep_shrink(const ScanArgs& a, int wg) {
     for (int c = 0; c < 4; ++c) {
       const int k = 4 * lane + 256 * c;
       f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (b < a.batch && k < kn) v = *gp(reinterpret_cast<const f32x4*>(a.x + (int64_t)b * a.x_stride + k0 + k));
+      if (b < h.batch && k < kn) v = *gp(reinterpret_cast<const f32x4*>(h.x + (int64_t)b * h.x_stride + k0 + k));
       *reinterpret_cast<f32x4*>(&xs[b][k]) = v;
     }
   }
@@ -204,11 +214,11 @@ __device__ __forceinline__ void prep_shrink(const ScanArgs& a, int wg) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const float* Ar = nullptr;
-    if (j0 + u < a.T) {
+    if (j0 + u < h.T) {
       const int j = j0 + u;
       int e = 0, base = 0;
       while (base + a.ent[e].rank <= j) base += a.ent[e++].rank;
-      Ar = a.ent[e].A + (int64_t)(j - base) * a.k + k0;
+      Ar = a.ent[e].A + (int64_t)(j - base) * h.k + k0;
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -218,7 +228,7 @@ __device__ __forceinline__ void prep_shrink(const ScanArgs& a, int wg) {
     }
   }
   __syncthreads();
-  if (j0 >= a.T) return;
+  if (j0 >= h.T) return;
   float acc[4][8];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
@@ -236,7 +246,7 @@ __device__ __forceinline__ void prep_shrink(const ScanArgs& a, int wg) {
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    if (j0 + u >= a.T) break;
+    if (j0 + u >= h.T) break;
     float sum[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) sum[b] = wave_sum(acc[u][b]);
@@ -244,16 +254,18 @@ __device__ __forceinline__ void prep_shrink(const ScanArgs& a, int wg) {
       float v = sum[0];
 #pragma unroll
       for (int b = 1; b < 8; ++b) v = lane == b ? sum[b] : v;
-      a.tpart[((int64_t)p * a.T + j0 + u) * 8 + lane] = v;
+      h.tpart[((int64_t)p * h.T + j0 + u) * 8 + lane] = v;
     }
   }
 }
 
 template <int QT>
-__global__ __launch_bounds__(256) void prep8_kernel(ScanArgs a) {
-  const int wg = blockIdx.x, nrow = 8 * a.nrw;
-  if (wg < nrow) prep_rows<QT>(a, wg);
-  else prep_shrink(a, wg - nrow);
+__global__ __launch_bounds__(256) void prep8_kernel(const float* p_x, u32x4* p_frag, float* p_xsum, float* p_tpart,
+                                                    int p_xs, int p_batch, int p_k, int p_nrw, int p_T, ScanArgs a) {
+  const PrepHot h{p_x, p_frag, p_xsum, p_tpart, p_xs, p_batch, p_k, p_nrw, p_T};
+  const int wg = blockIdx.x, nrow = 8 * h.nrw;
+  if (wg < nrow) prep_rows<QT>(h, a, wg);
+  else prep_shrink(h, a, wg - nrow);
 }
 
 // t[b][j] = the range partial sums tpart[p][j][b] added in range order; the
@@ -338,12 +350,12 @@ constexpr int kMaxT = 512;   // summed rank of a linear's list (the attach limit
 // units breadth first, so workgroups wg, wg + c, wg + 2c, ... share unit wg % c.
 // Unit u owns a contiguous run of t / c (+1 for the first t % c units) tiles,
 // split over its k workgroups the same way.  First tile and tile count.
-__device__ __forceinline__ void tiles_of(const MfmaSplit& sp, int wg, int& first, int& nt) {
-  const int c = sp.bal_c, u = wg % c, s = wg / c;
-  const int tu = sp.bal_t / c + (u < sp.bal_t % c ? 1 : 0);
-  const int u0 = u * (sp.bal_t / c) + min(u, sp.bal_t % c);
-  nt = tu / sp.bal_k + (s < tu % sp.bal_k ? 1 : 0);
-  first = u0 + s * (tu / sp.bal_k) + min(s, tu % sp.bal_k);
+__device__ __forceinline__ void tiles_of(int bal_k, int c, int bal_t, int wg, int& first, int& nt) {
+  const int u = wg % c, s = wg / c;
+  const int tu = bal_t / c + (u < bal_t % c ? 1 : 0);
+  const int u0 = u * (bal_t / c) + min(u, bal_t % c);
+  nt = tu / bal_k + (s < tu % bal_k ? 1 : 0);
+  first = u0 + s * (tu / bal_k) + min(s, tu % bal_k);
 }
 
 // Output (b, n) of segment g from its base sum s (before the 2^e_b scale):
@@ -369,9 +381,19 @@ __device__ __forceinline__ void finish_output(const GemvArgs& a, const GemvSeg& 
   g.y[(int64_t)b * g.y_stride + n] = v;
 }
 
+// Leading scalar arguments (preloaded into SGPRs at wave launch, so the first
+// slab loads wait for no argument fetch): segment 0's weights and scales, the
+// staged inputs and block sums, K, segment 0's height, blocks per split, the
+// even spread's tile count and a packed word (ks | nseg << 5 | bal_k << 7 |
+// bal_c << 10); they repeat fields of a and sp.
+__host__ __device__ constexpr int mfma_pack(int ks, int nseg, int bal_k, int bal_c) {
+  return ks | nseg << 5 | bal_k << 7 | bal_c << 10;
+}
+
 template <int QT>
 __global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
-    GemvArgs a, MfmaSplit sp, const u32x4* frag, const float* xsum, const int* ex) {
+    const uint8_t* p_qs, const void* p_sc, const u32x4* frag, const float* xsum, int p_k, int p_n, int p_per,
+    int p_balt, int p_pack, GemvArgs a, MfmaSplit sp, const int* ex) {
   using F = SlabFmt<QT>;
   constexpr int S = F::S;
   constexpr int kWaves = mfma_waves<QT>(), kMfmaThreads = 64 * kWaves;
@@ -383,23 +405,34 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int wg = blockIdx.x;
-  const int si = (a.nseg > 2 && wg >= a.seg[2].wg_begin) ? 2 : (a.nseg > 1 && wg >= a.seg[1].wg_begin) ? 1 : 0;
+  const int ksn = p_pack & 31, nseg = (p_pack >> 5) & 3, bal_k = (p_pack >> 7) & 7, bal_c = p_pack >> 10;
+  int si = 0, wgb = 0, n_rows = p_n;
+  const uint8_t* qs = p_qs;
+  const void* scp = p_sc;
+  if (nseg > 1) {  // several segments: which one holds wg, and its arrays (read from a)
+    asm volatile("");
+    si = (nseg > 2 && wg >= a.seg[2].wg_begin) ? 2 : wg >= a.seg[1].wg_begin ? 1 : 0;
+    wgb = a.seg[si].wg_begin;
+    qs = a.seg[si].qs;
+    scp = a.seg[si].sc;
+    n_rows = a.seg[si].n;
+  }
   const GemvSeg& g = a.seg[si];
-  const int local = wg - g.wg_begin;
-  const int rg = local / sp.ks, ks = local % sp.ks;
+  const int local = wg - wgb;
+  const int rg = local / ksn, ks = local % ksn;
   // 64 rows (4 tiles of 16) per workgroup, or fewer under the even spread
   int row0 = rg * 64, nt = 4;
-  if (sp.bal_k > 0) {
+  if (bal_k > 0) {
     int first;
-    tiles_of(sp, wg, first, nt);
+    tiles_of(bal_k, bal_c, p_balt, wg, first, nt);
     row0 = 16 * first;
   }
   // loads of rows past the workgroup's tiles go past the buffer end: they
   // return zero without a memory access (buffers and slab offsets stay below
   // 2^31 bytes, so the sum stays below 2^32)
   constexpr uint32_t kPastEnd = 0x80000000u;
-  const int K = a.k, nblk = K / 32;
-  const int kb0 = min(nblk, ks * sp.per), kb1 = min(nblk, kb0 + sp.per);
+  const int K = p_k, nblk = K / 32;
+  const int kb0 = min(nblk, ks * p_per), kb1 = min(nblk, kb0 + p_per);
   const int nsl = (kb1 - kb0 + S - 1) / S;
   const int64_t rbytes = Fmt<QT>::row_bytes(K);
 
@@ -411,14 +444,14 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
   // loop plus the slab's offset (wave-uniform).  Reads past the end of a
   // buffer return zero; rows past n and blocks past the range land there or in
   // the next row, and neither is used.
-  const uint32_t n32 = (uint32_t)g.n, nb32 = (uint32_t)nblk;
-  const __amdgpu_buffer_rsrc_t qs_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.qs), 0,
+  const uint32_t n32 = (uint32_t)n_rows, nb32 = (uint32_t)nblk;
+  const __amdgpu_buffer_rsrc_t qs_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(qs), 0,
                                                                          (int)(n32 * (uint32_t)rbytes), kRsrcWord3);
   uint32_t sc_bytes;
   if constexpr (QT == QBL_FMT_Q4K) sc_bytes = n32 * (uint32_t)(K / 256) * 16u;
   else sc_bytes = n32 * nb32 * (uint32_t)F::kScE;
   const __amdgpu_buffer_rsrc_t sc_r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.sc), 0, (int)sc_bytes, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(scp), 0, (int)sc_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t fr_r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(frag), 0, (int)(nb32 * 1024u), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t xs_r =
@@ -495,7 +528,7 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
     // the shrink results, behind the first slab loads: into LDS for this
     // workgroup's rows, or (split-K) one value per thread of the first
     // workgroups into a.t for the reduce launch
-    if (sp.ks == 1) {
+    if (ksn == 1) {
       for (int i = tid; i < 8 * sp.T; i += kMfmaThreads) {
         const int j = i >> 3, b = i & 7;
         if (b < a.batch) tl[b * sp.T + j] = t_value(sp.tpart, sp.P, sp.T, j, b);
@@ -573,7 +606,7 @@ __global__ __launch_bounds__(64 * mfma_waves<QT>(), 4) void gemv_mfma_kernel(
     }
     return hi + lo;
   };
-  if (sp.ks == 1) {  // thread -> (row rr, batch row b), b fastest: 8 lanes share a row of each B_i
+  if (ksn == 1) {  // thread -> (row rr, batch row b), b fastest: 8 lanes share a row of each B_i
     for (int idx = tid; idx < 64 * 8; idx += kMfmaThreads) {
       const int b = idx & 7, rr = idx >> 3, n = row0 + rr;
       if (b < a.batch && rr < 16 * nt && n < g.n) finish_output(a, g, ex, b, n, wg_sum(b, rr), tl, sp.T);
@@ -649,7 +682,8 @@ hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, void* 
   sa.xsum = xsum;
   sa.ex = ex;
   const int shrink_wgs = T > 0 ? P * ((T + kScanJ - 1) / kScanJ) : 0;
-  QBL_LAUNCH(prep8_kernel<QT>, dim3(8 * sa.nrw + shrink_wgs), dim3(256), 0, prep_lc, sa);
+  QBL_LAUNCH(prep8_kernel<QT>, dim3(8 * sa.nrw + shrink_wgs), dim3(256), 0, prep_lc, sa.x, sa.frag, sa.xsum, sa.tpart,
+             (int)sa.x_stride, sa.batch, sa.k, sa.nrw, sa.T, sa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int S = SlabFmt<QT>::S;
@@ -682,7 +716,7 @@ hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, void* 
     const int c = cu_count(), t = (a.seg[0].n + 15) / 16;
     const int most_even = (t + c - 1) / c, k = (most_even + 3) / 4;
     const int most_now = 4 * ((wg + c - 1) / c);
-    if (k >= 2 && most_even < most_now) {
+    if (k >= 2 && k <= 7 && most_even < most_now) {  // k fits the packed argument's 3 bits
       sp.bal_k = k;
       sp.bal_c = c;
       sp.bal_t = t;
@@ -690,15 +724,18 @@ hipError_t launch_qt(GemvArgs& a, const PrepEntry* ent, int n_ent, int T, void* 
     }
   }
   a.grid = wg;
+  const int pack = mfma_pack(sp.ks, a.nseg, sp.bal_k, sp.bal_c);
   if (sp.ks == 1) {
-    QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(64 * mfma_waves<QT>()), 0, lc, a, sp, frag, xsum, ex);
+    QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(64 * mfma_waves<QT>()), 0, lc, a.seg[0].qs, a.seg[0].sc, frag,
+               xsum, a.k, a.seg[0].n, sp.per, sp.bal_t, pack, a, sp, ex);
     return hipGetLastError();
   }
   // the timing events of lc go around both launches
   LaunchCtx first = lc, second = lc;
   first.stop = nullptr;
   second.start = nullptr;
-  QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(64 * mfma_waves<QT>()), 0, first, a, sp, frag, xsum, ex);
+  QBL_LAUNCH(gemv_mfma_kernel<QT>, dim3(wg), dim3(64 * mfma_waves<QT>()), 0, first, a.seg[0].qs, a.seg[0].sc, frag,
+             xsum, a.k, a.seg[0].n, sp.per, sp.bal_t, pack, a, sp, ex);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   QBL_LAUNCH(split_reduce_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, second, a, sp, ex);
@@ -728,7 +765,8 @@ hipError_t launch_gemv_mfma(GemvArgs& a, const PrepEntry* ent, int n_ent, int T,
                             const LaunchCtx& prep_lc, const LaunchCtx& lc) {
   (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
   if (a.batch < 2 || a.batch > 8 || a.nseg < 1 || a.nseg > kMaxSegs || !stage) return hipErrorInvalidValue;
-  if (a.k < 32 || a.k % (a.qtype == QBL_FMT_Q4K ? 256 : 32) || a.x_stride % 4) return hipErrorInvalidValue;
+  if (a.k < 32 || a.k % (a.qtype == QBL_FMT_Q4K ? 256 : 32) || a.x_stride % 4 || a.x_stride >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
   if (reinterpret_cast<uintptr_t>(stage) % 256 || reinterpret_cast<uintptr_t>(a.x) % 16) return hipErrorInvalidValue;
   if (ks < 0 || ks > 16 || n_ent < 0 || n_ent > kMaxPrepEntries || T < 0 || T > kMaxT) return hipErrorInvalidValue;
   int rk = 0;
