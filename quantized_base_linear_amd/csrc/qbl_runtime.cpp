@@ -169,6 +169,16 @@ struct ListImpl {
       hipStreamSynchronize(st);  // cannot track: make the use complete now
     }
   }
+  // the event that tracks this list's work on st (created on first use)
+  hipEvent_t event_for(hipStream_t st) {
+    std::lock_guard<std::mutex> g(ev_mu);
+    for (auto& u : uses)
+      if (u.first == st) return u.second;
+    hipEvent_t ev;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess) return nullptr;
+    uses.emplace_back(st, ev);
+    return ev;
+  }
   ~ListImpl() {
     for (auto& u : uses) {
       hipEventSynchronize(u.second);
@@ -179,13 +189,24 @@ struct ListImpl {
 
 // Records, at scope exit, that work enqueued on `st` may read list L, so that
 // L (and the adapter memory it holds) outlives that work even when a run
-// returns an error after enqueuing part of it.
+// returns an error after enqueuing part of it.  A run's last launch can carry
+// the list's event instead (the launch's stop event, completed with the kernel:
+// no separate record between this run's work and the next one's, ~0.8 us of
+// every block step); the record at scope exit is then skipped.
 struct ListUse {
   ListImpl* L;
   hipStream_t st;
   bool on;
+  bool attached = false;
+  // Puts the list's event on lc as the stop event of the run's last launch when
+  // lc carries no timing event; returns it (nullptr: record at scope exit).
+  hipEvent_t attach(qbl::LaunchCtx& lc) {
+    if (!on || lc.start || lc.stop) return nullptr;
+    lc.stop = L->event_for(st);
+    return lc.stop;
+  }
   ~ListUse() {
-    if (on) L->mark_use(st);
+    if (on && !attached) L->mark_use(st);
   }
 };
 
@@ -1208,7 +1229,7 @@ uint32_t next_tag() {
 qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, float* const* outs,
                      int nlin, const float* const* vin, int nv, int rms, int batch, int64_t v_stride,
                      float* xin_buf, float* t_buf, uint64_t* sp_buf, hipStream_t st, bool sum_ok = false,
-                     bool* summed = nullptr, void* stage = nullptr) {
+                     bool* summed = nullptr, void* stage = nullptr, ListUse* last = nullptr) {
   if (summed) *summed = false;
   const int64_t K = base->lin[(size_t)lin[0]].k;
   int T = 0;
@@ -1303,8 +1324,11 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
     f.t = reinterpret_cast<uint64_t*>(t_buf);
     f.t_copy_stride = qbl::t_copy_stride(T);
     KernelTimer tm(0, st);
-    hipError_t e = qbl::launch_fused(f, tm.ctx());
+    qbl::LaunchCtx lc = tm.ctx();
+    const hipEvent_t done = last ? last->attach(lc) : nullptr;
+    hipError_t e = qbl::launch_fused(f, lc);
     if (e != hipSuccess) return hip_fail(e, "fused gemv launch");
+    if (done) last->attached = true;
     tm.stop();
     if (summed) *summed = f.sum != 0;
     return QBL_OK;
@@ -1350,8 +1374,12 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
       if (!stage) return fail(QBL_E_ARG, "the batched GEMV needs a staging buffer");
       KernelTimer ts(1, st);
       KernelTimer tm(0, st);
-      hipError_t e = qbl::launch_gemv_mfma(a, ent, n_ent, T, stage, 0, ts.ctx(), tm.ctx());
+      qbl::LaunchCtx lc = tm.ctx();
+      // the list's event rides on this group's last kernel when it is the run's last
+      const hipEvent_t done = last && launched == nlin ? last->attach(lc) : nullptr;
+      hipError_t e = qbl::launch_gemv_mfma(a, ent, n_ent, T, stage, 0, ts.ctx(), lc);
       if (e != hipSuccess) return hip_fail(e, "batched gemv launch");
+      if (done) last->attached = true;
       ts.stop();
       tm.stop();
       continue;
@@ -1366,10 +1394,13 @@ qbl_status run_group(const qbl_base* base, const ListImpl* L, const int* lin, fl
 }
 
 // rms of one vector into y (a prep launch with no adapter rows)
-qbl_status run_rms(const float* v, int64_t n, float* y, hipStream_t st) {
+qbl_status run_rms(const float* v, int64_t n, float* y, hipStream_t st, ListUse* last = nullptr) {
   KernelTimer tm(1, st);
-  hipError_t e = qbl::launch_rms(v, (int)n, y, tm.ctx());
+  qbl::LaunchCtx lc = tm.ctx();
+  const hipEvent_t done = last ? last->attach(lc) : nullptr;
+  hipError_t e = qbl::launch_rms(v, (int)n, y, lc);
   if (e != hipSuccess) return hip_fail(e, "rms launch");
+  if (done) last->attached = true;
   tm.stop();
   return QBL_OK;
 }
@@ -1512,13 +1543,13 @@ qbl_status linear_run(qbl_comp* comp, int32_t linear, const float* x, float* y, 
   const int lin[1] = {linear};
   float* outs[1] = {y};
   const float* v[1] = {x};
-  const ListUse use{L.get(), st, !L->plan[(size_t)linear].empty()};
+  ListUse use{L.get(), st, !L->plan[(size_t)linear].empty()};
   void* stage = batch > 1 ? static_cast<char*>(ws) + linear_t_bytes(batch, T) : nullptr;
   uint64_t* sp = batch == 1 && sp_items > 0
                      ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + linear_t_bytes(batch, T))
                      : nullptr;
   return run_group(b, L.get(), lin, outs, 1, v, 1, 0, batch, D.k, nullptr, static_cast<float*>(ws), sp, st, false,
-                   nullptr, stage);
+                   nullptr, stage, &use);
 }
 
 }  // namespace
@@ -1655,9 +1686,9 @@ extern "C" qbl_status qbl_block(qbl_comp* comp, int32_t block, const float* x, f
     if (qbl_status s = check_handoffs()) return s;
     if (blocks_have_entries(L.get(), block, 1))
       if (qbl_status s = refuse_capture(st)) return s;
-    const ListUse use{L.get(), st, true};
+    ListUse use{L.get(), st, true};
     if (qbl_status s = run_block(b, L.get(), B, x, 0, w, st)) return s;
-    return run_rms(w.dd, B.d, y, st);
+    return run_rms(w.dd, B.d, y, st, &use);
   })
 }
 
@@ -1689,14 +1720,15 @@ extern "C" qbl_status qbl_decode(qbl_comp* comp, int32_t first_block, int32_t n_
     if (qbl_status s = check_handoffs()) return s;
     if (blocks_have_entries(L.get(), first_block, n_blocks))
       if (qbl_status s = refuse_capture(st)) return s;
-    const ListUse use{L.get(), st, true};
+    ListUse use{L.get(), st, true};
     for (int t = 0; t < n_tokens; ++t) {
       const float* in = t == 0 ? x0 : y_tokens + (int64_t)(t - 1) * d;
       for (int i = 0; i < n_blocks; ++i) {
         if (qbl_status s = run_block(b, L.get(), blocks[(size_t)i], i == 0 ? in : w.dd, i == 0 ? 0 : 1, w, st))
           return s;
       }
-      if (qbl_status s = run_rms(w.dd, d, y_tokens + (int64_t)t * d, st)) return s;
+      if (qbl_status s = run_rms(w.dd, d, y_tokens + (int64_t)t * d, st, t + 1 == n_tokens ? &use : nullptr))
+        return s;
     }
     return QBL_OK;
   })

@@ -146,3 +146,38 @@ def test_changes_during_a_running_decode_do_not_reach_it(torch_cuda):
         assert not torch.equal(y_base, y_ref)
     finally:
         b.close()
+
+
+@pytest.mark.parametrize("qtype,n,k,batch", [(1, 4096, 4096, 1), (2, 512, 8192, 8), (3, 640, 4096, 5)])
+def test_changes_right_after_a_linear_run_do_not_reach_it(torch_cuda, qtype, n, k, batch):
+    """A linear run's last launch carries the list's completion event (at batch
+    1 the fused launch; above it the GEMV or, with K split, the reduce launch:
+    512 x 8192 splits K).  Attaching, clearing and freeing the adapter right
+    after the run is enqueued, before any synchronisation, leaves its output
+    equal to an undisturbed run."""
+    torch = torch_cuda
+    wl = workloads.Workload(f"inflight_{qtype}_{n}_{k}_{batch}",
+                            [workloads.LinearSpec(f"inflight/{qtype}/{n}/{k}", n, k, qtype)],
+                            [workloads.AdapterSpec("A1", 32, 1.0), workloads.AdapterSpec("A2", 8, -0.5)],
+                            batch=batch)
+    log(f"lifecycle after a linear run: qtype={qtype} n={n} k={k} batch={batch}")
+    b = Built(wl, check_bytes=False, keep_oracle=False)
+    q = b.q
+    try:
+        x = torch.from_numpy(np.ascontiguousarray(wl.x(0), np.float32)).cuda()
+        b.attach([0, 1])
+        ws = q.workspace(b.comp, q.OP_LINEAR, 0, batch)
+        y_ref = torch.empty((batch, n), dtype=torch.float32, device="cuda")
+        q.qbl_linear(b.comp, 0, x, y_ref, batch, ws)
+        torch.cuda.synchronize()
+        y = torch.empty_like(y_ref)
+        q.qbl_linear(b.comp, 0, x, y, batch, ws)
+        q.qbl_comp_attach(b.comp, [b.adapters[1]], [2.0])
+        q.qbl_comp_clear(b.comp)
+        q.qbl_comp_drop_previous(b.comp)
+        q.qbl_adapter_free(b.adapters[0])       # its memory must outlive the run
+        b.adapters = b.adapters[1:]
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref)
+    finally:
+        b.close()
