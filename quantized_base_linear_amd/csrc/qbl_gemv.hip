@@ -426,7 +426,7 @@ __host__ __device__ constexpr int b1_flags(int sum, int nseg, int shrink_in_gemv
 // wave launch, so the first weight and input loads wait for no argument
 // fetch; everything else is read from f, and only behind uniform branches that
 // the first loads do not take.
-template <int QT, int W, int CPW, int G>
+template <int QT, int W, int CPW, int G, bool XL>
 __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_kernel(
     const uint8_t* p_qs0, const void* p_sc0, const float* p_v0, int p_k, int p_first, int p_rows, int p_n0,
     int p_flags, int p_rt, FusedArgs f) {
@@ -750,6 +750,8 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
 
   // the first sparse value of each row, requested before the barrier so that
   // its round trip overlaps the wait there
+  __shared__ uint64_t spl[XL ? kB1MaxSlots : 1];
+  __shared__ int spf[XL ? kB1MaxSlots : 1];
   uint64_t spw = 0;
   int sp_first = -1;
   if (f.sp_items > 0 && tid < nslots) {
@@ -758,9 +760,13 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
       if (f.sp_base[sg][i] >= 0) sp_first = i;
     if (sp_first >= 0 && row < a.seg[sg].n)
       spw = __hip_atomic_load(f.sp + f.sp_base[sg][sp_first] + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (XL) {  // for the row's lane group (below)
+      spl[tid] = spw;
+      spf[tid] = sp_first;
+    }
   }
   __syncthreads();
-  if (tid < nslots) {
+  if (!XL && tid < nslots) {  // one thread per row (the launch's ranks are at most 32)
     const int s = tid;
     const GemvSeg& g = a.seg[slot_seg(s)];
     const int row = slot_row(s);
@@ -801,6 +807,67 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
     if (f.sum) outl[s] = v;
     else if (row < g.n) g.y[row] = v;
   }
+  // With ranks above 32 (XL) each row finishes in a group of lps lanes (one per
+  // 16 of the launch's largest rank, up to 16, as the workgroup's threads
+  // allow): the lanes split each adapter's B row (16-byte pieces lps apart), so
+  // every lane issues at most four loads at once, and a fixed xor tree adds
+  // their partial sums (the same bits in every lane).  Launches whose ranks are
+  // at most 32 run the kernel compiled without this path (carrying it cost the
+  // rank-16 block step 0.6 us).
+  int lps = f.expand_lanes;
+  while (lps > 1 && lps * nslots > NT) lps >>= 1;
+  const int s = tid / lps, q = tid & (lps - 1);
+  if (XL && s < nslots) {
+    const GemvSeg& g = a.seg[slot_seg(s)];
+    const int row = slot_row(s);
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) v += (red[i][s][0] + red[i][s][1]) + (red[i][s][2] + red[i][s][3]);
+    v *= cscale;
+    for (int i = 0; i < g.lora.n_ad; ++i) {
+      const int rk = g.lora.rank[i];
+      if (rk == 0) {  // sparse: the group's first lane (only its v is stored)
+        float p = 0.0f;
+        if (q == 0 && row < g.n) {
+          const uint64_t* w = f.sp + f.sp_base[slot_seg(s)][i] + row;
+          const uint64_t sw = spl[s];
+          p = i == spf[s] && (uint32_t)(sw >> 32) == f.read_tag ? __uint_as_float((uint32_t)sw)
+                                                                  : tagged_get(w, f.read_tag, hw);
+        }
+        v = fmaf(g.lora.scale[i], cscale * p, v);
+        continue;
+      }
+      const float* ti = tl + g.lora.toff[i];
+      const float* Br = g.lora.B[i] + (int64_t)min(row, g.n - 1) * rk;
+      float p = 0.0f;
+      if (rk % 4 == 0) {  // 16-byte B loads (the row is 16-byte aligned), up to four issued together
+        for (int j0 = 4 * q; j0 < rk; j0 += 16 * lps) {
+          float4 b4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            b4[u] = j0 + 4 * lps * u < rk ? gload4(Br + j0 + 4 * lps * u) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 4 * lps * u;
+            if (j < rk) {
+              p = fmaf(b4[u].x, ti[j], p);
+              p = fmaf(b4[u].y, ti[j + 1], p);
+              p = fmaf(b4[u].z, ti[j + 2], p);
+              p = fmaf(b4[u].w, ti[j + 3], p);
+            }
+          }
+        }
+      } else {
+        for (int j = q; j < rk; j += lps) p = fmaf(Br[j], ti[j], p);
+      }
+      for (int o = lps >> 1; o > 0; o >>= 1) p += __shfl_xor(p, o);
+      v = fmaf(g.lora.scale[i], p, v);
+    }
+    if (q == 0) {
+      if (f.sum) outl[s] = v;
+      else if (row < g.n) g.y[row] = v;
+    }
+  }
   if (f.sum) {
     __syncthreads();
     const int row = row0 + tid;
@@ -812,14 +879,14 @@ __global__ __launch_bounds__(W * 64, (b1_min_waves<QT, W, CPW>())) void gemv_b1_
   }
 }
 
-// Workgroups of gemv_b1_kernel<QT, W, CPW, G> that one CU holds at once.
-template <int QT, int W, int CPW, int G>
+// Workgroups of gemv_b1_kernel<QT, W, CPW, G, XL> that one CU holds at once.
+template <int QT, int W, int CPW, int G, bool XL>
 int b1_resident_per_cu() {
   static std::atomic<int> cached{0};
   int n = cached.load(std::memory_order_relaxed);
   if (!n) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&gemv_b1_kernel<QT, W, CPW, G>), W * 64, 0) != hipSuccess ||
+            &n, reinterpret_cast<const void*>(&gemv_b1_kernel<QT, W, CPW, G, XL>), W * 64, 0) != hipSuccess ||
         n < 1)
       n = 1;
     cached.store(n, std::memory_order_relaxed);
@@ -849,7 +916,15 @@ hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
   // with one workgroup per unit, separate shrink workgroups take units of their
   // own and the rows spread over the others.  Separate ones also when there are
   // fewer GEMV workgroups than A rows.
-  const int per_cu = b1_resident_per_cu<QT, W, CPW, G>();
+  int max_rk = 0;
+  for (int i = 0; i < a.nseg; ++i)
+    for (int j = 0; j < a.seg[i].lora.n_ad; ++j) max_rk = std::max(max_rk, a.seg[i].lora.rank[j]);
+  // lane groups for ranks above 32 (rank 32 measured no faster with them)
+  f.expand_lanes = 1;
+  if (max_rk > 32)
+    while (f.expand_lanes < 16 && 16 * f.expand_lanes < max_rk) f.expand_lanes *= 2;
+  const bool xl = f.expand_lanes > 1;
+  const int per_cu = xl ? b1_resident_per_cu<QT, W, CPW, G, true>() : b1_resident_per_cu<QT, W, CPW, G, false>();
   f.shrink_wgs = 0;
   f.shrink_in_gemv = S::kShrinkInGemv && per_cu > 1 ? 1 : 0;
   if (!f.shrink_in_gemv) f.shrink_wgs = (f.rows_total + S::kRS - 1) / S::kRS;
@@ -901,8 +976,12 @@ hipError_t launch_b1_t(FusedArgs& f, const LaunchCtx& lc) {
   }
   a.grid = f.shrink_wgs + f.sparse_wgs + wg;
   const int flags = b1_flags(f.sum, a.nseg, f.shrink_in_gemv, f.shrink_wgs);
-  QBL_LAUNCH((gemv_b1_kernel<QT, W, CPW, G>), dim3(a.grid), dim3(W * 64), 0, lc, a.seg[0].qs, a.seg[0].sc, f.v[0], a.k,
-             f.shrink_wgs + f.sparse_wgs, f.rows_per_wg, a.seg[0].n, flags, f.rows_total, f);
+  if (xl)
+    QBL_LAUNCH((gemv_b1_kernel<QT, W, CPW, G, true>), dim3(a.grid), dim3(W * 64), 0, lc, a.seg[0].qs, a.seg[0].sc,
+               f.v[0], a.k, f.shrink_wgs + f.sparse_wgs, f.rows_per_wg, a.seg[0].n, flags, f.rows_total, f);
+  else
+    QBL_LAUNCH((gemv_b1_kernel<QT, W, CPW, G, false>), dim3(a.grid), dim3(W * 64), 0, lc, a.seg[0].qs, a.seg[0].sc,
+               f.v[0], a.k, f.shrink_wgs + f.sparse_wgs, f.rows_per_wg, a.seg[0].n, flags, f.rows_total, f);
   return hipGetLastError();
 }
 

@@ -118,6 +118,7 @@ struct FusedArgs {
   uint32_t* fail;      // status word a wait sets when it gives up (coherent host memory)
   uint32_t tag;        // this launch's number, never 0: written beside every handed-over value
   uint32_t read_tag;   // the number readers wait for: tag (another value only under test fault injection)
+  int expand_lanes;    // set by the launcher: lanes per row in the expand (1, or for ranks above 32 one per 16 of the largest)
   uint64_t* t;         // kTCopies copies of the rows_total shrink results, (tag << 32) | float bits
   int64_t t_copy_stride;  // words between copies (see t_copy_stride())
   PrepEntry ent[kMaxPrepEntries];

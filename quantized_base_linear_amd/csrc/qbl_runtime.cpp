@@ -1601,10 +1601,13 @@ extern "C" qbl_status qbl_linear_jit(qbl_comp* comp, int32_t linear, const uint1
     a.ws = static_cast<uint16_t*>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (qbl_status s = check_handoffs()) return s;
-    const ListUse use{L.get(), st, T > 0};
+    ListUse use{L.get(), st, T > 0};
     KernelTimer tm(2, st);
-    hipError_t e = qbl::launch_jit(a, tm.ctx());
+    qbl::LaunchCtx lc = tm.ctx();
+    const hipEvent_t done = use.attach(lc);  // on the GEMM launch, the last one
+    hipError_t e = qbl::launch_jit(a, lc);
     if (e != hipSuccess) return hip_fail(e, "jit launch");
+    if (done) use.attached = true;
     tm.stop();
     return QBL_OK;
   })

@@ -174,3 +174,28 @@ def test_block_with_two_sparse_deltas_around_a_lora():
     finally:
         b.close()
 
+
+
+@pytest.mark.parametrize("qtype,n,k,rank", [(1, 1000, 4128, 48), (2, 333, 4160, 80), (1, 4096, 11008, 64)])
+def test_sparse_delta_beside_a_high_rank_adapter(torch_cuda, qtype, n, k, rank):
+    """At batch 1 a list whose largest rank is above 32 finishes each row in a
+    group of lanes (the B row split over them, a fixed xor tree adding the
+    parts); the row's first sparse value, fetched before the barrier, reaches
+    the group through LDS.  Both orders of the list, against the oracle, and
+    the same call twice bitwise."""
+    torch = torch_cuda
+    wl = workloads.Workload(f"sp_hr_{qtype}_{n}_{k}_{rank}", [workloads.LinearSpec(f"sp_hr/{qtype}/{n}/{k}", n, k, qtype)],
+                            [workloads.AdapterSpec("A1", rank, 0.75), workloads.AdapterSpec("S1", 0, 1.5, 0.1)])
+    log(f"sparse beside rank {rank}: qtype={qtype} n={n} k={k}")
+    b = Built(wl)
+    try:
+        L = wl.linears[0]
+        x = wl.x(0)
+        for order, scales in (([0, 1], [0.75, 1.5]), ([1, 0], [1.5, 0.75])):
+            b.attach(order, scales)
+            y = _run(b, torch, 0, x)
+            ref = oracle.linear_dual(L.qtype, b.or_blocks[0], n, k, x, b.oracle_ads(0, order, scales))
+            assert rel_l2(y, ref) <= TOL, order
+            assert np.array_equal(_run(b, torch, 0, x), y)
+    finally:
+        b.close()
