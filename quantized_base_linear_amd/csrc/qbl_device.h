@@ -150,26 +150,33 @@ __device__ __forceinline__ float dot_q8(const uint4 q, const float4* xv, float x
 }
 
 // Sum_j q_j x_j over one q4_sm block: byte i holds q_{2i} (low nibble) and
-// q_{2i+1} (high nibble), so 32-bit word w covers weights 8w .. 8w+7.
+// q_{2i+1} (high nibble), so 32-bit word w covers weights 8w .. 8w+7.  The low
+// and the high nibbles of a word are spread into the bytes of one word each and
+// converted two at a time by the gfx950 fp8 (e4m3) conversion: a byte c < 16 is
+// the e4m3 value c 2^-9, so scale 2^9 gives the exact f16 integer c.  Each
+// product is one v_fma_mix_f32 (f16 code times float32 input, float32 fma), so
+// the sums are bitwise those of fmaf(float(c), x, s) in the same order.
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot_q4(const uint4 q, const float4* xv) {
+  constexpr float kFp8Scale = 512.0f;  // 2^9
   const uint32_t v[4] = {q.x, q.y, q.z, q.w};
   float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t lo = v[w] & 0x0F0F0F0Fu, hi = (v[w] >> 4) & 0x0F0F0F0Fu;
-    // The masked words are hidden from the optimiser: knowing the masks, it
-    // would extract every nibble with its own bit-field instruction before the
-    // conversion; opaque, each byte converts in one v_cvt_f32_ubyteN.
-    asm("" : "+v"(lo), "+v"(hi));
+    const uint32_t lo = v[w] & 0x0F0F0F0Fu, hi = (v[w] >> 4) & 0x0F0F0F0Fu;
+    const f16x2v l01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, kFp8Scale, false);
+    const f16x2v l23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, kFp8Scale, true);
+    const f16x2v h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, kFp8Scale, false);
+    const f16x2v h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, kFp8Scale, true);
     const float4 xa = xv[2 * w], xb = xv[2 * w + 1];
-    s0 = fmaf(ub(lo, 0), xa.x, s0);
-    s1 = fmaf(ub(hi, 0), xa.y, s1);
-    s0 = fmaf(ub(lo, 1), xa.z, s0);
-    s1 = fmaf(ub(hi, 1), xa.w, s1);
-    s0 = fmaf(ub(lo, 2), xb.x, s0);
-    s1 = fmaf(ub(hi, 2), xb.y, s1);
-    s0 = fmaf(ub(lo, 3), xb.z, s0);
-    s1 = fmaf(ub(hi, 3), xb.w, s1);
+    s0 = fmaf((float)l01[0], xa.x, s0);
+    s1 = fmaf((float)h01[0], xa.y, s1);
+    s0 = fmaf((float)l01[1], xa.z, s0);
+    s1 = fmaf((float)h01[1], xa.w, s1);
+    s0 = fmaf((float)l23[0], xb.x, s0);
+    s1 = fmaf((float)h23[0], xb.y, s1);
+    s0 = fmaf((float)l23[1], xb.z, s0);
+    s1 = fmaf((float)h23[1], xb.w, s1);
   }
   return s0 + s1;
 }
