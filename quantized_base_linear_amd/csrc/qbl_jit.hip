@@ -422,7 +422,9 @@ __global__ __launch_bounds__(JTHREADS) void jit_kernel(JitArgs a, int tp) {
 // ---------------------------------------------------------------------------
 constexpr int JWS_MFMA = 8, JWS_BUILD = 8, JWS_THREADS = (JWS_MFMA + JWS_BUILD) * 64;
 
-template <int QT, int RS>
+// SG (q8_0 with K a multiple of 256): a builder's scales come 8 blocks, 16 bytes,
+// at a time, once per 4 K-steps (see below).
+template <int QT, int RS, bool SG>
 __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) {
   static_assert(RS <= JRMAX, "ranks held in registers");
   extern __shared__ __attribute__((aligned(16))) uint16_t jit_lds[];
@@ -576,11 +578,27 @@ __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) 
       if (aok) *reinterpret_cast<uint4*>(As0 + b * kAsElems + lrow * kALD + 8 * apc) = r;
     }
   };
-  auto prefetch = [&](Ops& o, int st) __attribute__((always_inline)) {
+  // SG: the scales of K-steps 4g .. 4g + 3 (this builder's blocks 2 st + kb)
+  // are one 16-byte run of its row, blocks 8g .. 8g + 7.  sgc holds the run of
+  // the group being built; the next group's run is loaded into sgn with the
+  // operands of step 4g + 3, three steps before its first use, and moves to sgc
+  // when step 4g + 4 is built.  A step's phase st % 4 is passed as a constant
+  // where the caller knows it (ph >= 0).
+  uint4 sgc = make_uint4(0u, 0u, 0u, 0u), sgn = sgc;
+  auto load_sg = [&](uint4& r, int g) __attribute__((always_inline)) {
+    if constexpr (SG)
+      r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.sc) + (int64_t)nrow * nblk +
+                                          8 * min(g, nblk / 8 - 1));
+  };
+  auto prefetch = [&](Ops& o, int st, int ph = -1) __attribute__((always_inline)) {
     const int k0 = min(st, nk - 1) * JBK;  // steps past the end reload the last one
     const int kbase = k0 + 32 * kb;
     if (QT == QBL_FMT_Q8) {
-      o.scv = reinterpret_cast<const uint16_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+      if constexpr (SG) {
+        if ((ph >= 0 ? ph : st & 3) == 3) load_sg(sgn, (st >> 2) + 1);
+      } else {
+        o.scv = reinterpret_cast<const uint16_t*>(a.sc)[(int64_t)nrow * nblk + kbase / 32];
+      }
       o.qv = *reinterpret_cast<const uint4*>(a.qs + (int64_t)nrow * K + kbase + 16 * h);
     } else {
       if constexpr (QT == QBL_FMT_Q4K)
@@ -595,7 +613,7 @@ __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) 
   };
   // block (kb, nb) of the W tile of K-step k0 into buffer b; the low-rank sum
   // from the At rows in As[b]
-  auto build = [&](const Ops& o, int k0, int b) __attribute__((always_inline)) {
+  auto build = [&](const Ops& o, int k0, int b, int ph = -1) __attribute__((always_inline)) {
     f32x16 dsum;
 #pragma unroll
     for (int v = 0; v < 16; ++v) dsum[v] = 0.0f;
@@ -612,8 +630,15 @@ __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) 
       d = D;
       mn = -M;
     } else {
-      d = h2f(o.scv);
-      mn = QT == QBL_FMT_Q8 ? -128.0f * d : h2f(o.scv >> 16);
+      uint32_t scv = o.scv;
+      if constexpr (SG) {  // block 2 st + kb of the run of group st / 4: dword st % 4, half kb
+        const int st = k0 / JBK, p = ph >= 0 ? ph : st & 3;
+        if (p == 0 && st > 0) sgc = sgn;
+        const uint32_t dw = p == 0 ? sgc.x : p == 1 ? sgc.y : p == 2 ? sgc.z : sgc.w;
+        scv = kb ? dw >> 16 : dw;
+      }
+      d = h2f(scv);
+      mn = QT == QBL_FMT_Q8 ? -128.0f * d : h2f(scv >> 16);
     }
     const uint32_t qw[4] = {o.qv.x, o.qv.y, o.qv.z, o.qv.w};
     uint32_t packed[8];
@@ -646,6 +671,7 @@ __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) 
     store_at(r1, 1);
   }
   __syncthreads();
+  load_sg(sgc, 0);
   prefetch(opa, 0);
   build(opa, 0, 0);
   prefetch(opa, 1);
@@ -655,14 +681,22 @@ __global__ __launch_bounds__(JWS_THREADS) void jit_ws_kernel(JitArgs a, int tp) 
   // step ks: the next W tile (step ks + 1) from `next` into the other buffer,
   // At(ks + 2) into As[cur], `next` reloaded with Ops(ks + 3); the MFMA waves
   // work on step ks and stage X(ks + 1)
-  auto step = [&](int ks, Ops& next) __attribute__((always_inline)) {
+  auto step = [&](int ks, Ops& next, int ph = -1) __attribute__((always_inline)) {
     const int cur = ks & 1;
-    build(next, (ks + 1) * JBK, cur ^ 1);
+    build(next, (ks + 1) * JBK, cur ^ 1, ph < 0 ? -1 : (ph + 1) & 3);
     store_at(next.atr, cur);
-    prefetch(next, ks + 3);
+    prefetch(next, ks + 3, ph < 0 ? -1 : (ph + 3) & 3);
     __syncthreads();
   };
   int ks = 0;
+  if constexpr (SG) {  // four steps per iteration, phases fixed: each body's scale work is the same every time
+    for (; ks + 3 < nk; ks += 4) {
+      step(ks, opa, 0);
+      step(ks + 1, opb, 1);
+      step(ks + 2, opa, 2);
+      step(ks + 3, opb, 3);
+    }
+  }
   for (; ks + 1 < nk; ks += 2) {
     step(ks, opa);
     step(ks + 1, opb);
@@ -684,14 +718,23 @@ hipError_t launch_full(const JitArgs& a, int tp, const LaunchCtx& lc) {
   return hipGetLastError();
 }
 
-template <int QT, int RS>
-hipError_t launch_ws(const JitArgs& a, int tp, const LaunchCtx& lc) {
+template <int QT, int RS, bool SG>
+hipError_t launch_ws_sg(const JitArgs& a, int tp, const LaunchCtx& lc) {
   const dim3 grid((a.n + JBN - 1) / JBN, a.m / JBM);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&jit_ws_kernel<QT, RS>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&jit_ws_kernel<QT, RS, SG>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kJitLds);
   if (e != hipSuccess) return e;
-  QBL_LAUNCH((jit_ws_kernel<QT, RS>), grid, dim3(JWS_THREADS), kJitLds, lc, a, tp);
+  QBL_LAUNCH((jit_ws_kernel<QT, RS, SG>), grid, dim3(JWS_THREADS), kJitLds, lc, a, tp);
   return hipGetLastError();
+}
+
+template <int QT, int RS>
+hipError_t launch_ws(const JitArgs& a, int tp, const LaunchCtx& lc) {
+  // q8_0 rows whose scale arrays are 16-byte aligned (K a multiple of 256) take
+  // the scales 8 blocks at a time
+  if constexpr (QT == QBL_FMT_Q8)
+    if (a.k % 256 == 0) return launch_ws_sg<QT, RS, true>(a, tp, lc);
+  return launch_ws_sg<QT, RS, false>(a, tp, lc);
 }
 
 template <int QT, int RS>
