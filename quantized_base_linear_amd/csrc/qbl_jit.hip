@@ -102,11 +102,41 @@ __device__ __forceinline__ void stage_sb_elem(const JitArgs& a, int tp, uint32_t
   sB[o] = bf16_rne(v);
 }
 
+// Every rank a multiple of 8: elements o = 8 g .. 8 g + 7 lie in one row and in
+// one adapter's part (or all in the zero padding), so a thread stages them with
+// two 16-byte loads of B and one 16-byte store, each value rounded as above.
+__device__ __forceinline__ void stage_sb_vec8(const JitArgs& a, int tp, uint32_t g) {
+  if (g >= (uint32_t)a.n * (uint32_t)tp / 8u) return;  // (tp is a multiple of 16)
+  const uint32_t o = 8u * g;
+  const int n = (int)(o / (uint32_t)tp), t = (int)(o % (uint32_t)tp);
+  const int64_t nat = (int64_t)a.k * tp;
+  uint16_t* sB = a.ws + ((nat * 2 + 255) / 256 * 256) / 2;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int base = 0;
+  for (int j = 0; j < a.n_ad; ++j) {
+    if (t >= base && t < base + a.rank[j]) {
+      const float4* p = reinterpret_cast<const float4*>(a.B[j] + (int64_t)n * a.rank[j] + (t - base));
+      const float4 lo = p[0], hi = p[1];
+      const float s = a.scale[j];
+      v[0] = s * lo.x, v[1] = s * lo.y, v[2] = s * lo.z, v[3] = s * lo.w;
+      v[4] = s * hi.x, v[5] = s * hi.y, v[6] = s * hi.z, v[7] = s * hi.w;
+    }
+    base += a.rank[j];
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = bf16_rne(v[2 * i]) | ((uint32_t)bf16_rne(v[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(sB + o) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // One launch for both: workgroups [0, at_wgs) stage At tiles (ceil(k/16) along
-// k, then the rank tiles), the rest sB, 256 elements each.
+// k, then the rank tiles), the rest sB, 256 elements each (VEC8: 2048, eight
+// per thread).
+template <bool VEC8>
 __global__ __launch_bounds__(256) void stage_lora_kernel(JitArgs a, int tp, int at_kt, int at_wgs) {
   const int b = blockIdx.x;
   if (b < at_wgs) stage_at_tile(a, tp, b % at_kt, b / at_kt);
+  else if (VEC8) stage_sb_vec8(a, tp, (uint32_t)(b - at_wgs) * 256u + threadIdx.x);
   else stage_sb_elem(a, tp, (uint32_t)(b - at_wgs) * 256u + threadIdx.x);
 }
 
@@ -773,9 +803,16 @@ hipError_t launch_jit(const JitArgs& a, const LaunchCtx& lc) {
   if (tp > 0) {
     if ((int64_t)a.n * tp >= (int64_t)1 << 32 || a.k % 4) return hipErrorInvalidValue;
     const int at_kt = (a.k + kStageK - 1) / kStageK, at_wgs = at_kt * ((tp + kStageT - 1) / kStageT);
-    const int64_t sb_wgs = ((int64_t)a.n * tp + 255) / 256;
-    hipLaunchKernelGGL(stage_lora_kernel, dim3((unsigned)(at_wgs + sb_wgs)), dim3(256), 0, lc.stream, a, tp, at_kt,
-                       at_wgs);
+    bool vec8 = true;
+    for (int j = 0; j < a.n_ad; ++j) vec8 = vec8 && a.rank[j] % 8 == 0;
+    const int64_t per_wg = vec8 ? 2048 : 256;
+    const int64_t sb_wgs = ((int64_t)a.n * tp + per_wg - 1) / per_wg;
+    if (vec8)
+      hipLaunchKernelGGL(stage_lora_kernel<true>, dim3((unsigned)(at_wgs + sb_wgs)), dim3(256), 0, lc.stream, a, tp,
+                         at_kt, at_wgs);
+    else
+      hipLaunchKernelGGL(stage_lora_kernel<false>, dim3((unsigned)(at_wgs + sb_wgs)), dim3(256), 0, lc.stream, a,
+                         tp, at_kt, at_wgs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

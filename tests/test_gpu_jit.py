@@ -39,7 +39,9 @@ def _jit(b, torch, linear, xbits):
 # m a multiple of 256 (K of 64) takes the role-split kernel (here also at 512
 # and 1024 rows, ragged n, total ranks 8..64, every format), others the
 # general one; q8_0 with K a multiple of 256 takes its scales 8 blocks at a
-# time (K of 256, 768 and 1280: one group, groups in whole four-step rounds)
+# time (K of 256, 768 and 1280: one group, groups in whole four-step rounds);
+# ranks that are all multiples of 8 stage s B eight values per thread, others
+# (6 + 36) one
 @pytest.mark.parametrize("shape", [(96, 608, 1184, 1, (64,)), (300, 96, 200, 1, (16, 64)),
                                    (257, 1056, 130, 2, (32,)), (40, 640, 384, 1, (8, 8, 8)),
                                    (96, 512, 1184, 3, (64,)), (257, 1280, 130, 3, (16, 32)),
@@ -47,7 +49,7 @@ def _jit(b, torch, linear, xbits):
                                    (512, 640, 200, 1, (64,)), (1024, 256, 96, 2, (16, 32)),
                                    (512, 512, 130, 3, (8,)), (512, 192, 70, 2, (8, 8, 8)),
                                    (256, 256, 200, 1, (16,)), (512, 768, 96, 1, (8, 8, 8)),
-                                   (256, 1280, 130, 1, (64, 8))])
+                                   (256, 1280, 130, 1, (64, 8)), (256, 512, 200, 1, (6, 36))])
 def test_jit_parity(torch_cuda, shape):
     torch = torch_cuda
     m, k, n, qtype, ranks = shape
