@@ -96,12 +96,13 @@ __device__ __forceinline__ half8 codes_q4(uint32_t w) {
 //   formats as codes_q4 expects); xsum[blk][r] = X of batch row r for r < 8
 //   (float32, input order), 0 for r >= 8; ex[b] = e_b.  Rows b >= batch are zero.
 //   Shrink workgroups (range p, adapter rows [16 q, 16 q + 16)) follow:
-//   tpart[p][j][b] = sum over inputs [1024 p, 1024 p + 1024) of A[j][k] x[b][k]
-//   (lane l takes inputs 4 l + 256 c, c = 0..3, in order, then a fixed-order
+//   tpart[p][j][b] = sum over inputs [512 p, 512 p + 512) of A[j][k] x[b][k]
+//   (lane l takes inputs 4 l + 256 c, c = 0..1, in order, then a fixed-order
 //   wave sum); the GEMV adds the ranges in order.  Wave w takes rows 16 q + 4 w
 //   .. + 3, their loads issued together.
 // ---------------------------------------------------------------------------
-constexpr int kScanK = 1024;
+constexpr int kScanK = 512;
+constexpr int kScanC = kScanK / 256;  // 16-byte pieces of a range per lane
 constexpr int kScanJ = 16;
 constexpr int kRowBlocks = 256;  // blocks per row workgroup
 
@@ -202,7 +203,7 @@ __device__ __forceinline__ void prep_shrink(const PrepHot& h, const ScanArgs& a,
   for (int i = 0; i < 2; ++i) {  // thread: rows wave and wave + 4, inputs 4 lane + 256 c
     const int b = wave + 4 * i;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kScanC; ++c) {
       const int k = 4 * lane + 256 * c;
       f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
       if (b < h.batch && k < kn) v = *gp(reinterpret_cast<const f32x4*>(h.x + (int64_t)b * h.x_stride + k0 + k));
@@ -210,7 +211,7 @@ __device__ __forceinline__ void prep_shrink(const PrepHot& h, const ScanArgs& a,
     }
   }
   const int j0 = q * kScanJ + 4 * wave;
-  f32x4 w[4][4];
+  f32x4 w[4][kScanC];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const float* Ar = nullptr;
@@ -221,7 +222,7 @@ __device__ __forceinline__ void prep_shrink(const PrepHot& h, const ScanArgs& a,
       Ar = a.ent[e].A + (int64_t)(j - base) * h.k + k0;
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kScanC; ++c) {
       const int k = 4 * lane + 256 * c;
       w[u][c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
       if (Ar && k < kn) w[u][c] = *gp(reinterpret_cast<const f32x4*>(Ar + k));
@@ -235,7 +236,7 @@ __device__ __forceinline__ void prep_shrink(const PrepHot& h, const ScanArgs& a,
 #pragma unroll
     for (int b = 0; b < 8; ++b) acc[u][b] = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < kScanC; ++c) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const f32x4 xv = *reinterpret_cast<const f32x4*>(&xs[b][4 * lane + 256 * c]);
